@@ -1,0 +1,175 @@
+/*
+ * Oracle for the conv1d -> GroupNorm path: plain, slow, fp64 CPU loops.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this code; the product path
+ * (the HIP library under conv1d_implicit_gemm_amd/) never does, and the two
+ * share no source, header, helper or table.
+ *
+ * Every routine is the textbook definition written out with straightforward
+ * loops and sequential fp64 sums, parallelised with OpenMP over independent
+ * outputs only (each output is still summed in the same fixed order).
+ *
+ * Sources (web pages, cited by title and passage):
+ *   - "Kimi-K2.6 l2_p35" (POPCORNBENCH trace: Conv1d -> GroupNorm): the output
+ *     length formula in the default-configuration walk-through; the conv input
+ *     index t_out*stride + j*dilation - padding with zero outside [0,T); the
+ *     GroupNorm statistics over (C_out/G channels x T_out) per (n, group); the
+ *     population variance and eps inside the square root.
+ *   - "Kimi-K2.6 l1_p5" (POPCORNBENCH trace: causal Conv1d): causal padding of
+ *     (kernel_size-1)*dilation zeros on the left only; input position
+ *     t + j*dilation - causal_padding; weight index 0 is the oldest tap (no
+ *     kernel flip).
+ *   - "Kimi-K2.6 l2_p75" (POPCORNBENCH trace: Linear -> GroupNorm -> min ->
+ *     +bias): min over channels after the GroupNorm affine, then a
+ *     per-channel bias broadcast so out[i,j] = min_c z[i,c] + bias[j].
+ *   - LayerNorm over channels: at every (n,t) the C_out values are normalised
+ *     with the same formula as GroupNorm (population variance, eps inside the
+ *     root) and a per-channel affine.  The traces' LayerNorm ("Kimi-K2.6
+ *     l2_p3") normalises the last dimension; the over-channels mode is the
+ *     plain reading of the workload's "normalise the C_out values at each
+ *     (n,t)".
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Output length of a 1-D convolution with left/right zero padding
+ * ("Kimi-K2.6 l2_p35", T_out derivation; symmetric padding p gives
+ * pad_left = pad_right = p).  Returns -1 if there is no valid output. */
+int64_t oracle_out_len(int64_t T, int64_t K, int64_t stride, int64_t dilation,
+                       int64_t pad_left, int64_t pad_right) {
+  int64_t span = T + pad_left + pad_right - dilation * (K - 1) - 1;
+  if (T < 1 || K < 1 || stride < 1 || dilation < 1 || pad_left < 0 || pad_right < 0)
+    return -1;
+  if (span < 0) return -1;
+  return span / stride + 1;
+}
+
+/* y[n,c,t] = bias[c] + sum_ci sum_j w[c,ci,j] * X(n, ci, t*stride + j*dilation - pad_left)
+ * with X = 0 outside [0,T).  Layouts: x [N,C_in,T], w [C_out,C_in,K],
+ * y [N,C_out,T_out], all contiguous.  bias may be NULL (no bias).
+ * Summation order: ci outer, j inner, sequential in fp64. */
+void oracle_conv1d(int64_t N, int64_t C_in, int64_t C_out, int64_t T, int64_t K,
+                   int64_t stride, int64_t dilation, int64_t pad_left, int64_t pad_right,
+                   const double* x, const double* w, const double* bias, double* y) {
+  int64_t T_out = oracle_out_len(T, K, stride, dilation, pad_left, pad_right);
+  if (T_out < 1) return;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t c = 0; c < C_out; ++c) {
+      double* yrow = y + (n * C_out + c) * T_out;
+      for (int64_t t = 0; t < T_out; ++t) {
+        double acc = bias ? bias[c] : 0.0;
+        for (int64_t ci = 0; ci < C_in; ++ci) {
+          const double* xrow = x + (n * C_in + ci) * T;
+          const double* wrow = w + (c * C_in + ci) * K;
+          for (int64_t j = 0; j < K; ++j) {
+            int64_t u = t * stride + j * dilation - pad_left;
+            if (u >= 0 && u < T) acc += wrow[j] * xrow[u];
+          }
+        }
+        yrow[t] = acc;
+      }
+    }
+  }
+}
+
+/* GroupNorm over y [N,C,L]: for each (n,g) the set S holds the C/G channels
+ * [g*C/G, (g+1)*C/G) at every l < L.  mean = sum(S)/|S|;
+ * var = sum((s-mean)^2)/|S| (population, second pass over the data);
+ * z = (y-mean)/sqrt(var+eps)*gamma[c] + beta[c].
+ * gamma/beta may be NULL (1 and 0).  mean_out/rstd_out ([N,G]) may be NULL.
+ * Requires C % G == 0. */
+void oracle_group_norm(int64_t N, int64_t C, int64_t L, int64_t G, double eps,
+                       const double* y, const double* gamma, const double* beta,
+                       double* z, double* mean_out, double* rstd_out) {
+  int64_t cpg = C / G;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t g = 0; g < G; ++g) {
+      const double* base = y + (n * C + g * cpg) * L;
+      double cnt = (double)(cpg * L);
+      double s = 0.0;
+      for (int64_t i = 0; i < cpg * L; ++i) s += base[i];
+      double mean = s / cnt;
+      double ss = 0.0;
+      for (int64_t i = 0; i < cpg * L; ++i) {
+        double dlt = base[i] - mean;
+        ss += dlt * dlt;
+      }
+      double var = ss / cnt;
+      double rstd = 1.0 / sqrt(var + eps);
+      if (mean_out) mean_out[n * G + g] = mean;
+      if (rstd_out) rstd_out[n * G + g] = rstd;
+      for (int64_t cc = 0; cc < cpg; ++cc) {
+        int64_t c = g * cpg + cc;
+        double ga = gamma ? gamma[c] : 1.0;
+        double be = beta ? beta[c] : 0.0;
+        const double* yr = y + (n * C + c) * L;
+        double* zr = z + (n * C + c) * L;
+        for (int64_t l = 0; l < L; ++l) zr[l] = (yr[l] - mean) * rstd * ga + be;
+      }
+    }
+  }
+}
+
+/* LayerNorm over channels of y [N,C,L]: for each (n,l) the C values y[n,:,l]
+ * are normalised (population variance, two passes, eps inside the root) and
+ * get the per-channel affine gamma[c], beta[c] (NULL -> 1, 0).
+ * mean_out/rstd_out ([N,L]) may be NULL. */
+void oracle_layer_norm_channels(int64_t N, int64_t C, int64_t L, double eps,
+                                const double* y, const double* gamma, const double* beta,
+                                double* z, double* mean_out, double* rstd_out) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t l = 0; l < L; ++l) {
+      double s = 0.0;
+      for (int64_t c = 0; c < C; ++c) s += y[(n * C + c) * L + l];
+      double mean = s / (double)C;
+      double ss = 0.0;
+      for (int64_t c = 0; c < C; ++c) {
+        double dlt = y[(n * C + c) * L + l] - mean;
+        ss += dlt * dlt;
+      }
+      double rstd = 1.0 / sqrt(ss / (double)C + eps);
+      if (mean_out) mean_out[n * L + l] = mean;
+      if (rstd_out) rstd_out[n * L + l] = rstd;
+      for (int64_t c = 0; c < C; ++c) {
+        double ga = gamma ? gamma[c] : 1.0;
+        double be = beta ? beta[c] : 0.0;
+        z[(n * C + c) * L + l] = (y[(n * C + c) * L + l] - mean) * rstd * ga + be;
+      }
+    }
+  }
+}
+
+/* Per-row min over channels plus a broadcast per-channel bias
+ * ("Kimi-K2.6 l2_p75"): m[n,l] = min_c z[n,c,l]; out[n,c,l] = m[n,l] + bias2[c].
+ * rowmin_out ([N,L]) may be NULL. */
+void oracle_rowmin_bias(int64_t N, int64_t C, int64_t L, const double* z,
+                        const double* bias2, double* out, double* rowmin_out) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t l = 0; l < L; ++l) {
+      double m = z[(n * C) * L + l];
+      for (int64_t c = 1; c < C; ++c) {
+        double v = z[(n * C + c) * L + l];
+        if (v < m) m = v;
+      }
+      if (rowmin_out) rowmin_out[n * L + l] = m;
+      for (int64_t c = 0; c < C; ++c) out[(n * C + c) * L + l] = m + bias2[c];
+    }
+  }
+}
