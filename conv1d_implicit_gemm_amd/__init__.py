@@ -1,0 +1,296 @@
+"""conv1d_implicit_gemm_amd - MI355X (gfx950) conv1d -> GroupNorm.
+
+A thin ctypes binding over the C ABI in ``include/conv1d_gn.h``
+(``libconv1d_gn.so``, built by ``python -m conv1d_implicit_gemm_amd.build``).
+It only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory (tensors passed by
+``data_ptr()``) and the current HIP stream.  If the library is missing the
+functions raise; there is no other implementation to fall back to.
+
+Entry points (same names as the C ABI):
+    conv1d_forward(x, w, bias=None, *, stride, padding/pad_left/pad_right, causal, dilation)
+    conv1d_gn_forward(x, w, bias=None, *, ..., norm, groups, eps, gamma, beta,
+                      rowmin_bias=None, return_stats=False)
+    gn_stats(y, groups, eps)        -> (mean[N,G], rstd[N,G])
+    gn_apply(y, mean, rstd, gamma, beta, groups, out=None)
+Host-only helpers: out_len, route, workspace sizes, check.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libconv1d_gn.so")
+
+C1G_F32, C1G_BF16 = 0, 1
+NORM_NONE, NORM_GROUP, NORM_LAYER_CHANNELS = 0, 1, 2
+EPI_NONE, EPI_ROWMIN_BIAS = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+          3: "workspace missing or too small", 4: "misaligned pointer",
+          5: "HIP runtime error at launch"}
+
+# every symbol include/conv1d_gn.h declares
+EXPORTS = ["c1g_out_len", "c1g_check", "c1g_conv1d_workspace_size", "conv1d_forward",
+           "c1g_gn_stats_workspace_size", "gn_stats", "gn_apply",
+           "c1g_conv1d_gn_workspace_size", "conv1d_gn_forward", "c1g_route",
+           "c1g_status_string"]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("C_in", ctypes.c_int64), ("C_out", ctypes.c_int64),
+                ("T", ctypes.c_int64), ("K", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("dilation", ctypes.c_int32), ("pad_left", ctypes.c_int32),
+                ("pad_right", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class NormDesc(ctypes.Structure):
+    _fields_ = [("norm", ctypes.c_int32), ("G", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("epilogue", ctypes.c_int32)]
+
+
+class C1GError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, STATUS.get(status, "unknown"), status))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library():
+    """Load libconv1d_gn.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libconv1d_gn.so is not built; run "
+                               "`python -m conv1d_implicit_gemm_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PD, PN = ctypes.POINTER(ConvDesc), ctypes.POINTER(NormDesc)
+        i64, i32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        lib.c1g_out_len.restype = i64
+        lib.c1g_out_len.argtypes = [PD]
+        lib.c1g_check.restype = ctypes.c_int
+        lib.c1g_check.argtypes = [PD, PN, sz]
+        lib.c1g_conv1d_workspace_size.restype = sz
+        lib.c1g_conv1d_workspace_size.argtypes = [PD]
+        lib.conv1d_forward.restype = ctypes.c_int
+        lib.conv1d_forward.argtypes = [PD, P, P, P, P, P, sz, P]
+        lib.c1g_gn_stats_workspace_size.restype = sz
+        lib.c1g_gn_stats_workspace_size.argtypes = [i64, i64, i64, i32]
+        lib.gn_stats.restype = ctypes.c_int
+        lib.gn_stats.argtypes = [i64, i64, i64, i32, ctypes.c_float, P, P, P, P, sz, P]
+        lib.gn_apply.restype = ctypes.c_int
+        lib.gn_apply.argtypes = [i64, i64, i64, i32, P, P, P, P, P, P, P]
+        lib.c1g_conv1d_gn_workspace_size.restype = sz
+        lib.c1g_conv1d_gn_workspace_size.argtypes = [PD, PN]
+        lib.conv1d_gn_forward.restype = ctypes.c_int
+        lib.conv1d_gn_forward.argtypes = [PD, PN, P, P, P, P, P, P, P, P, P, P, sz, P]
+        lib.c1g_route.restype = ctypes.c_char_p
+        lib.c1g_route.argtypes = [PD, PN]
+        lib.c1g_status_string.restype = ctypes.c_char_p
+        lib.c1g_status_string.argtypes = [ctypes.c_int]
+        _lib = lib
+        return lib
+
+
+# ----------------------------------------------------------------- helpers
+def _pads(K, dilation, padding, pad_left, pad_right, causal):
+    if causal:
+        if pad_left is not None or pad_right is not None or padding:
+            raise ValueError("causal=True fixes the padding")
+        return (K - 1) * dilation, 0
+    if pad_left is None and pad_right is None:
+        return padding, padding
+    return (pad_left if pad_left is not None else padding,
+            pad_right if pad_right is not None else padding)
+
+
+def make_desc(N, C_in, C_out, T, K, *, stride=1, dilation=1, padding=0, pad_left=None,
+              pad_right=None, causal=False, dtype=C1G_F32) -> ConvDesc:
+    pl, pr = _pads(K, dilation, padding, pad_left, pad_right, causal)
+    return ConvDesc(N, C_in, C_out, T, K, stride, dilation, pl, pr, dtype)
+
+
+def make_norm(norm=None, groups=0, eps=1e-5, rowmin=False) -> NormDesc:
+    code = {None: NORM_NONE, "none": NORM_NONE, "group": NORM_GROUP,
+            "layer_channels": NORM_LAYER_CHANNELS}[norm]
+    return NormDesc(code, groups if code == NORM_GROUP else 0, eps,
+                    EPI_ROWMIN_BIAS if rowmin else EPI_NONE)
+
+
+def out_len(desc: ConvDesc) -> int:
+    return int(load_library().c1g_out_len(ctypes.byref(desc)))
+
+
+def route(desc: ConvDesc, norm: NormDesc = None) -> str:
+    return load_library().c1g_route(ctypes.byref(desc),
+                                    ctypes.byref(norm) if norm is not None else None).decode()
+
+
+def check(desc: ConvDesc, norm: NormDesc = None, ws_bytes: int = 1 << 62) -> int:
+    return int(load_library().c1g_check(ctypes.byref(desc),
+                                        ctypes.byref(norm) if norm is not None else None,
+                                        ws_bytes))
+
+
+def conv1d_workspace_size(desc: ConvDesc) -> int:
+    return int(load_library().c1g_conv1d_workspace_size(ctypes.byref(desc)))
+
+
+def conv1d_gn_workspace_size(desc: ConvDesc, norm: NormDesc) -> int:
+    return int(load_library().c1g_conv1d_gn_workspace_size(ctypes.byref(desc),
+                                                           ctypes.byref(norm)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _raise(status, where):
+    if status != 0:
+        raise C1GError(status, where)
+
+
+def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation):
+    if x.dim() != 3 or w.dim() != 3:
+        raise ValueError("x must be [N, C_in, T] and w [C_out, C_in, K]")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if x.dtype == torch.float32:
+        dt = C1G_F32
+    elif x.dtype == torch.bfloat16:
+        dt = C1G_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, "x", None, x.device)
+    _need(w, "w", x.dtype, x.device)
+    N, C_in, T = x.shape
+    C_out, C_in_w, K = w.shape
+    if C_in_w != C_in:
+        raise ValueError("x and w disagree on C_in")
+    desc = make_desc(N, C_in, C_out, T, K, stride=stride, dilation=dilation, padding=padding,
+                     pad_left=pad_left, pad_right=pad_right, causal=causal, dtype=dt)
+    return desc
+
+
+# ----------------------------------------------------------------- entry points
+def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
+                   causal=False, dilation=1, out=None, workspace=None):
+    """y = conv1d(x, w) + bias, fp32 output [N, C_out, T_out]."""
+    lib = load_library()
+    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation)
+    _need(bias, "bias", torch.float32, x.device)
+    T_out = lib.c1g_out_len(ctypes.byref(desc))
+    if T_out < 1:
+        _raise(1, "conv1d_forward")
+    if out is None:
+        out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=torch.float32)
+    _need(out, "out", torch.float32, x.device)
+    ws_bytes = lib.c1g_conv1d_workspace_size(ctypes.byref(desc))
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+    st = lib.conv1d_forward(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(out),
+                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                            _stream(x.device))
+    _raise(st, "conv1d_forward")
+    return out
+
+
+def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
+                      causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
+                      beta=None, rowmin_bias=None, return_stats=False, out=None,
+                      workspace=None):
+    """conv -> GroupNorm / LayerNorm over channels / none -> optional row-min + bias.
+
+    Returns out [N, C_out, T_out] (fp32), or (out, mean, rstd) with
+    return_stats=True (mean/rstd [N, G] for GroupNorm, [N, T_out] for the
+    channel LayerNorm)."""
+    lib = load_library()
+    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation)
+    nd = make_norm(norm, groups, eps, rowmin_bias is not None)
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
+        _need(t, nm, torch.float32, x.device)
+    T_out = lib.c1g_out_len(ctypes.byref(desc))
+    if T_out < 1:
+        _raise(1, "conv1d_gn_forward")
+    if out is None:
+        out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=torch.float32)
+    _need(out, "out", torch.float32, x.device)
+    mean = rstd = None
+    if return_stats and nd.norm != NORM_NONE:
+        shp = (desc.N, groups) if nd.norm == NORM_GROUP else (desc.N, T_out)
+        mean = torch.empty(shp, device=x.device, dtype=torch.float32)
+        rstd = torch.empty(shp, device=x.device, dtype=torch.float32)
+    ws_bytes = lib.c1g_conv1d_gn_workspace_size(ctypes.byref(desc), ctypes.byref(nd))
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+    st = lib.conv1d_gn_forward(ctypes.byref(desc), ctypes.byref(nd), _ptr(x), _ptr(w),
+                               _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(rowmin_bias),
+                               _ptr(out), _ptr(mean), _ptr(rstd), _ptr(workspace),
+                               workspace.numel() if workspace is not None else 0,
+                               _stream(x.device))
+    _raise(st, "conv1d_gn_forward")
+    return (out, mean, rstd) if return_stats else out
+
+
+def gn_stats(y, groups, eps=1e-5):
+    """GroupNorm statistics of y [N, C, L]: (mean[N,G], rstd[N,G])."""
+    lib = load_library()
+    if y.dim() != 3 or not y.is_cuda:
+        raise ValueError("y must be a [N, C, L] device tensor")
+    _need(y, "y", torch.float32, y.device)
+    N, C, L = y.shape
+    mean = torch.empty((N, groups), device=y.device, dtype=torch.float32)
+    rstd = torch.empty_like(mean)
+    ws_bytes = lib.c1g_gn_stats_workspace_size(N, C, L, groups)
+    ws = torch.empty(ws_bytes, device=y.device, dtype=torch.uint8) if ws_bytes else None
+    st = lib.gn_stats(N, C, L, groups, eps, _ptr(y), _ptr(mean), _ptr(rstd), _ptr(ws), ws_bytes,
+                      _stream(y.device))
+    _raise(st, "gn_stats")
+    return mean, rstd
+
+
+def gn_apply(y, mean, rstd, gamma=None, beta=None, groups=None, out=None):
+    """out = (y - mean) * rstd * gamma + beta with per-(n, group) statistics.
+    ``out=y`` normalises in place."""
+    lib = load_library()
+    if y.dim() != 3 or not y.is_cuda:
+        raise ValueError("y must be a [N, C, L] device tensor")
+    _need(y, "y", torch.float32, y.device)
+    N, C, L = y.shape
+    G = groups if groups is not None else mean.shape[1]
+    for t, nm in ((mean, "mean"), (rstd, "rstd"), (gamma, "gamma"), (beta, "beta")):
+        _need(t, nm, torch.float32, y.device)
+    if out is None:
+        out = torch.empty_like(y)
+    _need(out, "out", torch.float32, y.device)
+    st = lib.gn_apply(N, C, L, G, _ptr(y), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(beta),
+                      _ptr(out), _stream(y.device))
+    _raise(st, "gn_apply")
+    return out

@@ -1,0 +1,329 @@
+// C ABI of the conv1d -> GroupNorm library: validation, planning (output
+// length, route, workspace layout) and launches on the caller's stream.
+// Declarations and the contract of every entry point: include/conv1d_gn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/conv1d_gn.h"
+#include "launch.hpp"
+
+using namespace c1g;
+
+namespace {
+
+enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT };
+
+struct Plan {
+  int status = C1G_OK;
+  int route = R_INVALID;
+  int64_t T_out = -1;
+  bool bf16 = false;
+  int norm = C1G_NORM_NONE, epi = C1G_EPI_NONE;
+  int n_chunks = 0, n_ttiles = 0, n_ctiles = 0, tm = 0, tn = 0;
+  size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, total = 0;
+};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t out_len(const c1g_conv_desc* d) {
+  if (!d) return -1;
+  if (d->N < 1 || d->C_in < 1 || d->C_out < 1 || d->T < 1) return -1;
+  if (d->K < 1 || d->stride < 1 || d->dilation < 1 || d->pad_left < 0 || d->pad_right < 0)
+    return -1;
+  const int64_t span =
+      d->T + d->pad_left + d->pad_right - (int64_t)d->dilation * (d->K - 1) - 1;
+  if (span < 0) return -1;
+  return span / d->stride + 1;
+}
+
+// Everything the entry points need to know before touching the device.
+Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
+  Plan p;
+  p.T_out = out_len(d);
+  if (p.T_out < 1) { p.status = C1G_ERR_INVALID_ARG; return p; }
+  if (d->dtype != C1G_F32 && d->dtype != C1G_BF16) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+  p.bf16 = d->dtype == C1G_BF16;
+  if (nd) {
+    p.norm = nd->norm;
+    p.epi = nd->epilogue;
+    if (p.norm < C1G_NORM_NONE || p.norm > C1G_NORM_LAYER_CHANNELS ||
+        p.epi < C1G_EPI_NONE || p.epi > C1G_EPI_ROWMIN_BIAS) {
+      p.status = C1G_ERR_INVALID_ARG;
+      return p;
+    }
+    if (p.norm == C1G_NORM_GROUP && (nd->G < 1 || d->C_out % nd->G != 0)) {
+      p.status = C1G_ERR_INVALID_ARG;
+      return p;
+    }
+    if (p.norm != C1G_NORM_NONE && !(nd->eps > 0.f && std::isfinite(nd->eps))) {
+      p.status = C1G_ERR_INVALID_ARG;
+      return p;
+    }
+  }
+  // size limits of the kernels' index arithmetic and grids
+  const uint64_t n_out = (uint64_t)d->N * (uint64_t)d->C_out * (uint64_t)p.T_out;
+  if (n_out >= (1ull << 32) || d->N > 65535 || d->C_out > (1ll << 30) || d->C_in > (1ll << 30)) {
+    p.status = C1G_ERR_UNSUPPORTED;
+    return p;
+  }
+
+  // route
+  const bool want_gn = p.norm == C1G_NORM_GROUP, want_ln = p.norm == C1G_NORM_LAYER_CHANNELS;
+  if (!p.bf16 && want_gn && p.epi == C1G_EPI_NONE &&
+      fused_gn_supported(d->C_out, nd->G, p.T_out, d->stride, d->K, d->dilation)) {
+    p.route = R_FUSED;
+    p.total = 0;
+    return p;
+  }
+  p.route = (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE) ? R_CONV_ONLY : R_SPLIT;
+
+  size_t pack_bytes;
+  if (p.bf16) {
+    p.status = C1G_ERR_UNSUPPORTED;  // bf16 kernels are built in a later step
+    return p;
+  } else {
+    if (d->K > 8) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+    const int64_t xw = (int64_t)(ConvF32Cfg::TM - 1) * d->stride +
+                       (int64_t)(d->K - 1) * d->dilation + 1;
+    if (xw > conv_f32_window_cap(d->stride)) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+    p.tm = ConvF32Cfg::TM;
+    p.tn = ConvF32Cfg::TN;
+    p.n_chunks = (int)((d->C_in + ConvF32Cfg::CK - 1) / ConvF32Cfg::CK);
+    pack_bytes = conv_f32_packed_bytes(d->C_in, d->C_out, d->K);
+  }
+  const int64_t n_tt = (p.T_out + p.tm - 1) / p.tm, n_ct = (d->C_out + p.tn - 1) / p.tn;
+  if (n_tt > (1ll << 31) - 1 || n_ct > 65535) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+  p.n_ttiles = (int)n_tt;
+  p.n_ctiles = (int)n_ct;
+
+  size_t off = 0;
+  p.off_pack = off;
+  off = align_up(off + pack_bytes);
+  size_t part_bytes = 0, stat_elems = 0;
+  if (want_gn) {
+    part_bytes = (size_t)d->N * d->C_out * p.n_ttiles * 2 * sizeof(float);
+    stat_elems = (size_t)d->N * nd->G;
+  } else if (want_ln) {
+    part_bytes = (size_t)d->N * p.n_ctiles * p.T_out * 2 * sizeof(float);
+    stat_elems = (size_t)d->N * p.T_out;
+  }
+  p.off_part = off;
+  off = align_up(off + part_bytes);
+  p.off_mean = off;
+  off = align_up(off + stat_elems * sizeof(float));
+  p.off_rstd = off;
+  off = align_up(off + stat_elems * sizeof(float));
+  p.total = (p.route == R_CONV_ONLY) ? align_up(pack_bytes) : off;
+  return p;
+}
+
+bool aligned(const void* p, size_t a) { return (((uintptr_t)p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? C1G_OK : C1G_ERR_HIP; }
+
+// Convolution into y (with the requested statistics epilogue); packs weights first.
+int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w,
+             const float* bias, float* y, char* ws, int epi, hipStream_t s) {
+  ConvArgs a;
+  a.x = x;
+  a.wp = ws + p.off_pack;
+  a.bias = bias;
+  a.y = y;
+  a.part = (float*)(ws + p.off_part);
+  a.N = d->N;
+  a.C_in = d->C_in;
+  a.C_out = d->C_out;
+  a.T = d->T;
+  a.T_out = p.T_out;
+  a.K = d->K;
+  a.stride = d->stride;
+  a.dilation = d->dilation;
+  a.pad_left = d->pad_left;
+  a.n_chunks = p.n_chunks;
+  a.n_ttiles = p.n_ttiles;
+  a.n_ctiles = p.n_ctiles;
+  hipError_t e = conv_f32_pack((const float*)w, (float*)(ws + p.off_pack), d->C_in, d->C_out,
+                               d->K, s);
+  if (e != hipSuccess) return C1G_ERR_HIP;
+  return hip_status(conv_f32_launch(a, epi, s));
+}
+
+const char* route_name(int r) {
+  switch (r) {
+    case R_CONV_ONLY: return "conv_only";
+    case R_FUSED: return "fused_single_pass";
+    case R_SPLIT: return "split";
+    default: return "invalid";
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t c1g_out_len(const c1g_conv_desc* d) { return out_len(d); }
+
+int c1g_check(const c1g_conv_desc* d, const c1g_norm_desc* norm, size_t ws_bytes) {
+  if (!d) return C1G_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, norm);
+  if (p.status != C1G_OK) return p.status;
+  if (ws_bytes < p.total) return C1G_ERR_WORKSPACE;
+  return C1G_OK;
+}
+
+const char* c1g_route(const c1g_conv_desc* d, const c1g_norm_desc* norm) {
+  if (!d) return "invalid";
+  const Plan p = make_plan(d, norm);
+  return p.status == C1G_OK ? route_name(p.route) : "invalid";
+}
+
+size_t c1g_conv1d_workspace_size(const c1g_conv_desc* d) {
+  if (!d) return 0;
+  const Plan p = make_plan(d, nullptr);
+  return p.status == C1G_OK ? p.total : 0;
+}
+
+size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc* norm) {
+  if (!d) return 0;
+  const Plan p = make_plan(d, norm);
+  return p.status == C1G_OK ? p.total : 0;
+}
+
+int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
+                   float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return C1G_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, nullptr);
+  if (p.status != C1G_OK) return p.status;
+  if (!x || !w || !y) return C1G_ERR_INVALID_ARG;
+  const size_t es = p.bf16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(w, es) || !aligned(y, 4) || (bias && !aligned(bias, 4)))
+    return C1G_ERR_MISALIGNED;
+  if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
+  return run_conv(p, d, x, w, bias, y, (char*)ws, EPI_STORE, (hipStream_t)stream);
+}
+
+size_t c1g_gn_stats_workspace_size(int64_t N, int64_t C, int64_t L, int32_t G) {
+  (void)N; (void)C; (void)L; (void)G;
+  return 0;
+}
+
+int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float* y, float* mean,
+             float* rstd, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0 || !(eps > 0.f && std::isfinite(eps)))
+    return C1G_ERR_INVALID_ARG;
+  if (!y || !mean || !rstd) return C1G_ERR_INVALID_ARG;
+  if ((uint64_t)N * G > 0x7fffffffull) return C1G_ERR_UNSUPPORTED;
+  if (!aligned(y, 4) || !aligned(mean, 4) || !aligned(rstd, 4)) return C1G_ERR_MISALIGNED;
+  return hip_status(gn_stats_launch(y, N, C, L, G, eps, mean, rstd, (hipStream_t)stream));
+}
+
+int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const float* mean,
+             const float* rstd, const float* gamma, const float* beta, float* out,
+             void* stream) {
+  if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
+  if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
+  if ((uint64_t)N * C * L >= (1ull << 32) || C > (1ll << 31) || L > (1ll << 31))
+    return C1G_ERR_UNSUPPORTED;
+  if (!aligned(y, 4) || !aligned(out, 4) || !aligned(mean, 4) || !aligned(rstd, 4) ||
+      (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
+    return C1G_ERR_MISALIGNED;
+  return hip_status(
+      gn_apply_launch(y, mean, rstd, gamma, beta, out, N, C, L, G, (hipStream_t)stream));
+}
+
+int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
+                      const void* w, const float* bias, const float* gamma, const float* beta,
+                      const float* bias2, float* out, float* mean_out, float* rstd_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!d || !nd) return C1G_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, nd);
+  if (p.status != C1G_OK) return p.status;
+  if (!x || !w || !out) return C1G_ERR_INVALID_ARG;
+  if (p.epi == C1G_EPI_ROWMIN_BIAS && !bias2) return C1G_ERR_INVALID_ARG;
+  const size_t es = p.bf16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(w, es) || !aligned(out, 4) || (bias && !aligned(bias, 4)) ||
+      (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)) ||
+      (bias2 && !aligned(bias2, 4)) || (mean_out && !aligned(mean_out, 4)) ||
+      (rstd_out && !aligned(rstd_out, 4)))
+    return C1G_ERR_MISALIGNED;
+  if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+
+  if (p.route == R_FUSED) {
+    FusedArgs a;
+    a.x = (const float*)x;
+    a.w = (const float*)w;
+    a.bias = bias;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.out = out;
+    a.mean_out = mean_out;
+    a.rstd_out = rstd_out;
+    a.N = d->N;
+    a.C_in = d->C_in;
+    a.C_out = d->C_out;
+    a.T = d->T;
+    a.T_out = p.T_out;
+    a.K = d->K;
+    a.stride = d->stride;
+    a.dilation = d->dilation;
+    a.pad_left = d->pad_left;
+    a.G = nd->G;
+    a.eps = nd->eps;
+    return hip_status(fused_gn_launch(a, s));
+  }
+  if (p.route == R_CONV_ONLY)
+    return run_conv(p, d, x, w, bias, out, wsb, EPI_STORE, s);
+
+  // split route: conv (+ partial statistics) into out, merge, then in-place passes
+  const int conv_epi = p.norm == C1G_NORM_GROUP ? EPI_GN_PART
+                       : p.norm == C1G_NORM_LAYER_CHANNELS ? EPI_LN_PART : EPI_STORE;
+  int st = run_conv(p, d, x, w, bias, out, wsb, conv_epi, s);
+  if (st != C1G_OK) return st;
+  float* mean = mean_out ? mean_out : (float*)(wsb + p.off_mean);
+  float* rstd = rstd_out ? rstd_out : (float*)(wsb + p.off_rstd);
+  const float* part = (const float*)(wsb + p.off_part);
+  hipError_t e = hipSuccess;
+  if (p.norm == C1G_NORM_GROUP) {
+    e = gn_merge_launch(part, d->N, d->C_out, p.T_out, nd->G, p.n_ttiles, p.tm, nd->eps, mean,
+                        rstd, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    if (p.epi == C1G_EPI_NONE)
+      e = gn_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, p.T_out, nd->G, s);
+    else
+      e = rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, p.T_out,
+                             nd->G, 1, s);
+  } else if (p.norm == C1G_NORM_LAYER_CHANNELS) {
+    e = ln_merge_launch(part, d->N, d->C_out, p.T_out, p.n_ctiles, p.tn, nd->eps, mean, rstd, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    if (p.epi == C1G_EPI_NONE)
+      e = ln_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, p.T_out, s);
+    else
+      e = rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, p.T_out,
+                             0, 2, s);
+  } else {  // no norm, row-min epilogue only
+    e = rowmin_bias_launch(out, nullptr, nullptr, nullptr, nullptr, bias2, out, d->N, d->C_out,
+                           p.T_out, 0, 0, s);
+  }
+  return hip_status(e);
+}
+
+const char* c1g_status_string(int status) {
+  switch (status) {
+    case C1G_OK: return "ok";
+    case C1G_ERR_INVALID_ARG: return "invalid argument";
+    case C1G_ERR_UNSUPPORTED: return "unsupported configuration";
+    case C1G_ERR_WORKSPACE: return "workspace missing or too small";
+    case C1G_ERR_MISALIGNED: return "misaligned pointer";
+    case C1G_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device-side building blocks shared by the gfx950 kernels of the conv1d ->
+// GroupNorm library: vector types, MFMA wrappers, wave reductions and the
+// pairwise (count, mean, M2) merge used by every statistics reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace c1g {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// v_mfma_f32_16x16x4_f32.  Lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// the 16x16 result lives in lane (j + 16*(i/4)), register i%4.
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16 (gfx950).  Lane l supplies A[l%16][8*(l/16)+0..7]
+// and B[8*(l/16)+0..7][l%16]; result layout as above.
+__device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+// Running statistics of a set of values: count, mean and the sum of squared
+// deviations from the mean (M2).  merge() is the pairwise update for two
+// disjoint sets (Chan, Golub and LeVeque); it is exact in real arithmetic and
+// its result does not depend on how a set was split, only the rounding does.
+struct Stats {
+  float n, mean, m2;
+};
+
+__device__ __forceinline__ Stats stats_merge(Stats a, Stats b) {
+  float n = a.n + b.n;
+  if (b.n == 0.f) return a;
+  if (a.n == 0.f) return b;
+  float delta = b.mean - a.mean;
+  float fb = b.n / n;
+  Stats r;
+  r.n = n;
+  r.mean = a.mean + delta * fb;
+  r.m2 = a.m2 + b.m2 + delta * delta * a.n * fb;
+  return r;
+}
+
+// Exact-count sum over lanes whose indices differ only in the given mask bits.
+template <int MASK>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1)
+    if (MASK & m) v += shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+}  // namespace c1g

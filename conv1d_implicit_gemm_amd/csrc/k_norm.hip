@@ -1,0 +1,360 @@
+// Normalisation kernels of the split path (all HBM- or latency-bound):
+//   gn_merge   per-(n, c, t-tile) partials -> GroupNorm mean/rstd per (n, g)
+//   gn_stats   GroupNorm mean/rstd straight from an fp32 y (one pass)
+//   gn_apply   out = (y - mean) * rstd * gamma + beta, per (n, g) statistics
+//   ln_merge   per-(n, c-tile, t) partials -> LayerNorm-over-channels mean/rstd
+//   ln_apply   the same affine with per-(n, t) statistics
+//   rowmin     min over channels of the normalised value, plus bias2 broadcast
+//
+// Statistics follow "Kimi-K2.6 l2_p35" (GroupNorm over C/G channels x L per
+// (n, g), population variance, eps inside the square root) and the
+// statistics-then-apply split of "Kimi-K2.6 l2_p3"; the row-min epilogue is
+// "Kimi-K2.6 l2_p75" (min over channels after the affine, bias2 broadcast).
+// Every reduction runs in a fixed order (sequential per thread, then a fixed
+// tree), so results are bit-identical from run to run.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace c1g {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ Stats block_merge(Stats st, Stats* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = st;
+  __syncthreads();
+#pragma unroll
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if (tid < s) sh[tid] = stats_merge(sh[tid], sh[tid + s]);
+    __syncthreads();
+  }
+  return sh[0];
+}
+
+// Unsigned 32-bit division by a run-time constant (Granlund & Montgomery,
+// round-up multiplier): q = (mulhi(m, n) + n) >> l with l = ceil(log2(d)).
+struct FastDiv {
+  uint32_t d, m, l;
+  static FastDiv make(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while (l < 32 && (1ull << l) < d) ++l;
+    f.l = l;
+    f.m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+    return f;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint64_t t = ((uint64_t)n * m) >> 32;
+    return (uint32_t)((t + n) >> l);
+  }
+};
+
+__global__ __launch_bounds__(NT) void gn_merge_kernel(const float* __restrict__ part, int64_t C,
+                                                      int64_t L, int32_t G, int32_t n_ttiles,
+                                                      int32_t tm, float eps, float* mean,
+                                                      float* rstd) {
+  __shared__ Stats sh[NT];
+  const int64_t ng = blockIdx.x;
+  const int64_t n = ng / G, g = ng - n * G;
+  const int64_t cpg = C / G;
+  const int64_t P = cpg * n_ttiles;
+  const float* base = part + ((n * C + g * cpg) * n_ttiles) * 2;
+  Stats st = {0.f, 0.f, 0.f};
+  for (int64_t p = threadIdx.x; p < P; p += NT) {
+    const int tt = (int)(p % n_ttiles);
+    const int64_t cntl = L - (int64_t)tt * tm;
+    const float cnt = (float)(cntl < tm ? cntl : tm);
+    const f32x2 v = *(const f32x2*)(base + 2 * p);
+    st = stats_merge(st, Stats{cnt, v[0], v[1]});
+  }
+  st = block_merge(st, sh);
+  if (threadIdx.x == 0) {
+    mean[ng] = st.mean;
+    rstd[ng] = 1.0f / sqrtf(st.m2 / st.n + eps);
+  }
+}
+
+// Statistics of 16 values as one batch (two passes over registers).
+__device__ __forceinline__ Stats batch16(const f32x4 v[4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  const float mu = s * (1.0f / 16.0f);
+  float m2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float dv = v[i][e] - mu;
+      m2 += dv * dv;
+    }
+  return Stats{16.f, mu, m2};
+}
+
+__global__ __launch_bounds__(NT) void gn_stats_kernel(const float* __restrict__ y, int64_t C,
+                                                      int64_t L, int32_t G, float eps,
+                                                      float* mean, float* rstd) {
+  __shared__ Stats sh[NT];
+  const int64_t ng = blockIdx.x;
+  const int64_t n = ng / G, g = ng - n * G;
+  const int64_t cpg = C / G;
+  const int64_t len = cpg * L;
+  const float* p = y + (n * C + g * cpg) * L;  // a group's values are contiguous
+  int64_t head = (int64_t)(((16 - (((uintptr_t)p) & 15)) & 15) >> 2);
+  if (head > len) head = len;
+  const int tid = threadIdx.x;
+  Stats st = {0.f, 0.f, 0.f};
+  if (tid < head) st = Stats{1.f, p[tid], 0.f};
+  const f32x4* pv = (const f32x4*)(p + head);
+  const int64_t nvec = (len - head) >> 2;
+  const int64_t nb = nvec >> 2;  // batches of 4 vectors per thread-iteration
+  for (int64_t b = tid; b < nb; b += NT) {
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = pv[4 * b + i];
+    st = stats_merge(st, batch16(v));
+  }
+  for (int64_t q = 4 * nb + tid; q < nvec; q += NT) {
+    const f32x4 v = pv[q];
+    const float mu = ((v[0] + v[1]) + (v[2] + v[3])) * 0.25f;
+    float m2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { const float dv = v[e] - mu; m2 += dv * dv; }
+    st = stats_merge(st, Stats{4.f, mu, m2});
+  }
+  for (int64_t e = head + 4 * nvec + tid; e < len; e += NT) st = stats_merge(st, Stats{1.f, p[e], 0.f});
+  st = block_merge(st, sh);
+  if (tid == 0) {
+    mean[ng] = st.mean;
+    rstd[ng] = 1.0f / sqrtf(st.m2 / st.n + eps);
+  }
+}
+
+// mode 1: statistics per (n, g); mode 2: per (n, l)
+template <int MODE, bool VEC>
+__global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
+                                                   const float* __restrict__ mean,
+                                                   const float* __restrict__ rstd,
+                                                   const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, float* out,
+                                                   uint32_t total, FastDiv divL, FastDiv divC,
+                                                   uint32_t C, uint32_t L, uint32_t G,
+                                                   uint32_t cpg) {
+  const uint32_t step = gridDim.x * NT;
+  if (VEC) {
+    const uint32_t nv = total >> 2;
+    for (uint32_t v = blockIdx.x * NT + threadIdx.x; v < nv; v += step) {
+      const uint32_t e = v << 2;
+      const uint32_t row = divL.div(e);
+      const uint32_t l = e - row * L;
+      const uint32_t n = divC.div(row);
+      const uint32_t c = row - n * C;
+      const float ga = gamma ? gamma[c] : 1.f, be = beta ? beta[c] : 0.f;
+      const f32x4 yv = *(const f32x4*)(y + e);
+      f32x4 z;
+      if (MODE == 1) {
+        const uint32_t sidx = n * G + c / cpg;
+        const float mu = mean[sidx], sc = rstd[sidx] * ga;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (yv[i] - mu) * sc + be;
+      } else {
+        const f32x4 mu = *(const f32x4*)(mean + (size_t)n * L + l);
+        const f32x4 rs = *(const f32x4*)(rstd + (size_t)n * L + l);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (yv[i] - mu[i]) * (rs[i] * ga) + be;
+      }
+      *(f32x4*)(out + e) = z;
+    }
+  } else {
+    for (uint32_t e = blockIdx.x * NT + threadIdx.x; e < total; e += step) {
+      const uint32_t row = divL.div(e);
+      const uint32_t l = e - row * L;
+      const uint32_t n = divC.div(row);
+      const uint32_t c = row - n * C;
+      const float ga = gamma ? gamma[c] : 1.f, be = beta ? beta[c] : 0.f;
+      float mu, rs;
+      if (MODE == 1) {
+        mu = mean[n * G + c / cpg];
+        rs = rstd[n * G + c / cpg];
+      } else {
+        mu = mean[(size_t)n * L + l];
+        rs = rstd[(size_t)n * L + l];
+      }
+      out[e] = (y[e] - mu) * (rs * ga) + be;
+    }
+  }
+}
+
+__global__ __launch_bounds__(NT) void ln_merge_kernel(const float* __restrict__ part, int64_t N,
+                                                      int64_t C, int64_t L, int32_t n_ctiles,
+                                                      int32_t tn, float eps, float* mean,
+                                                      float* rstd) {
+  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (idx >= N * L) return;
+  const int64_t n = idx / L, l = idx - n * L;
+  Stats st = {0.f, 0.f, 0.f};
+  for (int ct = 0; ct < n_ctiles; ++ct) {
+    const int64_t rem = C - (int64_t)ct * tn;
+    const float cnt = (float)(rem < tn ? rem : tn);
+    const f32x2 v = *(const f32x2*)(part + ((n * n_ctiles + ct) * L + l) * 2);
+    st = stats_merge(st, Stats{cnt, v[0], v[1]});
+  }
+  mean[idx] = st.mean;
+  rstd[idx] = 1.0f / sqrtf(st.m2 / st.n + eps);
+}
+
+template <int KIND>
+__device__ __forceinline__ float normed(float v, const float* mean, const float* rstd,
+                                        const float* gamma, const float* beta, int64_t n,
+                                        int64_t c, int64_t l, int64_t L, int64_t G,
+                                        int64_t cpg) {
+  if (KIND == 0) return v;
+  const float ga = gamma ? gamma[c] : 1.f, be = beta ? beta[c] : 0.f;
+  const int64_t si = (KIND == 1) ? n * G + c / cpg : n * L + l;
+  return (v - mean[si]) * (rstd[si] * ga) + be;
+}
+
+// one thread per (n, l): two passes over the channels
+template <int KIND>
+__global__ __launch_bounds__(NT) void rowmin_kernel(const float* __restrict__ y,
+                                                    const float* mean, const float* rstd,
+                                                    const float* gamma, const float* beta,
+                                                    const float* __restrict__ bias2, float* out,
+                                                    int64_t N, int64_t C, int64_t L, int64_t G) {
+  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (idx >= N * L) return;
+  const int64_t n = idx / L, l = idx - n * L;
+  const int64_t cpg = G > 0 ? C / G : 1;
+  float m = __builtin_inff();
+  for (int64_t c = 0; c < C; ++c) {
+    const float z = normed<KIND>(y[(n * C + c) * L + l], mean, rstd, gamma, beta, n, c, l, L,
+                                 G, cpg);
+    m = z < m ? z : m;
+  }
+  for (int64_t c = 0; c < C; ++c) out[(n * C + c) * L + l] = m + bias2[c];
+}
+
+// L == 1: one workgroup per row n, threads over channels
+template <int KIND>
+__global__ __launch_bounds__(NT) void rowmin_l1_kernel(const float* __restrict__ y,
+                                                       const float* mean, const float* rstd,
+                                                       const float* gamma, const float* beta,
+                                                       const float* __restrict__ bias2,
+                                                       float* out, int64_t C, int64_t G) {
+  __shared__ float sh[NT];
+  const int64_t n = blockIdx.x;
+  const int64_t cpg = G > 0 ? C / G : 1;
+  float m = __builtin_inff();
+  for (int64_t c = threadIdx.x; c < C; c += NT) {
+    const float z = normed<KIND>(y[n * C + c], mean, rstd, gamma, beta, n, c, 0, 1, G, cpg);
+    m = z < m ? z : m;
+  }
+  sh[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] = fminf(sh[threadIdx.x], sh[threadIdx.x + s]);
+    __syncthreads();
+  }
+  m = sh[0];
+  for (int64_t c = threadIdx.x; c < C; c += NT) out[n * C + c] = m + bias2[c];
+}
+
+unsigned grid_for(uint64_t work) {
+  uint64_t b = (work + NT - 1) / NT;
+  const uint64_t cap = 256ull * 64;  // enough resident waves to saturate HBM
+  return (unsigned)(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+template <int MODE>
+hipError_t apply_launch(const float* y, const float* mean, const float* rstd,
+                        const float* gamma, const float* beta, float* out, int64_t N, int64_t C,
+                        int64_t L, int32_t G, hipStream_t s) {
+  const uint64_t total = (uint64_t)N * C * L;
+  if (total >= (1ull << 32)) return hipErrorInvalidValue;
+  const FastDiv dl = FastDiv::make((uint32_t)L), dc = FastDiv::make((uint32_t)C);
+  const uint32_t cpg = (MODE == 1) ? (uint32_t)(C / G) : 1u;
+  const bool vec = (L % 4 == 0) && ((((uintptr_t)y) & 15) == 0) && ((((uintptr_t)out) & 15) == 0) &&
+                   (MODE == 1 || ((((uintptr_t)mean) & 15) == 0 && (((uintptr_t)rstd) & 15) == 0));
+  if (vec) {
+    hipLaunchKernelGGL((apply_kernel<MODE, true>), dim3(grid_for(total / 4)), dim3(NT), 0, s, y,
+                       mean, rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
+                       (uint32_t)L, (uint32_t)G, cpg);
+  } else {
+    hipLaunchKernelGGL((apply_kernel<MODE, false>), dim3(grid_for(total)), dim3(NT), 0, s, y,
+                       mean, rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
+                       (uint32_t)L, (uint32_t)G, cpg);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t gn_merge_launch(const float* part, int64_t N, int64_t C, int64_t L, int32_t G,
+                           int32_t n_ttiles, int32_t tm, float eps, float* mean, float* rstd,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(gn_merge_kernel, dim3((unsigned)(N * G)), dim3(NT), 0, s, part, C, L, G,
+                     n_ttiles, tm, eps, mean, rstd);
+  return hipGetLastError();
+}
+
+hipError_t gn_stats_launch(const float* y, int64_t N, int64_t C, int64_t L, int32_t G,
+                           float eps, float* mean, float* rstd, hipStream_t s) {
+  hipLaunchKernelGGL(gn_stats_kernel, dim3((unsigned)(N * G)), dim3(NT), 0, s, y, C, L, G, eps,
+                     mean, rstd);
+  return hipGetLastError();
+}
+
+hipError_t gn_apply_launch(const float* y, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, float* out, int64_t N,
+                           int64_t C, int64_t L, int32_t G, hipStream_t s) {
+  return apply_launch<1>(y, mean, rstd, gamma, beta, out, N, C, L, G, s);
+}
+
+hipError_t ln_merge_launch(const float* part, int64_t N, int64_t C, int64_t L,
+                           int32_t n_ctiles, int32_t tn, float eps, float* mean, float* rstd,
+                           hipStream_t s) {
+  const int64_t work = N * L;
+  hipLaunchKernelGGL(ln_merge_kernel, dim3((unsigned)((work + NT - 1) / NT)), dim3(NT), 0, s,
+                     part, N, C, L, n_ctiles, tn, eps, mean, rstd);
+  return hipGetLastError();
+}
+
+hipError_t ln_apply_launch(const float* y, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, float* out, int64_t N,
+                           int64_t C, int64_t L, hipStream_t s) {
+  return apply_launch<2>(y, mean, rstd, gamma, beta, out, N, C, L, 1, s);
+}
+
+hipError_t rowmin_bias_launch(const float* y, const float* mean, const float* rstd,
+                              const float* gamma, const float* beta, const float* bias2,
+                              float* out, int64_t N, int64_t C, int64_t L, int32_t G,
+                              int norm_kind, hipStream_t s) {
+  if (L == 1) {
+    dim3 grid((unsigned)N);
+    if (norm_kind == 1)
+      hipLaunchKernelGGL(rowmin_l1_kernel<1>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
+                         bias2, out, C, (int64_t)G);
+    else if (norm_kind == 2)
+      hipLaunchKernelGGL(rowmin_l1_kernel<2>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
+                         bias2, out, C, (int64_t)G);
+    else
+      hipLaunchKernelGGL(rowmin_l1_kernel<0>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
+                         bias2, out, C, (int64_t)G);
+  } else {
+    dim3 grid((unsigned)((N * L + NT - 1) / NT));
+    if (norm_kind == 1)
+      hipLaunchKernelGGL(rowmin_kernel<1>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
+                         bias2, out, N, C, L, (int64_t)G);
+    else if (norm_kind == 2)
+      hipLaunchKernelGGL(rowmin_kernel<2>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
+                         bias2, out, N, C, L, (int64_t)G);
+    else
+      hipLaunchKernelGGL(rowmin_kernel<0>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
+                         bias2, out, N, C, L, (int64_t)G);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace c1g

@@ -1,0 +1,103 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernel
+// translation units.  Every launcher enqueues on the given stream, assumes
+// its arguments were validated by the planner, and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace c1g {
+
+// Epilogue of the split-path convolution kernels.
+enum ConvEpi : int {
+  EPI_STORE = 0,      // y = acc + bias
+  EPI_GN_PART = 1,    // y, plus per-(n, channel, t-tile) (mean, M2) partials
+  EPI_LN_PART = 2,    // y, plus per-(n, c-tile, t) (mean, M2) partials
+};
+
+// Geometry + pointers of one implicit-GEMM convolution launch.
+struct ConvArgs {
+  const void* x;       // [N, C_in, T] fp32 or bf16
+  const void* wp;      // packed weights (layout owned by the kernel file)
+  const float* bias;   // [C_out] or nullptr
+  float* y;            // [N, C_out, T_out]
+  float* part;         // partial statistics (EPI_GN_PART / EPI_LN_PART)
+  int64_t N, C_in, C_out, T, T_out;
+  int32_t K, stride, dilation, pad_left;
+  int32_t n_chunks;    // ceil(C_in / CK)
+  int32_t n_ttiles;    // ceil(T_out / TM)
+  int32_t n_ctiles;    // ceil(C_out / TN)
+};
+
+// ---- fp32 split-path convolution (k_conv_f32.hip)
+// Tile geometry: TM output positions x TN output channels, CK input channels
+// per K-chunk.  xcap is the widest input window one tile may need.
+struct ConvF32Cfg {
+  static constexpr int TM = 128, TN = 128, CK = 8;
+};
+int conv_f32_window_cap(int stride);  // largest input window a tile supports
+size_t conv_f32_packed_bytes(int64_t C_in, int64_t C_out, int K);
+hipError_t conv_f32_pack(const float* w, float* wp, int64_t C_in, int64_t C_out, int K,
+                         hipStream_t s);
+hipError_t conv_f32_launch(const ConvArgs& a, int epi, hipStream_t s);
+
+// ---- bf16 split-path convolution (k_conv_bf16.hip)
+struct ConvBf16Cfg {
+  static constexpr int TM = 128, TN = 128, CK = 32;
+};
+int conv_bf16_window_cap(int stride);
+size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K);
+hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
+                          hipStream_t s);
+hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s);
+
+// ---- fp32 fused conv + GroupNorm, one workgroup per (n, 16-channel block)
+// (k_fused_gn.hip).  Supported when C_out/G divides 16 and the whole
+// T_out fits the workgroup's registers.
+struct FusedArgs {
+  const float* x;
+  const float* w;      // unpacked [C_out, C_in, K]
+  const float* bias;
+  const float* gamma;
+  const float* beta;
+  float* out;
+  float* mean_out;     // [N, G] or nullptr
+  float* rstd_out;
+  int64_t N, C_in, C_out, T, T_out;
+  int32_t K, stride, dilation, pad_left, G;
+  float eps;
+};
+int fused_gn_max_tout(int stride, int K, int dilation);  // 0 if unsupported
+bool fused_gn_supported(int64_t C_out, int32_t G, int64_t T_out, int stride, int K,
+                        int dilation);
+hipError_t fused_gn_launch(const FusedArgs& a, hipStream_t s);
+
+// ---- normalisation kernels (k_norm.hip)
+// GroupNorm: partials [N, C, n_ttiles] (mean, M2) with tile length tm -> mean/rstd [N, G]
+hipError_t gn_merge_launch(const float* part, int64_t N, int64_t C, int64_t L, int32_t G,
+                           int32_t n_ttiles, int32_t tm, float eps, float* mean, float* rstd,
+                           hipStream_t s);
+// GroupNorm statistics straight from y [N, C, L] -> mean/rstd [N, G]
+hipError_t gn_stats_launch(const float* y, int64_t N, int64_t C, int64_t L, int32_t G,
+                           float eps, float* mean, float* rstd, hipStream_t s);
+// out = (y - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c]
+hipError_t gn_apply_launch(const float* y, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, float* out, int64_t N,
+                           int64_t C, int64_t L, int32_t G, hipStream_t s);
+// LayerNorm over channels: partials [N, n_ctiles, L] (mean, M2), tile width tn
+hipError_t ln_merge_launch(const float* part, int64_t N, int64_t C, int64_t L,
+                           int32_t n_ctiles, int32_t tn, float eps, float* mean, float* rstd,
+                           hipStream_t s);
+hipError_t ln_apply_launch(const float* y, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, float* out, int64_t N,
+                           int64_t C, int64_t L, hipStream_t s);
+// Row-min epilogue: z = (y - mean) * rstd * gamma + beta with statistics per
+// (n, group) (norm_kind 1), per (n, l) (norm_kind 2) or none (norm_kind 0);
+// out[n,c,l] = min_c z[n,c,l] + bias2[c].
+hipError_t rowmin_bias_launch(const float* y, const float* mean, const float* rstd,
+                              const float* gamma, const float* beta, const float* bias2,
+                              float* out, int64_t N, int64_t C, int64_t L, int32_t G,
+                              int norm_kind, hipStream_t s);
+
+}  // namespace c1g

@@ -1,0 +1,178 @@
+/*
+ * conv1d_gn.h - C ABI of the MI355X (gfx950) conv1d -> GroupNorm library.
+ *
+ * A 1-D convolution computed as an implicit GEMM (rows m = (n, t_out),
+ * columns = output channels, reduction over (input channel, tap)), feeding a
+ * GroupNorm, a LayerNorm over channels, or nothing, with an optional per-row
+ * min plus broadcast bias.
+ *
+ * Operation sources (web pages, cited by title and passage):
+ *   "Kimi-K2.6 l2_p35"  POPCORNBENCH trace, Conv1d -> GroupNorm: the problem
+ *                       statement (x [N,C_in,T], weight [C_out,C_in,K],
+ *                       gamma/beta [C_out]), the output-length formula, the
+ *                       conv input index with zero padding, GroupNorm over
+ *                       (C_out/G channels x T_out) per (n, group) with
+ *                       population variance and eps inside the square root.
+ *   "Kimi-K2.6 l1_p5"   POPCORNBENCH trace, causal Conv1d: left padding of
+ *                       (K-1)*dilation zeros, no right padding, tap 0 oldest.
+ *   "Kimi-K2.6 l2_p75"  POPCORNBENCH trace, Linear -> GroupNorm -> min ->
+ *                       +bias: the K=1, T=1 case, min over channels after
+ *                       the GroupNorm affine, bias broadcast over channels.
+ *   "Kimi-K2.6 l2_p3"   POPCORNBENCH trace: the stats-then-apply split of a
+ *                       normalisation (statistics first, one affine pass after).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, contiguous, in device memory (HBM of the
+ *     current HIP device).  x and w are fp32 or bf16 (c1g_dtype); every other
+ *     tensor, and every output, is fp32.
+ *   - Ownership: the caller allocates and frees every buffer, including the
+ *     workspace; the library never allocates, frees or synchronises.  Outputs
+ *     must not overlap inputs unless an entry point says so.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  All work
+ *     is enqueued on it in order and returns immediately; results are ready
+ *     when the stream is synchronised.
+ *   - Errors: arguments are validated before anything is launched; on any
+ *     error nothing is launched, outputs are untouched and a non-zero
+ *     c1g_status is returned.  A launch failure reported by the HIP runtime
+ *     returns C1G_ERR_HIP.  Device faults surface at the caller's next
+ *     synchronisation, like any stream work.
+ *   - Determinism: for a given device, shape and inputs the outputs are bit
+ *     identical from run to run (no atomics; fixed reduction orders).
+ *   - Thread safety: entry points may be called concurrently from several
+ *     host threads; calls on one stream execute in order.
+ */
+#ifndef CONV1D_GN_H
+#define CONV1D_GN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element type of x and w */
+enum c1g_dtype { C1G_F32 = 0, C1G_BF16 = 1 };
+
+/* normalisation applied to the convolution output y */
+enum c1g_norm {
+  C1G_NORM_NONE = 0,           /* out = y                                            */
+  C1G_NORM_GROUP = 1,          /* GroupNorm over (C_out/G x T_out) per (n, group)     */
+  C1G_NORM_LAYER_CHANNELS = 2  /* LayerNorm over the C_out values at each (n, t_out)  */
+};
+
+/* epilogue after the normalisation */
+enum c1g_epilogue {
+  C1G_EPI_NONE = 0,
+  C1G_EPI_ROWMIN_BIAS = 1      /* out[n,c,t] = min_c' z[n,c',t] + bias2[c]             */
+};
+
+enum c1g_status {
+  C1G_OK = 0,
+  C1G_ERR_INVALID_ARG = 1,     /* bad size, NULL required pointer, C_out % G != 0 ...  */
+  C1G_ERR_UNSUPPORTED = 2,     /* valid but not built (e.g. window wider than a tile)  */
+  C1G_ERR_WORKSPACE = 3,       /* workspace NULL or smaller than the size query       */
+  C1G_ERR_MISALIGNED = 4,      /* a tensor pointer not aligned to its element size    */
+  C1G_ERR_HIP = 5              /* the HIP runtime reported an error at launch         */
+};
+
+/* Geometry of the convolution.
+ *   x [N, C_in, T], w [C_out, C_in, K], y/out [N, C_out, T_out] with
+ *   T_out = floor((T + pad_left + pad_right - dilation*(K-1) - 1) / stride) + 1
+ *   ("Kimi-K2.6 l2_p35", output-length formula; symmetric padding p is
+ *   pad_left = pad_right = p; causal per "Kimi-K2.6 l1_p5" is
+ *   pad_left = (K-1)*dilation, pad_right = 0).
+ *   y[n,c,t] = bias[c] + sum_{ci<C_in} sum_{j<K} w[c,ci,j] * x[n,ci,t*stride+j*dilation-pad_left],
+ *   with x read as 0 outside [0, T): a cross-correlation, no kernel flip. */
+typedef struct c1g_conv_desc {
+  int64_t N, C_in, C_out, T;
+  int32_t K, stride, dilation;
+  int32_t pad_left, pad_right;
+  int32_t dtype;               /* enum c1g_dtype of x and w */
+} c1g_conv_desc;
+
+/* What follows the convolution in conv1d_gn_forward. */
+typedef struct c1g_norm_desc {
+  int32_t norm;                /* enum c1g_norm                                        */
+  int32_t G;                   /* groups for C1G_NORM_GROUP (C_out % G == 0); else 0   */
+  float eps;                   /* added to the variance inside the square root (> 0)   */
+  int32_t epilogue;            /* enum c1g_epilogue                                    */
+} c1g_norm_desc;
+
+/* T_out of the geometry, or -1 if the geometry is invalid or has no output.
+ * Pure host function; touches no device. */
+int64_t c1g_out_len(const c1g_conv_desc* d);
+
+/* Validation only: the status conv1d_gn_forward would return for this
+ * geometry, normalisation and workspace size before any pointer checks.
+ * norm may be NULL (plain convolution).  Pure host function. */
+int c1g_check(const c1g_conv_desc* d, const c1g_norm_desc* norm, size_t ws_bytes);
+
+/* Workspace bytes conv1d_forward needs for this geometry (0 for fp32). */
+size_t c1g_conv1d_workspace_size(const c1g_conv_desc* d);
+
+/* Plain convolution ("Kimi-K2.6 l1_p5" causal Conv1d; "Kimi-K2.6 l2_p35"
+ * conv index rule): y = conv(x, w) + bias.
+ *   x    [N, C_in, T]        fp32 or bf16, device
+ *   w    [C_out, C_in, K]    same type as x, device
+ *   bias [C_out] fp32 or NULL (no bias)
+ *   y    [N, C_out, T_out] fp32, device, written completely
+ *   ws   device scratch of ws_bytes >= c1g_conv1d_workspace_size(d)
+ *        (may be NULL when that size is 0); contents are clobbered. */
+int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
+                   float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes gn_stats needs. */
+size_t c1g_gn_stats_workspace_size(int64_t N, int64_t C, int64_t L, int32_t G);
+
+/* GroupNorm statistics of an existing y ("Kimi-K2.6 l2_p35" GroupNorm
+ * definition; "Kimi-K2.6 l2_p3" statistics-then-apply split):
+ *   y    [N, C, L] fp32 device, C % G == 0
+ *   mean [N, G]  fp32 device: mean of the C/G x L values of (n, g)
+ *   rstd [N, G]  fp32 device: 1/sqrt(population variance + eps)
+ *   ws   device scratch of ws_bytes >= c1g_gn_stats_workspace_size(...) */
+int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float* y,
+             float* mean, float* rstd, void* ws, size_t ws_bytes, void* stream);
+
+/* GroupNorm normalise + affine:
+ *   out[n,c,l] = (y[n,c,l] - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c],  g = c / (C/G)
+ *   y, out [N, C, L] fp32 device; out may equal y (in place), no other overlap
+ *   mean, rstd [N, G] fp32 device
+ *   gamma, beta [C] fp32 device, or NULL (1 and 0) */
+int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const float* mean,
+             const float* rstd, const float* gamma, const float* beta, float* out,
+             void* stream);
+
+/* Workspace bytes conv1d_gn_forward needs. */
+size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc* norm);
+
+/* The whole path: conv -> normalisation -> optional row-min epilogue.
+ *   x, w, bias     as conv1d_forward
+ *   gamma, beta    [C_out] fp32 or NULL (1 and 0): the normalisation's affine
+ *                  (ignored when norm == C1G_NORM_NONE)
+ *   bias2          [C_out] fp32, required iff epilogue == C1G_EPI_ROWMIN_BIAS
+ *   out            [N, C_out, T_out] fp32 device, written completely
+ *   mean_out, rstd_out  optional fp32 device outputs ([N,G] for GroupNorm,
+ *                  [N,T_out] for LayerNorm over channels), or NULL
+ *   ws             device scratch of ws_bytes >= c1g_conv1d_gn_workspace_size
+ * GroupNorm: z = (y - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c]
+ *   ("Kimi-K2.6 l2_p35"); LayerNorm over channels: the same formula with the
+ *   statistics of y[n,:,t]; row-min: out = min over channels of z at (n,t)
+ *   plus bias2[c] ("Kimi-K2.6 l2_p75"). */
+int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const void* x,
+                      const void* w, const float* bias, const float* gamma, const float* beta,
+                      const float* bias2, float* out, float* mean_out, float* rstd_out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Name of the kernel route conv1d_gn_forward takes for these arguments
+ * ("fused_lds", "split", "gemm_rows", ...), or "invalid".  Pure host function. */
+const char* c1g_route(const c1g_conv_desc* d, const c1g_norm_desc* norm);
+
+/* Static string describing a status code. */
+const char* c1g_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV1D_GN_H */

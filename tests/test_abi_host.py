@@ -1,0 +1,150 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and its host-only planning and validation behave as documented.
+No compute call is made (there is no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import conv1d_implicit_gemm_amd as c1g
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv1d_gn.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_0-9]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_lists_every_binding_export():
+    assert header_functions() == sorted(c1g.EXPORTS)
+
+
+@pytest.mark.parametrize("name", header_functions())
+def test_library_exports_symbol(name):
+    lib = c1g.load_library()
+    assert hasattr(lib, name), name
+    assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    lib = c1g.load_library()
+    for code, text in c1g.STATUS.items():
+        assert lib.c1g_status_string(code).decode() == text
+
+
+@pytest.mark.parametrize("T,K,s,d,pl,pr", [
+    (1024, 3, 1, 1, 1, 1), (8192, 4, 1, 1, 3, 0), (1, 1, 1, 1, 0, 0), (4096, 5, 1, 2, 2, 2),
+    (7, 3, 2, 1, 0, 0), (10, 4, 3, 2, 1, 2), (5, 3, 1, 3, 0, 0), (2, 5, 1, 1, 0, 0)])
+def test_out_len_matches_oracle(T, K, s, d, pl, pr):
+    desc = c1g.ConvDesc(2, 3, 4, T, K, s, d, pl, pr, c1g.C1G_F32)
+    assert c1g.out_len(desc) == oracle.out_len(T, K, s, d, pl, pr)
+
+
+def _desc(**kw):
+    base = dict(N=2, C_in=16, C_out=32, T=256, K=3, stride=1, dilation=1, pad_left=1,
+                pad_right=1, dtype=c1g.C1G_F32)
+    base.update(kw)
+    return c1g.ConvDesc(base["N"], base["C_in"], base["C_out"], base["T"], base["K"],
+                        base["stride"], base["dilation"], base["pad_left"], base["pad_right"],
+                        base["dtype"])
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(C_in=0), dict(C_out=0), dict(T=0), dict(K=0),
+                                dict(stride=0), dict(dilation=0), dict(pad_left=-1),
+                                dict(pad_right=-1), dict(T=2, K=5, pad_left=0, pad_right=0)])
+def test_invalid_geometry(kw):
+    d = _desc(**kw)
+    assert c1g.check(d) == 1
+    assert c1g.route(d) == "invalid"
+    assert c1g.out_len(d) == -1
+
+
+def test_invalid_norm_args():
+    d = _desc()
+    assert c1g.check(d, c1g.NormDesc(c1g.NORM_GROUP, 5, 1e-5, 0)) == 1   # 32 % 5
+    assert c1g.check(d, c1g.NormDesc(c1g.NORM_GROUP, 0, 1e-5, 0)) == 1
+    assert c1g.check(d, c1g.NormDesc(c1g.NORM_GROUP, 8, 0.0, 0)) == 1    # eps must be > 0
+    assert c1g.check(d, c1g.NormDesc(c1g.NORM_GROUP, 8, float("nan"), 0)) == 1
+    assert c1g.check(d, c1g.NormDesc(7, 8, 1e-5, 0)) == 1
+    assert c1g.check(d, c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 9)) == 1
+    assert c1g.check(_desc(dtype=7)) == 2
+
+
+def test_routes():
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    assert c1g.route(_desc(), gn) == "fused_single_pass"
+    big = _desc(N=16, C_in=128, C_out=256, T=1024)
+    assert c1g.route(big, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0)) == "fused_single_pass"
+    # C_out/G = 3 does not divide 16 -> split path
+    assert c1g.route(_desc(C_out=24), gn) == "split"
+    # too long for the on-chip slab -> split path
+    assert c1g.route(_desc(T=1500), gn) == "split"
+    assert c1g.route(_desc(), c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == "split"
+    assert c1g.route(_desc(), c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 1)) == "split"
+    assert c1g.route(_desc()) == "conv_only"
+
+
+def test_workspace_sizes():
+    d = _desc(C_out=24)
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    need = c1g.conv1d_gn_workspace_size(d, gn)
+    assert need > 0
+    assert c1g.check(d, gn, need) == 0
+    assert c1g.check(d, gn, need - 1) == 3
+    # fused route needs none
+    assert c1g.conv1d_gn_workspace_size(_desc(), gn) == 0
+    assert c1g.conv1d_workspace_size(_desc()) > 0
+
+
+def test_unsupported_sizes():
+    # taps beyond the LDS weight image
+    assert c1g.check(_desc(K=9, pad_left=4, pad_right=4)) == 2
+    # input window wider than any tile variant
+    assert c1g.check(_desc(stride=8, T=4096)) == 2
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 2, 8)
+    w = torch.zeros(3, 2, 3)
+    with pytest.raises(ValueError):
+        c1g.conv1d_forward(x, w)
+
+
+def test_pointer_checks_fail_before_any_launch():
+    """Validation rejects bad pointers without touching memory or the device:
+    fake addresses are safe because nothing is dereferenced or launched."""
+    lib = c1g.load_library()
+    d = _desc()
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    P = ctypes.c_void_p
+    good = P(0x10000)
+    odd = P(0x10002)      # 2-byte aligned: not enough for fp32
+    # missing required pointers
+    assert lib.conv1d_forward(ctypes.byref(d), None, good, None, good, good, 1 << 30, None) == 1
+    assert lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(gn), good, good, None, None, None,
+                                 None, None, None, None, None, 0, None) == 1
+    # misaligned fp32 tensors
+    assert lib.conv1d_forward(ctypes.byref(d), odd, good, None, good, good, 1 << 30, None) == 4
+    assert lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(gn), good, good, None, odd, None,
+                                 None, good, None, None, None, 0, None) == 4
+    # workspace too small
+    need = c1g.conv1d_workspace_size(d)
+    assert lib.conv1d_forward(ctypes.byref(d), good, good, None, good, good, need - 1, None) == 3
+    assert lib.conv1d_forward(ctypes.byref(d), good, good, None, good, None, 0, None) == 3
+    # row-min epilogue without bias2
+    rm = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 1)
+    assert lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(rm), good, good, None, None, None,
+                                 None, good, None, None, good, 1 << 30, None) == 1
+    # standalone GroupNorm entry points
+    assert lib.gn_stats(2, 32, 10, 5, 1e-5, good, good, good, None, 0, None) == 1
+    assert lib.gn_stats(2, 32, 10, 8, 1e-5, odd, good, good, None, 0, None) == 4
+    assert lib.gn_apply(2, 32, 10, 8, good, good, good, None, None, None, None) == 1
+    assert lib.gn_apply(2, 32, 10, 8, good, odd, good, None, None, good, None) == 4

@@ -1,0 +1,172 @@
+"""GPU parity of the fp32 path against the fp64 oracle (element by element,
+max-abs 1e-4 after normalisation), plus the properties the pages fix that can
+be checked bit-exactly on the device: causality, the delta kernel and
+run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import conv1d_implicit_gemm_amd as c1g
+import oracle
+from conv1d_implicit_gemm_amd.workloads import WORKLOADS, Workload, make_inputs, to_f64_numpy
+from tests.gpu_util import (DEV, TOL_F32, announce, check_parity, max_abs_err, run_library,
+                            run_oracle, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+W = Workload
+# Shapes that span several tiles and end in ragged tails (tile: 128 positions x
+# 128 channels, 8 input channels per K-chunk), every route, and the edge cases.
+CONV_CASES = [
+    W("conv_ragged_k3", N=2, C_in=19, C_out=150, T=300, K=3, pad_left=1, pad_right=1,
+      norm=None),
+    W("conv_causal_k4", N=2, C_in=24, C_out=40, T=515, K=4, pad_left=3, pad_right=0, norm=None,
+      bias=False),
+    W("conv_stride2_d3", N=3, C_in=9, C_out=130, T=701, K=5, stride=2, dilation=3, pad_left=4,
+      pad_right=1, norm=None),
+    W("conv_stride3", N=1, C_in=5, C_out=7, T=1000, K=2, stride=3, norm=None),
+    W("conv_k1", N=2, C_in=33, C_out=17, T=129, K=1, norm=None),
+    W("conv_k1_t1", N=37, C_in=40, C_out=65, T=1, K=1, norm=None),
+    W("conv_odd_T", N=2, C_in=7, C_out=9, T=131, K=3, pad_left=1, pad_right=1, norm=None),
+    W("conv_no_pad_short", N=1, C_in=3, C_out=5, T=6, K=4, norm=None),
+    W("conv_k8", N=1, C_in=16, C_out=20, T=200, K=8, pad_left=7, norm=None),
+]
+
+
+@pytest.mark.parametrize("wl", CONV_CASES, ids=lambda w: w.name)
+def test_conv_parity(wl):
+    check_parity(wl)
+
+
+GN_CASES = [
+    WORKLOADS["conv1d_gn_f32_n2_c16x32_t256_k3"],
+    WORKLOADS["conv1d_gn_f32_n16_c128x256_t1024_k3"],
+    # fused route: ragged T_out, channel count not a multiple of 16, cpg 1/2/16
+    W("fused_ragged", N=3, C_in=10, C_out=24, T=333, K=3, pad_left=1, pad_right=1, G=6),
+    W("fused_cpg1", N=2, C_in=8, C_out=16, T=100, K=2, G=16),
+    W("fused_cpg16", N=2, C_in=12, C_out=48, T=517, K=3, dilation=2, pad_left=2, pad_right=2,
+      G=3),
+    W("fused_no_affine_no_bias", N=1, C_in=4, C_out=8, T=64, K=3, G=2, bias=False,
+      affine=False),
+    W("fused_t1", N=4, C_in=40, C_out=32, T=1, K=1, G=4),
+    # split route: C_out/G not a divisor of 16, or T_out beyond the on-chip slab
+    W("split_cpg3", N=2, C_in=20, C_out=24, T=300, K=3, pad_left=1, pad_right=1, G=8),
+    W("split_long", N=2, C_in=16, C_out=32, T=1500, K=3, pad_left=1, pad_right=1, G=8),
+    W("split_stride2", N=2, C_in=9, C_out=40, T=500, K=4, stride=2, G=5),
+    W("split_cpg24_ctile_straddle", N=2, C_in=17, C_out=240, T=130, K=3, pad_left=1,
+      pad_right=1, G=10),
+]
+
+
+@pytest.mark.parametrize("wl", GN_CASES, ids=lambda w: w.name)
+def test_groupnorm_parity(wl):
+    check_parity(wl)
+
+
+LN_ROWMIN_CASES = [
+    W("ln_channels", N=2, C_in=12, C_out=160, T=200, K=3, pad_left=1, pad_right=1,
+      norm="layer_channels"),
+    W("ln_channels_t1", N=5, C_in=12, C_out=40, T=1, K=1, norm="layer_channels"),
+    W("gn_rowmin_t1", N=64, C_in=96, C_out=256, T=1, K=1, G=16, bias=False, rowmin_bias=True),
+    W("gn_rowmin_t", N=2, C_in=8, C_out=48, T=70, K=3, pad_left=1, pad_right=1, G=4,
+      rowmin_bias=True),
+    W("ln_rowmin", N=2, C_in=8, C_out=48, T=70, K=3, pad_left=1, pad_right=1,
+      norm="layer_channels", rowmin_bias=True),
+    W("rowmin_only", N=3, C_in=8, C_out=20, T=33, K=3, norm=None, rowmin_bias=True),
+]
+
+
+@pytest.mark.parametrize("wl", LN_ROWMIN_CASES, ids=lambda w: w.name)
+def test_ln_rowmin_parity(wl):
+    check_parity(wl)
+
+
+def test_causal_conv_full_size_sampled():
+    """The causal workload at full size; the oracle checks two whole samples
+    (the first and the last) element by element."""
+    wl = WORKLOADS["causal_conv1d_f32_n32_c256x256_t8192_k4"]
+    announce(wl.name)
+    inp = make_inputs(wl, 0)
+    got = run_library(wl, inp)
+    for n in (0, wl.N - 1):
+        ref = run_oracle(wl, inp, n_slice=slice(n, n + 1))
+        err = max_abs_err(got[n:n + 1], ref["out"])
+        assert err <= TOL_F32, (n, err)
+
+
+def test_causality_bitwise():
+    """Perturbing x after t0 leaves y[..., :t0+1] bit-identical on the device."""
+    wl = W("causal", N=2, C_in=20, C_out=36, T=400, K=4, pad_left=3, pad_right=0, norm=None)
+    announce("causality")
+    inp = make_inputs(wl, 1)
+    y0 = run_library(wl, inp)
+    for t0 in (0, 127, 128, 250):
+        inp2 = dict(inp)
+        x2 = inp["x"].clone()
+        x2[:, :, t0 + 1:] += torch.randn(x2[:, :, t0 + 1:].shape) * 5
+        inp2["x"] = x2
+        y1 = run_library(wl, inp2)
+        assert torch.equal(y0[:, :, :t0 + 1], y1[:, :, :t0 + 1]), t0
+        assert not torch.equal(y0[:, :, t0 + 1:], y1[:, :, t0 + 1:])
+
+
+@pytest.mark.parametrize("K,s,d,pl,pr", [(4, 1, 1, 3, 0), (3, 2, 2, 1, 2), (5, 1, 3, 6, 6)])
+def test_delta_kernel_bitwise(K, s, d, pl, pr):
+    """w[c,ci,j] = [c==ci][j==j0]: y is x read at t*s + j0*d - pl, exactly."""
+    announce("delta", K, s, d, pl, pr)
+    C, T = 20, 300
+    x = torch.randn(2, C, T)
+    for j0 in range(K):
+        w = torch.zeros(C, C, K)
+        w[torch.arange(C), torch.arange(C), j0] = 1.0
+        y = c1g.conv1d_forward(to_dev(x), to_dev(w), stride=s, dilation=d, pad_left=pl,
+                               pad_right=pr).cpu()
+        T_out = y.shape[2]
+        u = torch.arange(T_out) * s + j0 * d - pl
+        valid = (u >= 0) & (u < T)
+        want = torch.zeros(2, C, T_out)
+        want[:, :, valid] = x[:, :, u[valid]]
+        assert torch.equal(y, want), j0
+
+
+@pytest.mark.parametrize("name", ["conv1d_gn_f32_n16_c128x256_t1024_k3", "split_cpg3"])
+def test_determinism(name):
+    wl = WORKLOADS.get(name) or next(w for w in GN_CASES if w.name == name)
+    announce("determinism", name)
+    inp = make_inputs(wl, 3)
+    a = run_library(wl, inp)
+    b = run_library(wl, inp)
+    assert torch.equal(a, b)
+
+
+def test_gn_stats_and_apply_standalone():
+    """gn_stats + gn_apply on an existing y (and in place) vs the oracle's GroupNorm."""
+    announce("gn_stats/gn_apply")
+    g = torch.Generator().manual_seed(5)
+    for (N, C, L, G) in [(2, 32, 1000, 8), (3, 24, 77, 8), (1, 16, 4093, 4), (4, 12, 1, 3)]:
+        y = torch.randn(N, C, L, generator=g) * 2 + 0.5
+        gam = torch.rand(C, generator=g) + 0.5
+        bet = torch.randn(C, generator=g) * 0.1
+        z_ref, m_ref, r_ref = oracle.group_norm(y.double().numpy(), G, 1e-5,
+                                                gam.double().numpy(), bet.double().numpy())
+        yd = to_dev(y)
+        mean, rstd = c1g.gn_stats(yd, G, 1e-5)
+        assert max_abs_err(mean, m_ref) <= 1e-5
+        assert float(np.max(np.abs(rstd.cpu().double().numpy() / r_ref - 1))) <= 1e-5
+        out = c1g.gn_apply(yd, mean, rstd, to_dev(gam), to_dev(bet), groups=G)
+        assert max_abs_err(out, z_ref) <= TOL_F32
+        c1g.gn_apply(yd, mean, rstd, to_dev(gam), to_dev(bet), groups=G, out=yd)  # in place
+        assert torch.equal(yd, out)
+
+
+def test_error_status_no_launch():
+    """Invalid calls return a status and leave the output untouched."""
+    announce("errors")
+    x = torch.randn(2, 4, 50, device=DEV)
+    w = torch.randn(8, 4, 3, device=DEV)
+    out = torch.full((2, 8, 48), 7.0, device=DEV)
+    with pytest.raises(c1g.C1GError) as ei:
+        c1g.conv1d_gn_forward(x, w, norm="group", groups=3, out=out)   # 8 % 3 != 0
+    assert ei.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.full_like(out, 7.0))
