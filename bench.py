@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the conv1d -> GroupNorm path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one conv1d_gn_forward call (every kernel of the path) over one
+batch of seeded synthetic input already resident in HBM.  W untimed steps,
+then K steps timed with HIP events on the launch stream, bracketed by device
+synchronisation.  Prints ONE JSON line with the throughput (TFLOP/s of the
+implicit GEMM, 2*M*N*K per step), the roofline position of the dominant
+kernel, and the fp64 CPU oracle timed on this host's cores as a reference
+baseline.
+
+Other modes (used by the profiling runs recorded under profiles/):
+    --mode copy     a plain device-to-device copy of known size, to scale the
+                    FETCH_SIZE / WRITE_SIZE counters to bytes
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused conv1d+GroupNorm TFLOP/s and GB/s at 1 GPU; % of MFMA/HBM roofline"
+PEAKS = {  # MI355X published dense peaks
+    "f32": ("mfma", 157.3, "TFLOP/s"),
+    "bf16": ("mfma", 2500.0, "TFLOP/s"),
+    "hbm": ("hbm", 8000.0, "GB/s"),
+}
+# kernel source files whose change invalidates stored counter readings
+KERNEL_SOURCES = {
+    "fused_single_pass": ["conv1d_implicit_gemm_amd/csrc/k_fused_gn.hip",
+                          "conv1d_implicit_gemm_amd/csrc/common.hpp"],
+}
+
+
+def source_hash(route):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(route, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, route):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/<workload>.md), or None when absent or when the
+    kernel's source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", workload + ".md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"```json counters\n(.*?)\n```", txt, flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != source_hash(route):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, flops, budget_s=10.0):
+    """The oracle, as it stands, on the full workload, repeated until about
+    budget_s seconds of wall time have passed (at least once)."""
+    import oracle
+    from conv1d_implicit_gemm_amd.workloads import to_f64_numpy as f
+    args = dict(stride=wl.stride, dilation=wl.dilation, pad_left=wl.pad_left,
+                pad_right=wl.pad_right, norm=wl.norm, G=wl.G, eps=wl.eps,
+                gamma=f(inp["gamma"]), beta=f(inp["beta"]), bias2=f(inp["bias2"]))
+    x, w, b = f(inp["x"]), f(inp["w"]), f(inp["bias"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(x, w, b, **args)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "full workload (all %d samples), %d run(s) in %.1f s, fp64" % (wl.N, reps, el)}
+
+
+def copy_mode(args):
+    import torch
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, device="cuda:0", dtype=torch.float32).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": args.steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        return copy_mode(args)
+
+    import torch
+    import conv1d_implicit_gemm_amd as c1g
+    from conv1d_implicit_gemm_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    name = args.workload or HEADLINE
+    wl = WORKLOADS[name]
+    dev = "cuda:0"
+    inp = make_inputs(wl, 0)
+    d = {k: (v.to(dev).contiguous() if v is not None else None) for k, v in inp.items()}
+    op = c1g.PreparedConv1dGN(d["x"], d["w"], d["bias"], stride=wl.stride,
+                              dilation=wl.dilation, pad_left=wl.pad_left,
+                              pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
+                              gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"])
+    T_out = op.T_out
+    flops = 2 * wl.N * T_out * wl.C_out * wl.C_in * wl.K
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        op()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps on the launch stream
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        op()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # the dominant kernel's duration: on the single-pass route one step is one
+    # launch, timed per launch with events on the same stream
+    kern_ms = None
+    if op.route == "fused_single_pass":
+        n = min(args.steps, 100)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            op()
+            b.record(stream)
+        torch.cuda.synchronize()
+        kern_ms = sum(a.elapsed_time(b) for a, b in evs) / n
+    else:
+        kern_ms = ms_per_step
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    bound, peak, unit = PEAKS[wl.dtype]
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    algo_bytes = (wl.N * wl.C_in * wl.T * wl.elem_bytes + wl.C_out * wl.C_in * wl.K *
+                  wl.elem_bytes + wl.N * wl.C_out * T_out * 4)
+    traffic = stored_traffic(name, op.route)
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded; shapes of the pages' workloads)",
+        "config": {"workload": name, "N": wl.N, "C_in": wl.C_in, "C_out": wl.C_out, "T": wl.T,
+                   "T_out": T_out, "K": wl.K, "stride": wl.stride, "dilation": wl.dilation,
+                   "pad_left": wl.pad_left, "pad_right": wl.pad_right, "norm": wl.norm,
+                   "G": wl.G, "rowmin_bias": wl.rowmin_bias, "route": op.route,
+                   "parallelism": "single GPU"},
+        "gbps_algorithmic": round(algo_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, flops)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

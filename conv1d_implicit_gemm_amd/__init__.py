@@ -294,3 +294,49 @@ def gn_apply(y, mean, rstd, gamma=None, beta=None, groups=None, out=None):
                       _ptr(out), _stream(y.device))
     _raise(st, "gn_apply")
     return out
+
+
+class PreparedConv1dGN:
+    """conv1d_gn_forward with every argument marshalled once.
+
+    Holds references to the tensors it was built from; each call enqueues the
+    same work on the stream that was current at construction.  For tight
+    loops (benchmarks, graph capture) where per-call validation in Python
+    would dominate."""
+
+    def __init__(self, x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
+                 causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
+                 beta=None, rowmin_bias=None, out=None, mean=None, rstd=None):
+        lib = load_library()
+        self.desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation)
+        self.norm = make_norm(norm, groups, eps, rowmin_bias is not None)
+        for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"),
+                      (rowmin_bias, "rowmin_bias"), (mean, "mean"), (rstd, "rstd")):
+            _need(t, nm, torch.float32, x.device)
+        self.T_out = lib.c1g_out_len(ctypes.byref(self.desc))
+        if self.T_out < 1:
+            _raise(1, "PreparedConv1dGN")
+        if out is None:
+            out = torch.empty((self.desc.N, self.desc.C_out, self.T_out), device=x.device,
+                              dtype=torch.float32)
+        _need(out, "out", torch.float32, x.device)
+        ws_bytes = lib.c1g_conv1d_gn_workspace_size(ctypes.byref(self.desc),
+                                                   ctypes.byref(self.norm))
+        self.workspace = (torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+                          if ws_bytes else None)
+        self.route = route(self.desc, self.norm)
+        self.out = out
+        self._keep = (x, w, bias, gamma, beta, rowmin_bias, mean, rstd)
+        self._fn = lib.conv1d_gn_forward
+        self._args = (ctypes.byref(self.desc), ctypes.byref(self.norm), _ptr(x), _ptr(w),
+                      _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(rowmin_bias), _ptr(out),
+                      _ptr(mean), _ptr(rstd), _ptr(self.workspace), ws_bytes,
+                      _stream(x.device))
+        check_status = lib.c1g_check(ctypes.byref(self.desc), ctypes.byref(self.norm), ws_bytes)
+        _raise(check_status, "PreparedConv1dGN")
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            _raise(st, "conv1d_gn_forward")
+        return self.out

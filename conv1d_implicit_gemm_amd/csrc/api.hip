@@ -74,7 +74,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   // route
   const bool want_gn = p.norm == C1G_NORM_GROUP, want_ln = p.norm == C1G_NORM_LAYER_CHANNELS;
   if (!p.bf16 && want_gn && p.epi == C1G_EPI_NONE &&
-      fused_gn_supported(d->C_out, nd->G, p.T_out, d->stride, d->K, d->dilation)) {
+      fused_gn_supported(d->C_in, d->C_out, nd->G, p.T_out, d->stride, d->K, d->dilation)) {
     p.route = R_FUSED;
     p.total = 0;
     return p;

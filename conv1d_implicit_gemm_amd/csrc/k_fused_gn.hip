@@ -9,13 +9,24 @@
 // subtiles of positions x 16 channels (v_mfma_f32_16x16x4_f32), so y never
 // goes to HBM and is never re-read.
 //
-// Per K-chunk (8 input channels, all taps) the input halo window of the whole
-// sequence is staged in LDS once and read by every tap at a shifted offset;
-// the next chunk is fetched into registers while the current one is consumed.
-// After the K loop the group statistics are taken in two passes over the
-// registers (sum -> mean, then sum of squared deviations -> variance), reduced
-// across lanes with xor shuffles and across waves in a fixed order through LDS
-// (deterministic), then each value is normalised, scaled and written once.
+// K loop: per chunk of 16 input channels (all taps) the input halo window of
+// the whole sequence and the chunk's weights are staged in LDS, and every tap
+// reads the window at a shifted offset.  Two LDS stages: while one chunk is
+// consumed, the next one streams in with gfx950's direct global->LDS loads
+// (global_load_lds_dwordx4 / _dword), which bypass VGPRs and do not occupy the
+// waves' LDS instruction queues, so the MFMA operand reads are never stuck
+// behind staging writes.  Window slots in the zero padding are zeroed once and
+// never loaded.  A register-staged variant serves inputs whose rows are not
+// 16-byte aligned.
+//
+// Each K-step (4 input channels at one tap) reads the A operands of the next
+// step from LDS before issuing its own MQ independent MFMAs; scheduling fences
+// keep that order and keep each step's accumulators apart.
+//
+// Epilogue: the group statistics are taken in two passes over the registers
+// (sum -> mean, then sum of squared deviations -> variance), reduced across
+// lanes with xor shuffles and across waves in a fixed order through LDS
+// (deterministic); each value is then normalised, scaled and written once.
 //
 // blockIdx -> (n, channel block) is remapped so that the workgroups of one
 // sample land on the same XCD and share its L2 copy of x[n].
@@ -28,7 +39,7 @@ namespace {
 constexpr int NW = 8;              // waves per workgroup
 constexpr int NTHR = NW * 64;
 constexpr int CB = 16;             // channels per workgroup
-constexpr int CK = 8;              // input channels per K-chunk
+constexpr int CK = 16;             // input channels per K-chunk
 constexpr int KMAX = 8;
 constexpr int HALO_MAX = 28;       // (K-1)*dilation supported
 
@@ -37,129 +48,85 @@ struct FusedGeom {
   static constexpr int TCOV = NW * MQ * 16;          // positions covered
   static constexpr int XL = TCOV + 32;               // staged window width
   static constexpr int XS = XL + 16;                 // LDS row stride (== 16 mod 32)
-  static constexpr int XQ = XL / 4;
+  static constexpr int XQ = XL / 4;                  // 16-byte slots per row
   static constexpr int XV = (CK * XQ + NTHR - 1) / NTHR;
   static constexpr int WV = (KMAX * CK * CB + NTHR - 1) / NTHR;
+  static constexpr int DPR = (XQ + 63) / 64;         // direct-load instructions per row
 };
 
-template <int MQ>
-__global__ __launch_bounds__(NTHR) void fused_conv_gn_kernel(FusedArgs a) {
-  using Gm = FusedGeom<MQ>;
-  __shared__ float Xs[CK * Gm::XS];
-  __shared__ float Ws[KMAX * CK * CB];
-  __shared__ float red[NW * CB];
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, kq = lane >> 4;
+// Direct global->LDS copies: lane i of the wave writes lds_wave_base + i*size.
+__device__ __forceinline__ void dma16(const float* src, float* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const float* src, float* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+}
 
+struct Coord {
+  int64_t n;
+  int cbase;
+};
+
+__device__ __forceinline__ Coord wg_coord(const FusedArgs& a) {
   // XCD-aware mapping: consecutive workgroup ids round-robin over the 8 XCDs;
   // give each XCD a contiguous range of (n, block) so one sample's blocks share an L2.
   const int nblk = (int)((a.C_out + CB - 1) / CB);
   const int total = (int)(a.N * nblk);
   int lin = blockIdx.x;
   if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int64_t n = lin / nblk;
-  const int cb = lin - (int)n * nblk;
-  const int cbase = cb * CB;
+  Coord r;
+  r.n = lin / nblk;
+  r.cbase = (lin - (int)r.n * nblk) * CB;
+  return r;
+}
 
-  const int K = a.K, d = a.dilation;
-  const int64_t T = a.T, T_out = a.T_out;
-  const int64_t tbase = -(int64_t)a.pad_left;
-  const int64_t tal = (tbase >= 0) ? (tbase & ~(int64_t)3) : -(((-tbase) + 3) & ~(int64_t)3);
-  const int shift = (int)(tbase - tal);
-  const int n_chunks = (int)((a.C_in + CK - 1) / CK);
-
-  const float* __restrict__ x = a.x;
-  const float* __restrict__ w = a.w;
-
-  f32x4 xr[Gm::XV];
-  float wr[Gm::WV];
-
-  auto fetch = [&](int chunk) {
-    const int64_t ci0 = (int64_t)chunk * CK;
+// One chunk of MFMA work on a staged (window, weight) pair.
+template <int MQ, int KT>
+__device__ __forceinline__ void compute_chunk(const float* xs, const float* ws,
+                                              f32x4 (&acc)[MQ], int abase, int bbase, int d) {
+  using Gm = FusedGeom<MQ>;
+  constexpr int HS = CK / 4;          // K-steps per tap
+  constexpr int NSTEP = KT * HS;
+  float av[2][MQ], bv[NSTEP];
 #pragma unroll
-    for (int i = 0; i < Gm::XV; ++i) {
-      const int q = tid + NTHR * i;
-      const int row = q / Gm::XQ, c4 = q - row * Gm::XQ;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      const int64_t ci = ci0 + row;
-      if (row < CK && ci < a.C_in) {
-        const int64_t t = tal + 4 * c4;
-        const float* src = x + (n * a.C_in + ci) * T;
-        if (t >= 0 && t + 3 < T && ((((uintptr_t)(src + t)) & 15) == 0)) {
-          v = *(const f32x4*)(src + t);
-        } else {
+  for (int st = 0; st < NSTEP; ++st) bv[st] = ws[bbase + ((st / HS) * CK + 4 * (st % HS)) * CB];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (t + e >= 0 && t + e < T) v[e] = src[t + e];
-        }
-      }
-      xr[i] = v;
-    }
-    // weight chunk image [j][cl][c], c fastest
+  for (int m = 0; m < MQ; ++m) av[0][m] = xs[abase + m * 16];
 #pragma unroll
-    for (int i = 0; i < Gm::WV; ++i) {
-      const int e = tid + NTHR * i;
-      const int c = e & (CB - 1);
-      const int rest = e >> 4;
-      const int cl = rest % CK, j = rest / CK;
-      float v = 0.f;
-      const int64_t co = cbase + c, ci = ci0 + cl;
-      if (j < K && co < a.C_out && ci < a.C_in) v = w[(co * a.C_in + ci) * K + j];
-      wr[i] = v;
-    }
-  };
-  auto stash = [&]() {
+  for (int st = 0; st < NSTEP; ++st) {
+    if (st + 1 < NSTEP) {
+      const int j = (st + 1) / HS, h = (st + 1) % HS;
+      const int ao = abase + 4 * h * Gm::XS + j * d;
 #pragma unroll
-    for (int i = 0; i < Gm::XV; ++i) {
-      const int q = tid + NTHR * i;
-      const int row = q / Gm::XQ, c4 = q - row * Gm::XQ;
-      if (row < CK) *(f32x4*)(Xs + row * Gm::XS + 4 * c4) = xr[i];
+      for (int m = 0; m < MQ; ++m) av[(st + 1) & 1][m] = xs[ao + m * 16];
     }
 #pragma unroll
-    for (int i = 0; i < Gm::WV; ++i) {
-      const int e = tid + NTHR * i;
-      if (e < KMAX * CK * CB) Ws[e] = wr[i];
-    }
-  };
-
-  f32x4 acc[MQ];
-#pragma unroll
-  for (int m = 0; m < MQ; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const int abase = kq * Gm::XS + shift + wave * MQ * 16 + lr;  // stride 1
-  const int bbase = kq * CB + lr;
-
-  fetch(0);
-  stash();
-  __syncthreads();
-  for (int chunk = 0; chunk < n_chunks; ++chunk) {
-    if (chunk + 1 < n_chunks) fetch(chunk + 1);
-    for (int j = 0; j < K; ++j) {
-#pragma unroll
-      for (int h = 0; h < CK / 4; ++h) {
-        const float bv = Ws[bbase + (j * CK + 4 * h) * CB];
-        const int ao = abase + 4 * h * Gm::XS + j * d;
-#pragma unroll
-        for (int m = 0; m < MQ; ++m) acc[m] = mfma16x16x4(Xs[ao + m * 16], bv, acc[m]);
-      }
-    }
-    __syncthreads();
-    if (chunk + 1 < n_chunks) {
-      stash();
-      __syncthreads();
-    }
+    for (int m = 0; m < MQ; ++m) acc[m] = mfma16x16x4(av[st & 1][m], bv[st], acc[m]);
+    // keep the order: the next step's LDS reads before this step's MFMAs,
+    // and no instruction crossing a step boundary
+    if (st + 1 < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, MQ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MQ, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
 
-  // ---------------------------------------------------------------- epilogue
-  const int c = cbase + lr;
+// Statistics, normalisation and the single write of the output slab.
+template <int MQ>
+__device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
+                                         f32x4 (&acc)[MQ], float* red) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int64_t n = co.n, T_out = a.T_out;
+  const int c = co.cbase + lr;
   const bool cvalid = c < a.C_out;
   const float bias = (a.bias != nullptr && cvalid) ? a.bias[c] : 0.f;
   const int cpg = (int)(a.C_out / a.G);
   const int gl = lr / cpg;                 // group within the block
-  const int ngl = CB / cpg;
   const int t_lane = wave * MQ * 16 + 4 * kq;
+  const bool full = FusedGeom<MQ>::TCOV == T_out;
 
   float sum = 0.f;
 #pragma unroll
@@ -167,7 +134,7 @@ __global__ __launch_bounds__(NTHR) void fused_conv_gn_kernel(FusedArgs a) {
     acc[m] += bias;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (t_lane + m * 16 + r < T_out) sum += acc[m][r];
+      if (full || t_lane + m * 16 + r < T_out) sum += acc[m][r];
   }
   // lanes of one group differ in the low log2(cpg) bits of lr and in kq
   auto group_reduce = [&](float v) {
@@ -195,7 +162,7 @@ __global__ __launch_bounds__(NTHR) void fused_conv_gn_kernel(FusedArgs a) {
   for (int m = 0; m < MQ; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (t_lane + m * 16 + r < T_out) {
+      if (full || t_lane + m * 16 + r < T_out) {
         const float dv = acc[m][r] - mean;
         ss += dv * dv;
       }
@@ -228,15 +195,218 @@ __global__ __launch_bounds__(NTHR) void fused_conv_gn_kernel(FusedArgs a) {
       if (a.rstd_out) a.rstd_out[n * a.G + g] = rstd;
     }
   }
-  (void)ngl;
+}
+
+// ------------------------------------------------------------ direct-load variant
+// Requires T % 4 == 0 and a 16-byte aligned x: every 16-byte window slot then
+// lies entirely inside [0,T) or entirely in the padding.
+template <int MQ, int KT>
+__global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
+  using Gm = FusedGeom<MQ>;
+  // two stages; distinct arrays so the compiler can tell a stage being read
+  // from the stage being filled (gfx950 allows 160 KB of LDS per workgroup)
+  __shared__ __attribute__((aligned(16))) float Xs0[CK * Gm::XS];
+  __shared__ __attribute__((aligned(16))) float Xs1[CK * Gm::XS];
+  __shared__ __attribute__((aligned(16))) float Ws0[KT * CK * CB];
+  __shared__ __attribute__((aligned(16))) float Ws1[KT * CK * CB];
+  __shared__ float red[NW * CB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, kq = lane >> 4;
+  const Coord co = wg_coord(a);
+  const int64_t n = co.n;
+  const int cbase = co.cbase;
+  const int d = a.dilation;
+  const int64_t T = a.T;
+  const int64_t tbase = -(int64_t)a.pad_left;
+  const int64_t tal = (tbase >= 0) ? (tbase & ~(int64_t)3) : -(((-tbase) + 3) & ~(int64_t)3);
+  const int shift = (int)(tbase - tal);
+  const int n_chunks = (int)((a.C_in + CK - 1) / CK);
+  const float* xn = a.x + n * a.C_in * T;
+  constexpr int K = KT;
+
+  // zero the padding slots of both window stages and, for a partial channel
+  // block, the weight entries of channels past C_out; loads never touch them
+  for (int e = tid; e < 2 * CK * Gm::XQ; e += NTHR) {
+    const int b = e / (CK * Gm::XQ), rq = e - b * (CK * Gm::XQ);
+    const int r = rq / Gm::XQ, q = rq - r * Gm::XQ;
+    const int64_t t = tal + 4 * q;
+    if (!(t >= 0 && t + 3 < T))
+      *(f32x4*)((b ? Xs1 : Xs0) + r * Gm::XS + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  for (int e = tid; e < 2 * K * CK * CB; e += NTHR) {
+    const int b = e / (K * CK * CB), p = e - b * (K * CK * CB);
+    if (cbase + (p & (CB - 1)) >= a.C_out) (b ? Ws1 : Ws0)[p] = 0.f;
+  }
+
+  // issue the direct loads of one chunk into a stage (window rows wave,
+  // wave + NW, ...; weight instructions wave, wave + NW, ...)
+  auto stage = [&](int chunk, float* xs, float* ws) {
+    const int64_t ci0 = (int64_t)chunk * CK;
+    for (int r = wave; r < CK; r += NW) {
+      const bool row_ok = ci0 + r < a.C_in;
+      const float* src_row = xn + (ci0 + r) * T + tal;
+#pragma unroll
+      for (int p = 0; p < Gm::DPR; ++p) {
+        const int q = 64 * p + lane;
+        const int64_t t = tal + 4 * q;
+        float* dst = xs + r * Gm::XS + 4 * 64 * p;       // wave-uniform base
+        if (row_ok && q < Gm::XQ && t >= 0 && t + 3 < T) dma16(src_row + 4 * q, dst);
+      }
+      if (!row_ok)  // partial last chunk: rows past C_in are zero
+        for (int q = lane; q < Gm::XQ; q += 64)
+          *(f32x4*)(xs + r * Gm::XS + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    constexpr int NWI = K * CK * CB / 64;                // weight instructions
+    for (int p = wave; p < NWI; p += NW) {
+      const int e = 64 * p + lane;                       // LDS position
+      const int c = e & (CB - 1), jc = e >> 4;
+      const int j = jc / CK, cl = jc - j * CK;
+      float* dst = ws + 64 * p;
+      const bool cok = cbase + c < a.C_out;
+      if (cok && ci0 + cl < a.C_in)
+        dma4(a.w + ((int64_t)(cbase + c) * a.C_in + ci0 + cl) * K + j, dst);
+      else if (cok)
+        ws[e] = 0.f;
+    }
+  };
+
+  f32x4 acc[MQ];
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int abase = kq * Gm::XS + shift + wave * MQ * 16 + lr;  // stride 1
+  const int bbase = kq * CB + lr;
+
+  __syncthreads();  // zero fill done before the first loads land
+  stage(0, Xs0, Ws0);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; c += 2) {
+    if (c + 1 < n_chunks) stage(c + 1, Xs1, Ws1);
+    compute_chunk<MQ, KT>(Xs0, Ws0, acc, abase, bbase, d);
+    __syncthreads();
+    if (c + 1 >= n_chunks) break;
+    if (c + 2 < n_chunks) stage(c + 2, Xs0, Ws0);
+    compute_chunk<MQ, KT>(Xs1, Ws1, acc, abase, bbase, d);
+    __syncthreads();
+  }
+  epilogue<MQ>(a, co, acc, red);
+}
+
+// ------------------------------------------------------------ register-staged variant
+// Any T and alignment: each thread loads its window slots element by element
+// (zero outside [0,T)) into registers one chunk ahead and writes them to LDS.
+template <int MQ, int KT>
+__global__ __launch_bounds__(NTHR) void fused_gn_regs_kernel(FusedArgs a) {
+  using Gm = FusedGeom<MQ>;
+  __shared__ __attribute__((aligned(16))) float Xs[CK * Gm::XS];
+  __shared__ __attribute__((aligned(16))) float Ws[KT * CK * CB];
+  __shared__ float red[NW * CB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, kq = lane >> 4;
+  const Coord co = wg_coord(a);
+  const int64_t n = co.n;
+  const int cbase = co.cbase;
+  const int d = a.dilation;
+  const int64_t T = a.T;
+  const int64_t tbase = -(int64_t)a.pad_left;
+  const int64_t tal = (tbase >= 0) ? (tbase & ~(int64_t)3) : -(((-tbase) + 3) & ~(int64_t)3);
+  const int shift = (int)(tbase - tal);
+  const int n_chunks = (int)((a.C_in + CK - 1) / CK);
+  const float* xn = a.x + n * a.C_in * T;
+  constexpr int K = KT;
+
+  f32x4 xr[Gm::XV];
+  float wr[Gm::WV];
+  auto fetch = [&](int chunk) {
+    const int64_t ci0 = (int64_t)chunk * CK;
+#pragma unroll
+    for (int i = 0; i < Gm::XV; ++i) {
+      const int q = tid + NTHR * i;
+      const int row = q / Gm::XQ, c4 = q - row * Gm::XQ;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (row < CK && ci0 + row < a.C_in) {
+        const int64_t t = tal + 4 * c4;
+        const float* src = xn + (ci0 + row) * T;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (t + e >= 0 && t + e < T) v[e] = src[t + e];
+      }
+      xr[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::WV; ++i) {
+      const int e = tid + NTHR * i;
+      const int c = e & (CB - 1), jc = e >> 4;
+      const int j = jc / CK, cl = jc - j * CK;
+      float v = 0.f;
+      if (j < K && cbase + c < a.C_out && ci0 + cl < a.C_in)
+        v = a.w[((int64_t)(cbase + c) * a.C_in + ci0 + cl) * K + j];
+      wr[i] = v;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < Gm::XV; ++i) {
+      const int q = tid + NTHR * i;
+      const int row = q / Gm::XQ, c4 = q - row * Gm::XQ;
+      if (row < CK) *(f32x4*)(Xs + row * Gm::XS + 4 * c4) = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < Gm::WV; ++i) {
+      const int e = tid + NTHR * i;
+      if (e < K * CK * CB) Ws[e] = wr[i];
+    }
+  };
+
+  f32x4 acc[MQ];
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int abase = kq * Gm::XS + shift + wave * MQ * 16 + lr;
+  const int bbase = kq * CB + lr;
+
+  fetch(0);
+  stash();
+  __syncthreads();
+  for (int chunk = 0; chunk < n_chunks; ++chunk) {
+    if (chunk + 1 < n_chunks) fetch(chunk + 1);
+    compute_chunk<MQ, KT>(Xs, Ws, acc, abase, bbase, d);
+    __syncthreads();
+    if (chunk + 1 < n_chunks) {
+      stash();
+      __syncthreads();
+    }
+  }
+  epilogue<MQ>(a, co, acc, red);
+}
+
+template <int MQ, int KT>
+hipError_t launch_mqk(const FusedArgs& a, hipStream_t s) {
+  const int nblk = (int)((a.C_out + CB - 1) / CB);
+  dim3 grid((unsigned)(a.N * nblk));
+  const bool direct = (a.T % 4 == 0) && ((((uintptr_t)a.x) & 15) == 0);
+  if (direct)
+    hipLaunchKernelGGL((fused_gn_dma_kernel<MQ, KT>), grid, dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL((fused_gn_regs_kernel<MQ, KT>), grid, dim3(NTHR), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int MQ>
 hipError_t launch_mq(const FusedArgs& a, hipStream_t s) {
-  const int nblk = (int)((a.C_out + CB - 1) / CB);
-  dim3 grid((unsigned)(a.N * nblk));
-  hipLaunchKernelGGL(fused_conv_gn_kernel<MQ>, grid, dim3(NTHR), 0, s, a);
-  return hipGetLastError();
+  switch (a.K) {
+    case 1: return launch_mqk<MQ, 1>(a, s);
+    case 2: return launch_mqk<MQ, 2>(a, s);
+    case 3: return launch_mqk<MQ, 3>(a, s);
+    case 4: return launch_mqk<MQ, 4>(a, s);
+    case 5: return launch_mqk<MQ, 5>(a, s);
+    case 6: return launch_mqk<MQ, 6>(a, s);
+    case 7: return launch_mqk<MQ, 7>(a, s);
+    case 8: return launch_mqk<MQ, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -246,9 +416,10 @@ int fused_gn_max_tout(int stride, int K, int dilation) {
   return NW * 8 * 16;
 }
 
-bool fused_gn_supported(int64_t C_out, int32_t G, int64_t T_out, int stride, int K,
-                        int dilation) {
+bool fused_gn_supported(int64_t C_in, int64_t C_out, int32_t G, int64_t T_out, int stride,
+                        int K, int dilation) {
   if (G < 1 || C_out % G) return false;
+  if (C_out * C_in * K >= (1ll << 31)) return false;  // 32-bit weight offsets
   const int64_t cpg = C_out / G;
   if (cpg > CB || (CB % cpg) != 0) return false;
   return T_out >= 1 && T_out <= fused_gn_max_tout(stride, K, dilation);

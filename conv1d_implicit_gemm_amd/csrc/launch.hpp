@@ -69,8 +69,8 @@ struct FusedArgs {
   float eps;
 };
 int fused_gn_max_tout(int stride, int K, int dilation);  // 0 if unsupported
-bool fused_gn_supported(int64_t C_out, int32_t G, int64_t T_out, int stride, int K,
-                        int dilation);
+bool fused_gn_supported(int64_t C_in, int64_t C_out, int32_t G, int64_t T_out, int stride,
+                        int K, int dilation);
 hipError_t fused_gn_launch(const FusedArgs& a, hipStream_t s);
 
 // ---- normalisation kernels (k_norm.hip)
