@@ -14,7 +14,7 @@ using namespace c1g;
 
 namespace {
 
-enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT };
+enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT, R_GEMM };
 
 struct Plan {
   int status = C1G_OK;
@@ -23,6 +23,7 @@ struct Plan {
   bool bf16 = false;
   int norm = C1G_NORM_NONE, epi = C1G_EPI_NONE;
   int n_chunks = 0, n_ttiles = 0, n_ctiles = 0, tm = 0, tn = 0;
+  bool gemm_fused = false;  // R_GEMM: GroupNorm + row-min inside the GEMM epilogue
   size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, total = 0;
 };
 
@@ -73,18 +74,42 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
 
   // route
   const bool want_gn = p.norm == C1G_NORM_GROUP, want_ln = p.norm == C1G_NORM_LAYER_CHANNELS;
+  const bool conv_only = p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE;
   if (!p.bf16 && want_gn && p.epi == C1G_EPI_NONE &&
       fused_gn_supported(d->C_in, d->C_out, nd->G, p.T_out, d->stride, d->K, d->dilation)) {
     p.route = R_FUSED;
     p.total = 0;
     return p;
   }
-  p.route = (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE) ? R_CONV_ONLY : R_SPLIT;
+  // K = 1, T = 1 (a Linear layer) in bf16: plain GEMM over rows n
+  if (p.bf16 && d->K == 1 && d->T == 1 && d->pad_left == 0 && d->pad_right == 0 &&
+      d->C_in % 8 == 0) {
+    p.route = R_GEMM;
+    p.tn = gemm_bf16_tile_c();
+    p.n_ctiles = (int)((d->C_out + p.tn - 1) / p.tn);
+    p.n_ttiles = (int)((d->N + gemm_bf16_tile_n() - 1) / gemm_bf16_tile_n());
+    p.gemm_fused = want_gn && p.epi == C1G_EPI_ROWMIN_BIAS && d->C_out / nd->G == 16;
+    size_t off = 0;
+    p.off_part = off;
+    off = align_up(off + (p.gemm_fused ? (size_t)d->N * p.n_ctiles * sizeof(float) : 0));
+    const size_t stat = want_gn ? (size_t)d->N * nd->G : want_ln ? (size_t)d->N : 0;
+    p.off_mean = off;
+    off = align_up(off + stat * sizeof(float));
+    p.off_rstd = off;
+    off = align_up(off + stat * sizeof(float));
+    p.total = conv_only ? 0 : off;
+    return p;
+  }
+  p.route = conv_only ? R_CONV_ONLY : R_SPLIT;
 
   size_t pack_bytes;
   if (p.bf16) {
-    p.status = C1G_ERR_UNSUPPORTED;  // bf16 kernels are built in a later step
-    return p;
+    const int tm = conv_bf16_tile_m(d->stride, d->K, d->dilation);
+    if (tm == 0) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+    p.tm = tm;
+    p.tn = ConvBf16Cfg::TN;
+    p.n_chunks = (int)((d->C_in + ConvBf16Cfg::CK - 1) / ConvBf16Cfg::CK);
+    pack_bytes = conv_bf16_packed_bytes(d->C_in, d->C_out, d->K);
   } else {
     if (d->K > 8) { p.status = C1G_ERR_UNSUPPORTED; return p; }
     const int64_t xw = (int64_t)(ConvF32Cfg::TM - 1) * d->stride +
@@ -146,10 +171,72 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
   a.n_chunks = p.n_chunks;
   a.n_ttiles = p.n_ttiles;
   a.n_ctiles = p.n_ctiles;
-  hipError_t e = conv_f32_pack((const float*)w, (float*)(ws + p.off_pack), d->C_in, d->C_out,
-                               d->K, s);
+  hipError_t e;
+  if (p.bf16) {
+    e = conv_bf16_pack((const uint16_t*)w, (uint16_t*)(ws + p.off_pack), d->C_in, d->C_out,
+                       d->K, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    return hip_status(conv_bf16_launch(a, epi, s));
+  }
+  e = conv_f32_pack((const float*)w, (float*)(ws + p.off_pack), d->C_in, d->C_out, d->K, s);
   if (e != hipSuccess) return C1G_ERR_HIP;
   return hip_status(conv_f32_launch(a, epi, s));
+}
+
+// K = 1, T = 1 bf16 GEMM route: y[n][c] (== out viewed as [N, C_out, 1]).
+int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
+             const void* w, const float* bias, const float* gamma, const float* beta,
+             const float* bias2, float* out, float* mean_out, float* rstd_out, char* ws,
+             hipStream_t s) {
+  if (!aligned(x, 16) || !aligned(w, 16)) return C1G_ERR_MISALIGNED;
+  GemmArgs g;
+  g.x = x;
+  g.w = w;
+  g.bias = bias;
+  g.gamma = gamma;
+  g.beta = beta;
+  g.y = out;
+  g.part = (float*)(ws + p.off_part);
+  g.mean_out = mean_out;
+  g.rstd_out = rstd_out;
+  g.N = d->N;
+  g.C_in = d->C_in;
+  g.C_out = d->C_out;
+  g.G = nd ? nd->G : 0;
+  g.n_ctiles = p.n_ctiles;
+  g.n_ntiles = p.n_ttiles;
+  g.eps = nd ? nd->eps : 0.f;
+  if (p.gemm_fused) {
+    hipError_t e = gemm_bf16_launch(g, GEMM_GN_ROWMIN, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    return hip_status(rowmin_bcast_launch(g.part, d->N, p.n_ctiles, bias2, out, d->C_out, s));
+  }
+  hipError_t e = gemm_bf16_launch(g, GEMM_STORE, s);
+  if (e != hipSuccess) return C1G_ERR_HIP;
+  if (!nd || (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE)) return C1G_OK;
+  // y is [N, C_out, 1]: a group's values are contiguous, as are a row's channels
+  float* mean = mean_out ? mean_out : (float*)(ws + p.off_mean);
+  float* rstd = rstd_out ? rstd_out : (float*)(ws + p.off_rstd);
+  if (p.norm == C1G_NORM_GROUP) {
+    e = gn_stats_launch(out, d->N, d->C_out, 1, nd->G, nd->eps, mean, rstd, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    e = (p.epi == C1G_EPI_NONE)
+            ? gn_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, 1, nd->G, s)
+            : rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, 1,
+                                 nd->G, 1, s);
+  } else if (p.norm == C1G_NORM_LAYER_CHANNELS) {
+    // LayerNorm over the channels of one position == GroupNorm with one group
+    e = gn_stats_launch(out, d->N, d->C_out, 1, 1, nd->eps, mean, rstd, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    e = (p.epi == C1G_EPI_NONE)
+            ? ln_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, 1, s)
+            : rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, 1, 0,
+                                 2, s);
+  } else {
+    e = rowmin_bias_launch(out, nullptr, nullptr, nullptr, nullptr, bias2, out, d->N, d->C_out,
+                           1, 0, 0, s);
+  }
+  return hip_status(e);
 }
 
 const char* route_name(int r) {
@@ -157,6 +244,7 @@ const char* route_name(int r) {
     case R_CONV_ONLY: return "conv_only";
     case R_FUSED: return "fused_single_pass";
     case R_SPLIT: return "split";
+    case R_GEMM: return "gemm_rows";
     default: return "invalid";
   }
 }
@@ -203,6 +291,9 @@ int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const f
   if (!aligned(x, es) || !aligned(w, es) || !aligned(y, 4) || (bias && !aligned(bias, 4)))
     return C1G_ERR_MISALIGNED;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
+  if (p.route == R_GEMM)
+    return run_gemm(p, d, nullptr, x, w, bias, nullptr, nullptr, nullptr, y, nullptr, nullptr,
+                    (char*)ws, (hipStream_t)stream);
   return run_conv(p, d, x, w, bias, y, (char*)ws, EPI_STORE, (hipStream_t)stream);
 }
 
@@ -278,6 +369,8 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
     a.eps = nd->eps;
     return hip_status(fused_gn_launch(a, s));
   }
+  if (p.route == R_GEMM)
+    return run_gemm(p, d, nd, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, wsb, s);
   if (p.route == R_CONV_ONLY)
     return run_conv(p, d, x, w, bias, out, wsb, EPI_STORE, s);
 

@@ -1,0 +1,134 @@
+// Epilogue shared by the split-path implicit-GEMM convolution kernels.
+//
+// The workgroup tile is TM = WGM*WM*16 output positions x TN = WGN*WN*16
+// output channels; wave (wm, wn) owns WM x WN MFMA 16x16 tiles, lane
+// (lr = lane%16, kq = lane/16) holding rows t = 4*kq + r (r = 0..3) of column
+// c = lr of each tile.
+//
+//   EPI_STORE    y = acc + bias
+//   EPI_GN_PART  also, per channel, (mean, M2) over the tile's valid
+//                positions -> part[(n*C_out + c)*n_ttiles + ttile]
+//   EPI_LN_PART  also, per position, (mean, M2) over the tile's valid
+//                channels  -> part[(n*n_ctiles + ctile)*T_out + t]
+//
+// Partial statistics: two passes over the registers (mean, then squared
+// deviations), xor-shuffle sums across lanes, then a fixed-order pairwise
+// merge across waves through LDS; every partial has one fixed slot (no
+// atomics), so the later merge is deterministic.
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace c1g {
+
+template <int WM, int WN, int WGM, int WGN>
+__device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
+                                              f32x4 (&acc)[WM][WN], int64_t n, int64_t t0,
+                                              int c0, int ttile, int ctile, int wm, int wn,
+                                              Stats* red) {
+  constexpr int TM = WGM * WM * 16, TN = WGN * WN * 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int64_t T_out = a.T_out;
+  const bool vec_ok = ((T_out & 3) == 0) && ((((uintptr_t)a.y) & 15) == 0);
+#pragma unroll
+  for (int jn = 0; jn < WN; ++jn) {
+    const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+    const float b = (a.bias != nullptr && c < a.C_out) ? a.bias[c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      acc[i][jn] += b;
+      if (c < a.C_out) {
+        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq;
+        float* dst = a.y + (n * a.C_out + c) * T_out;
+        if (vec_ok && t + 3 < T_out) {
+          *(f32x4*)(dst + t) = acc[i][jn];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (t + r < T_out) dst[t + r] = acc[i][jn][r];
+        }
+      }
+    }
+  }
+  if (epi == EPI_STORE) return;
+
+  __syncthreads();  // the staging LDS is free again: reuse it for the cross-wave merge
+
+  if (epi == EPI_GN_PART) {
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      float sum = 0.f, cnt = 0.f;
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
+          if (t < T_out) { sum += acc[i][jn][r]; cnt += 1.f; }
+        }
+      sum = xor_sum<48>(sum);
+      cnt = xor_sum<48>(cnt);
+      const float mean = cnt > 0.f ? sum / cnt : 0.f;
+      float m2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
+          if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
+        }
+      m2 = xor_sum<48>(m2);
+      if (kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
+    }
+    __syncthreads();
+    for (int cl = tid; cl < TN; cl += blockDim.x) {
+      const int c = c0 + cl;
+      if (c < a.C_out) {
+        Stats st = red[cl];
+#pragma unroll
+        for (int w = 1; w < WGM; ++w) st = stats_merge(st, red[w * TN + cl]);
+        f32x2 v = {st.mean, st.m2};
+        *(f32x2*)(a.part + ((n * a.C_out + c) * a.n_ttiles + ttile) * 2) = v;
+      }
+    }
+  } else {  // EPI_LN_PART
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sum = 0.f, cnt = 0.f;
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn) {
+          const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+          if (c < a.C_out) { sum += acc[i][jn][r]; cnt += 1.f; }
+        }
+        sum = xor_sum<15>(sum);
+        cnt = xor_sum<15>(cnt);
+        const float mean = cnt > 0.f ? sum / cnt : 0.f;
+        float m2 = 0.f;
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn) {
+          const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+          if (c < a.C_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
+        }
+        m2 = xor_sum<15>(m2);
+        const int tl = wm * WM * 16 + i * 16 + 4 * kq + r;
+        if (lr == 0) red[wn * TM + tl] = Stats{cnt, mean, m2};
+      }
+    __syncthreads();
+    for (int tl = tid; tl < TM; tl += blockDim.x) {
+      const int64_t t = t0 + tl;
+      if (t < T_out) {
+        Stats st = red[tl];
+#pragma unroll
+        for (int w = 1; w < WGN; ++w) st = stats_merge(st, red[w * TM + tl]);
+        f32x2 v = {st.mean, st.m2};
+        *(f32x2*)(a.part + ((n * a.n_ctiles + ctile) * T_out + t) * 2) = v;
+      }
+    }
+  }
+}
+
+}  // namespace c1g

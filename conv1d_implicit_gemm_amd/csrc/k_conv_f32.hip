@@ -19,6 +19,7 @@
 // LayerNorm over channels.  Partials are written to fixed slots (no atomics),
 // so the later merge is deterministic.
 #include "common.hpp"
+#include "conv_epilogue.hpp"
 #include "launch.hpp"
 
 namespace c1g {
@@ -148,103 +149,7 @@ __global__ __launch_bounds__(NTHR) void conv_f32_kernel(ConvArgs a, int epi) {
     }
   }
 
-  // ---------------------------------------------------------------- epilogue
-  const int64_t T_out = a.T_out;
-  const bool vec_ok = ((T_out & 3) == 0) && ((((uintptr_t)a.y) & 15) == 0);
-#pragma unroll
-  for (int jn = 0; jn < WN; ++jn) {
-    const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-    const float b = (a.bias != nullptr && c < a.C_out) ? a.bias[c] : 0.f;
-#pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      acc[i][jn] += b;
-      if (c < a.C_out) {
-        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq;
-        float* dst = a.y + (n * a.C_out + c) * T_out;
-        if (vec_ok && t + 3 < T_out) {
-          *(f32x4*)(dst + t) = acc[i][jn];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (t + r < T_out) dst[t + r] = acc[i][jn][r];
-        }
-      }
-    }
-  }
-  if (epi == EPI_STORE) return;
-
-  __syncthreads();  // LDS is free again: reuse it for the cross-wave merge
-  Stats* red = (Stats*)lds;
-
-  if (epi == EPI_GN_PART) {
-    // per channel: statistics over this tile's valid positions
-#pragma unroll
-    for (int jn = 0; jn < WN; ++jn) {
-      float sum = 0.f, cnt = 0.f;
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-          if (t < T_out) { sum += acc[i][jn][r]; cnt += 1.f; }
-        }
-      sum = xor_sum<48>(sum);
-      cnt = xor_sum<48>(cnt);
-      const float mean = cnt > 0.f ? sum / cnt : 0.f;
-      float m2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-          if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
-        }
-      m2 = xor_sum<48>(m2);
-      if (kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
-    }
-    __syncthreads();
-    if (tid < TN) {
-      const int c = c0 + tid;
-      if (c < a.C_out) {
-        const Stats st = stats_merge(red[tid], red[TN + tid]);
-        f32x2 v = {st.mean, st.m2};
-        *(f32x2*)(a.part + ((n * a.C_out + c) * a.n_ttiles + ttile) * 2) = v;
-      }
-    }
-  } else {  // EPI_LN_PART: per position, statistics over this tile's channels
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sum = 0.f, cnt = 0.f;
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) {
-          const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-          if (c < a.C_out) { sum += acc[i][jn][r]; cnt += 1.f; }
-        }
-        sum = xor_sum<15>(sum);
-        cnt = xor_sum<15>(cnt);
-        const float mean = cnt > 0.f ? sum / cnt : 0.f;
-        float m2 = 0.f;
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) {
-          const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-          if (c < a.C_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
-        }
-        m2 = xor_sum<15>(m2);
-        const int tl = wm * WM * 16 + i * 16 + 4 * kq + r;
-        if (lr == 0) red[wn * TM + tl] = Stats{cnt, mean, m2};
-      }
-    __syncthreads();
-    if (tid < TM) {
-      const int64_t t = t0 + tid;
-      if (t < T_out) {
-        const Stats st = stats_merge(red[tid], red[TM + tid]);
-        f32x2 v = {st.mean, st.m2};
-        *(f32x2*)(a.part + ((n * a.n_ctiles + ctile) * T_out + t) * 2) = v;
-      }
-    }
-  }
+  conv_epilogue<WM, WN, 2, 2>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)lds);
 }
 
 // Weight image: wp[((ctile*n_chunks + chunk)*K*CK + j*CK + cl)*TN + c]

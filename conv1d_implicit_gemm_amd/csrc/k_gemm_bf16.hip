@@ -1,0 +1,262 @@
+// bf16 GEMM for the K = 1, T = 1 convolution (a Linear layer):
+//   y[n][c] = sum_ci x[n][ci] * w[c][ci]      (x [N, C_in], w [C_out, C_in])
+// with an optional fused GroupNorm + per-row min epilogue ("Kimi-K2.6 l2_p75":
+// Linear -> GroupNorm -> min over channels -> + bias broadcast; with T = 1 a
+// GroupNorm group is C_out/G consecutive channels of one row).
+//
+// MFMA view (v_mfma_f32_16x16x32_bf16): A = w (rows c), B = x^T (columns n);
+// both operands are contiguous along the reduction, so each 64-element chunk
+// of a row is copied global -> LDS with direct loads into rows of 144 bytes
+// (72 bf16, the last 16 bytes unused) so the 16-byte operand reads of 8
+// consecutive rows hit 8 distinct bank groups.  Workgroup: 256 threads = 2x2
+// waves, tile 256 (c) x 128 (n), wave tile 128 x 64 = 8 x 4 MFMA tiles;
+// two LDS stages (the next chunk streams in while the current one is used).
+// Workgroups are mapped so that each XCD works on a compact block of tiles and
+// its L2 serves the shared rows of w and x.
+//
+// Result layout: lane (lr, kq), register r of tile (i, j) holds
+// c = c0 + 16 i + 4 kq + r, n = n0 + 16 j + lr, so a 16-channel group of one
+// row is exactly one MFMA tile column (4 registers x 4 lanes).
+//
+// Epilogues: GEMM_STORE writes y (+bias).  GEMM_GN_ROWMIN (C_out/G == 16)
+// normalises each group in registers (two-pass mean/variance over its 16
+// values), applies gamma/beta, and reduces min over the tile's channels into
+// one partial per (n, c-tile) (fixed slots, no atomics); optional mean/rstd
+// outputs.  rowmin_bcast then folds the partials in a fixed order and writes
+// out[n][c] = min + bias2[c].
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace c1g {
+namespace {
+
+constexpr int NTHR = 256;
+constexpr int BM = 256;        // channels per tile (A rows)
+constexpr int BN = 128;        // samples per tile (B rows)
+constexpr int KC = 64;         // reduction chunk
+constexpr int RS = KC + 8;     // LDS row stride in bf16 (144 bytes)
+constexpr int SLOTS = RS / 8;  // 16-byte slots per LDS row (8 data + 1 unused)
+constexpr int WMT = 8, WNT = 4;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef uint16_t u16;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+
+// Copy rows [r0, r0+rows) x [k0, k0+KC) of a row-major [R, C_in] bf16 matrix
+// into an LDS stage of `rows` x RS.  Slot e of the stage (row e / SLOTS,
+// column group e % SLOTS) is written by lane e % 64 of instruction e / 64.
+// Rows past R read row R-1 (their results are never used); column groups past
+// C_in are zero-filled with ordinary LDS stores instead of loaded.
+template <int ROWS>
+__device__ __forceinline__ void stage_rows(const u16* __restrict__ g, int64_t R, int64_t C_in,
+                                           int64_t r0, int64_t k0, u16* lds, int wave,
+                                           int lane) {
+  constexpr int NS = ROWS * SLOTS;
+  for (int p = wave; p * 64 < NS; p += 4) {
+    const int e = p * 64 + lane;
+    const int row = e / SLOTS, q = e - row * SLOTS;
+    int64_t gr = r0 + row;
+    if (gr > R - 1) gr = R - 1;
+    const int64_t k = k0 + 8 * (q < 8 ? q : 0);
+    const bool live = e < NS && q < 8;
+    if (live && k < C_in)
+      dma16(g + gr * C_in + k, (char*)lds + p * 1024);
+    else if (live)
+      *(u32x4*)(lds + row * RS + 8 * q) = (u32x4){0u, 0u, 0u, 0u};
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 As0[BM * RS];
+  __shared__ __attribute__((aligned(16))) u16 As1[BM * RS];
+  __shared__ __attribute__((aligned(16))) u16 Bs0[BN * RS];
+  __shared__ __attribute__((aligned(16))) u16 Bs1[BN * RS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wc = wave & 1, wnn = wave >> 1;
+  const int lr = lane & 15, kq = lane >> 4;
+
+  // XCD-aware tile order: blocks round-robin over 8 XCDs; give XCD x the
+  // contiguous tile range [x*tiles/8, (x+1)*tiles/8), enumerated n-tile fastest
+  // so the c-tiles (rows of w) it touches are few and shared in its L2.
+  const int tiles = a.n_ctiles * a.n_ntiles;
+  int lin = blockIdx.x;
+  if ((tiles & 7) == 0) lin = (blockIdx.x & 7) * (tiles >> 3) + (blockIdx.x >> 3);
+  const int ntile = lin % a.n_ntiles, ctile = lin / a.n_ntiles;
+  const int64_t c0 = (int64_t)ctile * BM, n0 = (int64_t)ntile * BN;
+
+  const u16* __restrict__ w = (const u16*)a.w;
+  const u16* __restrict__ x = (const u16*)a.x;
+  const int n_chunks = (int)((a.C_in + KC - 1) / KC);
+
+  f32x4 acc[WMT][WNT];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int arow = wc * WMT * 16 + lr, brow = wnn * WNT * 16 + lr;
+  auto compute = [&](const u16* as, const u16* bs) {
+    bf16x8 av[WMT], bv[WNT];
+#pragma unroll
+    for (int ks = 0; ks < KC / 32; ++ks) {
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+        av[i] = *(const bf16x8*)(as + (arow + 16 * i) * RS + 32 * ks + 8 * kq);
+#pragma unroll
+      for (int j = 0; j < WNT; ++j)
+        bv[j] = *(const bf16x8*)(bs + (brow + 16 * j) * RS + 32 * ks + 8 * kq);
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) acc[i][j] = mfma16x16x32bf16(av[i], bv[j], acc[i][j]);
+    }
+  };
+  auto stage = [&](int chunk, u16* as, u16* bs) {
+    const int64_t k0 = (int64_t)chunk * KC;
+    stage_rows<BM>(w, a.C_out, a.C_in, c0, k0, as, wave, lane);
+    stage_rows<BN>(x, a.N, a.C_in, n0, k0, bs, wave, lane);
+  };
+
+  stage(0, As0, Bs0);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; c += 2) {
+    if (c + 1 < n_chunks) stage(c + 1, As1, Bs1);
+    compute(As0, Bs0);
+    __syncthreads();
+    if (c + 1 >= n_chunks) break;
+    if (c + 2 < n_chunks) stage(c + 2, As0, Bs0);
+    compute(As1, Bs1);
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------------ epilogue
+  if (EPI == GEMM_STORE) {
+    const bool vec = (a.C_out % 4 == 0) && ((((uintptr_t)a.y) & 15) == 0);
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      const int64_t c = c0 + wc * WMT * 16 + 16 * i + 4 * kq;
+      f32x4 b = {0.f, 0.f, 0.f, 0.f};
+      if (a.bias)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[r] = (c + r < a.C_out) ? a.bias[c + r] : 0.f;
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const int64_t nn = n0 + wnn * WNT * 16 + 16 * j + lr;
+        if (nn >= a.N) continue;
+        const f32x4 v = acc[i][j] + b;
+        float* dst = a.y + nn * a.C_out + c;
+        if (vec && c + 3 < a.C_out) {
+          *(f32x4*)dst = v;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (c + r < a.C_out) dst[r] = v[r];
+        }
+      }
+    }
+  } else {  // GEMM_GN_ROWMIN: groups of 16 channels = one tile column block
+    float* red = (float*)As0;  // free after the last barrier
+    float rmin[WNT];
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) rmin[j] = __builtin_inff();
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) {
+      const int64_t cg = c0 + wc * WMT * 16 + 16 * i;  // first channel of the group
+      const bool gvalid = cg < a.C_out;
+      const int64_t c = cg + 4 * kq;
+      f32x4 ga = {1.f, 1.f, 1.f, 1.f}, be = {0.f, 0.f, 0.f, 0.f}, bi = {0.f, 0.f, 0.f, 0.f};
+      if (gvalid) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (a.gamma) ga[r] = a.gamma[c + r];
+          if (a.beta) be[r] = a.beta[c + r];
+          if (a.bias) bi[r] = a.bias[c + r];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WNT; ++j) {
+        const f32x4 v = acc[i][j] + bi;
+        float s = (v[0] + v[1]) + (v[2] + v[3]);
+        s += shfl_xor(s, 16);
+        s += shfl_xor(s, 32);
+        const float mean = s * (1.0f / 16.0f);
+        float q = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { const float dv = v[r] - mean; q += dv * dv; }
+        q += shfl_xor(q, 16);
+        q += shfl_xor(q, 32);
+        const float rstd = 1.0f / sqrtf(q * (1.0f / 16.0f) + a.eps);
+        float m = __builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fminf(m, (v[r] - mean) * (rstd * ga[r]) + be[r]);
+        if (gvalid) rmin[j] = fminf(rmin[j], m);
+        const int64_t nn = n0 + wnn * WNT * 16 + 16 * j + lr;
+        if (gvalid && kq == 0 && nn < a.N) {
+          const int64_t g = cg / 16;
+          if (a.mean_out) a.mean_out[nn * a.G + g] = mean;
+          if (a.rstd_out) a.rstd_out[nn * a.G + g] = rstd;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WNT; ++j) {
+      float m = rmin[j];
+      m = fminf(m, shfl_xor(m, 16));
+      m = fminf(m, shfl_xor(m, 32));
+      if (kq == 0) red[wc * BN + wnn * WNT * 16 + 16 * j + lr] = m;
+    }
+    __syncthreads();
+    if (tid < BN) {
+      const int64_t nn = n0 + tid;
+      if (nn < a.N) a.part[nn * a.n_ctiles + ctile] = fminf(red[tid], red[BN + tid]);
+    }
+  }
+}
+
+// out[n][c] = min over c-tiles of part[n][*] + bias2[c]; one workgroup per row
+__global__ __launch_bounds__(NTHR) void rowmin_bcast_kernel(const float* __restrict__ part,
+                                                            int n_ctiles,
+                                                            const float* __restrict__ bias2,
+                                                            float* out, int64_t C) {
+  const int64_t n = blockIdx.x;
+  float m = __builtin_inff();
+  for (int t = 0; t < n_ctiles; ++t) m = fminf(m, part[n * n_ctiles + t]);
+  float* row = out + n * C;
+  if ((C % 4) == 0 && (((uintptr_t)out) & 15) == 0 && (((uintptr_t)bias2) & 15) == 0) {
+    for (int64_t q = threadIdx.x; q < C / 4; q += NTHR) {
+      const f32x4 b = *(const f32x4*)(bias2 + 4 * q);
+      *(f32x4*)(row + 4 * q) = b + m;
+    }
+  } else {
+    for (int64_t c = threadIdx.x; c < C; c += NTHR) row[c] = m + bias2[c];
+  }
+}
+
+}  // namespace
+
+hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s) {
+  dim3 grid((unsigned)(a.n_ctiles * a.n_ntiles));
+  if (epi == GEMM_STORE)
+    hipLaunchKernelGGL(gemm_bf16_kernel<GEMM_STORE>, grid, dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemm_bf16_kernel<GEMM_GN_ROWMIN>, grid, dim3(NTHR), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const float* bias2,
+                               float* out, int64_t C, hipStream_t s) {
+  hipLaunchKernelGGL(rowmin_bcast_kernel, dim3((unsigned)N), dim3(NTHR), 0, s, part, n_ctiles,
+                     bias2, out, C);
+  return hipGetLastError();
+}
+
+int gemm_bf16_tile_c() { return BM; }
+int gemm_bf16_tile_n() { return BN; }
+
+}  // namespace c1g

@@ -43,14 +43,39 @@ hipError_t conv_f32_pack(const float* w, float* wp, int64_t C_in, int64_t C_out,
 hipError_t conv_f32_launch(const ConvArgs& a, int epi, hipStream_t s);
 
 // ---- bf16 split-path convolution (k_conv_bf16.hip)
+// Tile: TM (256 or 64, chosen from stride/K/dilation) positions x TN channels,
+// CK input channels per chunk; taps K <= 5.
 struct ConvBf16Cfg {
-  static constexpr int TM = 128, TN = 128, CK = 32;
+  static constexpr int TN = 128, CK = 32;
 };
-int conv_bf16_window_cap(int stride);
+int conv_bf16_tile_m(int stride, int K, int dilation);  // 0 if unsupported
 size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K);
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
                           hipStream_t s);
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s);
+
+// ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
+enum GemmEpi : int { GEMM_STORE = 0, GEMM_GN_ROWMIN = 1 };
+struct GemmArgs {
+  const void* x;       // [N, C_in] bf16, 16-byte aligned, C_in % 8 == 0
+  const void* w;       // [C_out, C_in] bf16, 16-byte aligned
+  const float* bias;   // [C_out] or nullptr
+  const float* gamma;  // GN_ROWMIN: [C_out] or nullptr
+  const float* beta;
+  float* y;            // STORE: [N, C_out]
+  float* part;         // GN_ROWMIN: [N, n_ctiles] per-tile row minima
+  float* mean_out;     // GN_ROWMIN: [N, G] or nullptr
+  float* rstd_out;
+  int64_t N, C_in, C_out;
+  int32_t G, n_ctiles, n_ntiles;
+  float eps;
+};
+int gemm_bf16_tile_c();
+int gemm_bf16_tile_n();
+hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s);
+// out[n][c] = min_t part[n][t] + bias2[c]
+hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const float* bias2,
+                               float* out, int64_t C, hipStream_t s);
 
 // ---- fp32 fused conv + GroupNorm, one workgroup per (n, 16-channel block)
 // (k_fused_gn.hip).  Supported when C_out/G divides 16 and the whole

@@ -89,6 +89,15 @@ def test_routes():
     assert c1g.route(_desc(), c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == "split"
     assert c1g.route(_desc(), c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 1)) == "split"
     assert c1g.route(_desc()) == "conv_only"
+    bf = c1g.C1G_BF16
+    lin = _desc(N=1024, C_in=8192, C_out=8192, T=1, K=1, pad_left=0, pad_right=0, dtype=bf)
+    assert c1g.route(lin, c1g.NormDesc(c1g.NORM_GROUP, 512, 1e-5, 1)) == "gemm_rows"
+    assert c1g.route(lin) == "gemm_rows"
+    conv = _desc(N=64, C_in=512, C_out=1024, T=4096, K=5, dilation=2, pad_left=2,
+                 pad_right=2, dtype=bf)
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0)) == "split"
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == "split"
+    assert c1g.route(conv) == "conv_only"
 
 
 def test_workspace_sizes():
@@ -108,6 +117,8 @@ def test_unsupported_sizes():
     assert c1g.check(_desc(K=9, pad_left=4, pad_right=4)) == 2
     # input window wider than any tile variant
     assert c1g.check(_desc(stride=8, T=4096)) == 2
+    # bf16 convolution: taps beyond the weight stages
+    assert c1g.check(_desc(K=6, pad_left=2, pad_right=3, dtype=c1g.C1G_BF16)) == 2
 
 
 def test_binding_rejects_cpu_tensors():

@@ -1,0 +1,99 @@
+"""GPU parity of the bf16 path (bf16 x and w, fp32 accumulation and outputs)
+against the fp64 oracle on the same bf16 values: max-abs 2e-2 after
+normalisation, element by element."""
+import numpy as np
+import pytest
+import torch
+
+import conv1d_implicit_gemm_amd as c1g
+from conv1d_implicit_gemm_amd.workloads import WORKLOADS, Workload, make_inputs
+from tests.gpu_util import (TOL_BF16, announce, check_parity, max_abs_err, run_library,
+                            run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+W = Workload
+BF = dict(dtype="bf16")
+# conv tiles: 128 (or 64 for wide windows) positions x 128 channels, 32 input
+# channels per chunk; shapes span several tiles and end in ragged tails
+CONV_CASES = [
+    W("bf16_conv_gn_k5d2", N=2, C_in=72, C_out=160, T=300, K=5, dilation=2, pad_left=2,
+      pad_right=2, G=8, **BF),
+    W("bf16_conv_gn_causal", N=2, C_in=64, C_out=96, T=264, K=4, pad_left=3, G=12, **BF),
+    W("bf16_conv_gn_odd_T", N=2, C_in=40, C_out=64, T=203, K=3, pad_left=1, pad_right=1,
+      G=4, **BF),
+    W("bf16_conv_gn_stride3_tile64", N=2, C_in=33, C_out=48, T=401, K=3, stride=3,
+      pad_left=1, pad_right=1, G=6, **BF),
+    W("bf16_conv_only", N=3, C_in=48, C_out=130, T=256, K=2, norm=None, **BF),
+    W("bf16_conv_ln", N=2, C_in=64, C_out=200, T=140, K=5, dilation=2, pad_left=2,
+      pad_right=2, norm="layer_channels", **BF),
+    W("bf16_conv_gn_rowmin", N=2, C_in=32, C_out=64, T=96, K=3, pad_left=1, pad_right=1,
+      G=4, rowmin_bias=True, **BF),
+]
+
+
+@pytest.mark.parametrize("wl", CONV_CASES, ids=lambda w: w.name)
+def test_bf16_conv_parity(wl):
+    check_parity(wl)
+
+
+# K = 1, T = 1: the GEMM route, with every epilogue combination
+GEMM_CASES = [
+    W("gemm_gn_rowmin_fused", N=70, C_in=256, C_out=512, T=1, K=1, G=32, bias=False,
+      rowmin_bias=True, **BF),
+    W("gemm_gn_rowmin_ragged", N=130, C_in=136, C_out=272, T=1, K=1, G=17, rowmin_bias=True,
+      **BF),
+    W("gemm_gn_rowmin_cpg8", N=40, C_in=64, C_out=256, T=1, K=1, G=32, rowmin_bias=True, **BF),
+    W("gemm_gn", N=33, C_in=96, C_out=128, T=1, K=1, G=8, **BF),
+    W("gemm_ln", N=33, C_in=96, C_out=200, T=1, K=1, norm="layer_channels", **BF),
+    W("gemm_only", N=50, C_in=64, C_out=300, T=1, K=1, norm=None, **BF),
+    W("gemm_rowmin_only", N=20, C_in=64, C_out=48, T=1, K=1, norm=None, rowmin_bias=True, **BF),
+]
+
+
+@pytest.mark.parametrize("wl", GEMM_CASES, ids=lambda w: w.name)
+def test_bf16_gemm_parity(wl):
+    check_parity(wl)
+
+
+def test_gemm_route_is_taken():
+    d = c1g.make_desc(1024, 8192, 8192, 1, 1, dtype=c1g.C1G_BF16)
+    assert c1g.route(d, c1g.make_norm("group", 512, 1e-5, True)) == "gemm_rows"
+
+
+def test_linear_gn_rowmin_full_size_sampled():
+    """The Linear -> GroupNorm -> min -> +bias workload at full size; the
+    oracle checks 12 whole rows (every row's result depends on that row only)."""
+    wl = WORKLOADS["gemm_gn_rowmin_bf16_m1024_n8192_k8192"]
+    announce(wl.name)
+    inp = make_inputs(wl, 0)
+    got = run_library(wl, inp)
+    rows = [0, 1, 2, 127, 128, 255, 256, 511, 640, 1000, 1022, 1023]
+    ref = run_oracle(wl, inp, n_slice=rows)
+    err = max_abs_err(got[rows], ref["out"])
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("name", ["conv1d_gn_bf16_n64_c512x1024_t4096_k5d2",
+                                  "conv1d_lnc_bf16_n64_c512x1024_t4096_k5d2"])
+def test_dilated_conv_full_size_sampled(name):
+    """The bf16 dilated-conv workload at full size; the oracle checks two whole
+    samples (GroupNorm and channel-LayerNorm statistics are per sample)."""
+    wl = WORKLOADS[name]
+    announce(wl.name)
+    inp = make_inputs(wl, 0)
+    got = run_library(wl, inp)
+    for n in (0, wl.N - 1):
+        ref = run_oracle(wl, inp, n_slice=slice(n, n + 1))
+        err = max_abs_err(got[n:n + 1], ref["out"])
+        assert err <= TOL_BF16, (n, err)
+
+
+def test_bf16_determinism():
+    wl = CONV_CASES[0]
+    announce("bf16 determinism")
+    inp = make_inputs(wl, 4)
+    assert torch.equal(run_library(wl, inp), run_library(wl, inp))
+    g = GEMM_CASES[0]
+    inp = make_inputs(g, 4)
+    assert torch.equal(run_library(g, inp), run_library(g, inp))
