@@ -14,8 +14,9 @@
 // once per call into the exact LDS image of each (c-tile, chunk) and streamed
 // with direct global->LDS loads.
 //
-// Workgroup: 256 threads = 2x2 waves; tile TM (t) x 128 (c); wave tile
-// (TM/2) x 64 = WM x 4 MFMA tiles.  Two LDS stages: the next chunk's weights
+// Workgroup: WGM x 2 waves; tile TM = WGM*WM*16 (t) x 128 (c); wave tile
+// WM x 4 MFMA tiles (256 x 128 with 8 waves of 64 x 64 for unit stride and
+// short halos, 64 x 128 with 4 waves otherwise).  Two LDS stages: the next chunk's weights
 // stream in and its window is fetched into registers while the current chunk
 // is consumed.  Epilogue: shared with the fp32 kernel (store y, GroupNorm or
 // channel-LayerNorm partial statistics).
@@ -30,12 +31,11 @@ constexpr int TN = ConvBf16Cfg::TN;  // 128 output channels per tile
 constexpr int CK = ConvBf16Cfg::CK;  // 32 input channels per chunk
 constexpr int RS = CK + 8;           // LDS row stride in bf16 (80 bytes)
 constexpr int KMAX = 5;              // taps (LDS budget of the weight stages)
-constexpr int NTHR = 256;
 constexpr int WN = 4;                // MFMA tiles per wave along c
+constexpr int WGN = 2;               // waves along c (TN = WGN * WN * 16)
 constexpr int XCAP = 288;            // window positions per stage
 constexpr int XTG = XCAP / 8;        // 8-position groups per window
 constexpr int XBLK = XTG * (CK / 8); // 8x8 blocks per window
-constexpr int XB = (XBLK + NTHR - 1) / NTHR;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint16_t u16;
@@ -58,9 +58,11 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-template <int WM, int KT, bool FAST>
-__global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
-  constexpr int TM = 2 * WM * 16;
+template <int WGM, int WM, int KT, bool FAST>
+__global__ __launch_bounds__(WGM * WGN * 64) void conv_bf16_kernel(ConvArgs a, int epi) {
+  constexpr int NTHR = WGM * WGN * 64, NWAVE = WGM * WGN;
+  constexpr int TM = WGM * WM * 16;
+  constexpr int XB = (XBLK + NTHR - 1) / NTHR;
   __shared__ __attribute__((aligned(16))) u16 Xs0[XCAP * RS];
   __shared__ __attribute__((aligned(16))) u16 Xs1[XCAP * RS];
   __shared__ __attribute__((aligned(16))) u16 Ws0[KMAX * TN * RS];
@@ -68,10 +70,17 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int lr = lane & 15, kq = lane >> 4;
-  const int ttile = blockIdx.x, ctile = blockIdx.y;
-  const int64_t n = blockIdx.z;
+  // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
+  // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
+  // c-tile fastest, so the channel tiles of one input window share an L2.
+  const int total = a.n_ttiles * a.n_ctiles * (int)a.N;
+  int lin = blockIdx.x;
+  if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int ctile = lin % a.n_ctiles;
+  const int ttile = (lin / a.n_ctiles) % a.n_ttiles;
+  const int64_t n = lin / (a.n_ctiles * a.n_ttiles);
   const int64_t t0 = (int64_t)ttile * TM;
   const int c0 = ctile * TN;
   const int s = a.stride, d = a.dilation;
@@ -132,7 +141,8 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   const int wbytes = KT * TN * RS * 2;
   auto dma_w = [&](int chunk, u16* ws) {
     const char* src = (const char*)(wp + ((int64_t)ctile * a.n_chunks + chunk) * (int64_t)(KT * TN * RS));
-    for (int p = wave; p * 1024 < wbytes; p += 4) dma16(src + p * 1024 + lane * 16, (char*)ws + p * 1024);
+    for (int p = wave; p * 1024 < wbytes; p += NWAVE)
+      dma16(src + p * 1024 + lane * 16, (char*)ws + p * 1024);
   };
 
   f32x4 acc[WM][WN];
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
     __syncthreads();
   }
 
-  conv_epilogue<WM, WN, 2, 2>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
+  conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
 }
 
 // Weight image: one block of KT*TN*RS bf16 per (ctile, chunk), laid out
@@ -209,25 +219,26 @@ __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict
   wp[idx] = (r < CK && co < C_out && ci < C_in) ? w[(co * C_in + ci) * K + j] : (u16)0;
 }
 
-template <int WM, int KT>
+template <int WGM, int WM, int KT>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
-  dim3 grid(a.n_ttiles, a.n_ctiles, (unsigned)a.N);
+  dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
+  constexpr int nthr = WGM * WGN * 64;
   const bool fast = (a.T % 8 == 0) && ((((uintptr_t)a.x) & 15) == 0);
   if (fast)
-    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, true>), grid, dim3(NTHR), 0, st, a, epi);
+    hipLaunchKernelGGL((conv_bf16_kernel<WGM, WM, KT, true>), grid, dim3(nthr), 0, st, a, epi);
   else
-    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, false>), grid, dim3(NTHR), 0, st, a, epi);
+    hipLaunchKernelGGL((conv_bf16_kernel<WGM, WM, KT, false>), grid, dim3(nthr), 0, st, a, epi);
   return hipGetLastError();
 }
 
-template <int WM>
+template <int WGM, int WM>
 hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st) {
   switch (a.K) {
-    case 1: return launch_wk<WM, 1>(a, epi, st);
-    case 2: return launch_wk<WM, 2>(a, epi, st);
-    case 3: return launch_wk<WM, 3>(a, epi, st);
-    case 4: return launch_wk<WM, 4>(a, epi, st);
-    case 5: return launch_wk<WM, 5>(a, epi, st);
+    case 1: return launch_wk<WGM, WM, 1>(a, epi, st);
+    case 2: return launch_wk<WGM, WM, 2>(a, epi, st);
+    case 3: return launch_wk<WGM, WM, 3>(a, epi, st);
+    case 4: return launch_wk<WGM, WM, 4>(a, epi, st);
+    case 5: return launch_wk<WGM, WM, 5>(a, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -241,7 +252,7 @@ int64_t window(int tm, int stride, int K, int dilation) {
 
 int conv_bf16_tile_m(int stride, int K, int dilation) {
   if (K < 1 || K > KMAX) return 0;
-  if (window(128, stride, K, dilation) <= XCAP) return 128;
+  if (window(256, stride, K, dilation) <= XCAP) return 256;
   if (window(64, stride, K, dilation) <= XCAP) return 64;
   return 0;
 }
@@ -263,8 +274,8 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
 
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
-  if (tm == 128) return launch_w<4>(a, epi, s);
-  if (tm == 64) return launch_w<2>(a, epi, s);
+  if (tm == 256) return launch_w<4, 4>(a, epi, s);  // 8 waves, 64 x 64 each
+  if (tm == 64) return launch_w<2, 2>(a, epi, s);   // 4 waves, 32 x 64 each
   return hipErrorInvalidValue;
 }
 
