@@ -83,7 +83,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   }
   // K = 1, T = 1 (a Linear layer) in bf16: plain GEMM over rows n
   if (p.bf16 && d->K == 1 && d->T == 1 && d->pad_left == 0 && d->pad_right == 0 &&
-      d->C_in % 8 == 0) {
+      d->C_in % 8 == 0 && (d->N > d->C_out ? d->N : d->C_out) * d->C_in < (1ll << 31)) {
     p.route = R_GEMM;
     p.tn = gemm_bf16_tile_c();
     p.n_ctiles = (int)((d->C_out + p.tn - 1) / p.tn);

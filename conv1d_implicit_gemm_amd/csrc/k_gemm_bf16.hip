@@ -6,11 +6,11 @@
 //
 // MFMA view (v_mfma_f32_16x16x32_bf16): A = w (rows c), B = x^T (columns n);
 // both operands are contiguous along the reduction, so each 64-element chunk
-// of a row is copied global -> LDS with direct loads into rows of 144 bytes
-// (72 bf16, the last 16 bytes unused) so the 16-byte operand reads of 8
-// consecutive rows hit 8 distinct bank groups.  Workgroup: 256 threads = 2x2
-// waves, tile 256 (c) x 128 (n), wave tile 128 x 64 = 8 x 4 MFMA tiles;
-// two LDS stages (the next chunk streams in while the current one is used).
+// of a row is loaded with 16-byte loads (two chunks ahead, into registers) and
+// written to LDS rows of 144 bytes (72 bf16, the last 16 bytes unused) so the
+// 16-byte operand reads of 8 consecutive rows hit 8 distinct bank groups.  Workgroup: 512 threads = 4x2
+// waves, tile 256 (c) x 128 (n), wave tile 64 x 64 = 4 x 4 MFMA tiles;
+// two LDS stages (one is read while the other is written from registers).
 // Workgroups are mapped so that each XCD works on a compact block of tiles and
 // its L2 serves the shared rows of w and x.
 //
@@ -30,55 +30,30 @@
 namespace c1g {
 namespace {
 
-constexpr int NTHR = 256;
+constexpr int WGC = 4, WGNN = 2;  // waves along c and along n
+constexpr int NWAVE = WGC * WGNN;
+constexpr int NTHR = NWAVE * 64;
 constexpr int BM = 256;        // channels per tile (A rows)
 constexpr int BN = 128;        // samples per tile (B rows)
-constexpr int KC = 64;         // reduction chunk
+constexpr int KC = 64;         // reduction chunk (two MFMA K-steps)
 constexpr int RS = KC + 8;     // LDS row stride in bf16 (144 bytes)
-constexpr int SLOTS = RS / 8;  // 16-byte slots per LDS row (8 data + 1 unused)
-constexpr int WMT = 8, WNT = 4;
+constexpr int QPR = KC / 8;    // 16-byte slots of data per row
+constexpr int NSLOT = (BM + BN) * QPR;           // slots per chunk (A rows, then B rows)
+constexpr int SPT = NSLOT / NTHR;                // slots per thread
+static_assert(NSLOT % NTHR == 0, "whole slots per thread");
+constexpr int WMT = BM / (16 * WGC), WNT = BN / (16 * WGNN);  // 4 x 4 MFMA tiles per wave
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint16_t u16;
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
-}
-
-// Copy rows [r0, r0+rows) x [k0, k0+KC) of a row-major [R, C_in] bf16 matrix
-// into an LDS stage of `rows` x RS.  Slot e of the stage (row e / SLOTS,
-// column group e % SLOTS) is written by lane e % 64 of instruction e / 64.
-// Rows past R read row R-1 (their results are never used); column groups past
-// C_in are zero-filled with ordinary LDS stores instead of loaded.
-template <int ROWS>
-__device__ __forceinline__ void stage_rows(const u16* __restrict__ g, int64_t R, int64_t C_in,
-                                           int64_t r0, int64_t k0, u16* lds, int wave,
-                                           int lane) {
-  constexpr int NS = ROWS * SLOTS;
-  for (int p = wave; p * 64 < NS; p += 4) {
-    const int e = p * 64 + lane;
-    const int row = e / SLOTS, q = e - row * SLOTS;
-    int64_t gr = r0 + row;
-    if (gr > R - 1) gr = R - 1;
-    const int64_t k = k0 + 8 * (q < 8 ? q : 0);
-    const bool live = e < NS && q < 8;
-    if (live && k < C_in)
-      dma16(g + gr * C_in + k, (char*)lds + p * 1024);
-    else if (live)
-      *(u32x4*)(lds + row * RS + 8 * q) = (u32x4){0u, 0u, 0u, 0u};
-  }
-}
-
 template <int EPI>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 As0[BM * RS];
-  __shared__ __attribute__((aligned(16))) u16 As1[BM * RS];
-  __shared__ __attribute__((aligned(16))) u16 Bs0[BN * RS];
-  __shared__ __attribute__((aligned(16))) u16 Bs1[BN * RS];
+  __shared__ __attribute__((aligned(16))) u16 As0[BM * RS], As1[BM * RS];
+  __shared__ __attribute__((aligned(16))) u16 Bs0[BN * RS], Bs1[BN * RS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wc = wave & 1, wnn = wave >> 1;
+  const int wc = wave % WGC, wnn = wave / WGC;
   const int lr = lane & 15, kq = lane >> 4;
 
   // XCD-aware tile order: blocks round-robin over 8 XCDs; give XCD x the
@@ -115,23 +90,64 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       for (int i = 0; i < WMT; ++i)
 #pragma unroll
         for (int j = 0; j < WNT; ++j) acc[i][j] = mfma16x16x32bf16(av[i], bv[j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);  // one K-step's operands live at a time
     }
   };
-  auto stage = [&](int chunk, u16* as, u16* bs) {
+  // Staging: thread tid owns slots tid + NTHR*i of a chunk (A rows first, then
+  // B rows; slot = row * QPR + 16-byte column group), so slot i of every thread
+  // is an A slot for i < SPT_A and a B slot after.  Loads are unconditional
+  // (rows past the matrix read its last row, reduction columns past C_in read
+  // column 0) and the zero padding of the reduction tail is applied when the
+  // registers are written to LDS; chunk c+2 is loaded while chunk c+1 waits in
+  // registers.
+  constexpr int SPT_A = BM * QPR / NTHR;
+  static_assert(BM * QPR % NTHR == 0, "A slots fill whole thread rounds");
+  const int q = tid % QPR;
+  const int rbase = tid / QPR;                 // row of slot 0 (A) / slot SPT_A (B)
+  constexpr int RSTEP = NTHR / QPR;            // rows between a thread's slots
+  const bool ktail = (a.C_in % KC) != 0;
+  auto slot_src = [&](int i, int64_t k0) -> const u16* {
+    const bool b = i >= SPT_A;
+    const int row = rbase + RSTEP * (b ? i - SPT_A : i);
+    int64_t gr = (b ? n0 : c0) + row;
+    const int64_t R = b ? a.N : a.C_out;
+    if (gr > R - 1) gr = R - 1;
+    int64_t k = k0 + 8 * q;
+    if (ktail && k >= a.C_in) k = 0;
+    return (b ? x : w) + gr * a.C_in + k;
+  };
+  auto fetch = [&](int chunk, u32x4 (&r)[SPT]) {
     const int64_t k0 = (int64_t)chunk * KC;
-    stage_rows<BM>(w, a.C_out, a.C_in, c0, k0, as, wave, lane);
-    stage_rows<BN>(x, a.N, a.C_in, n0, k0, bs, wave, lane);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) r[i] = *(const u32x4*)slot_src(i, k0);
+  };
+  auto stash = [&](int chunk, const u32x4 (&r)[SPT], u16* as, u16* bs) {
+    const bool zero = ktail && (int64_t)chunk * KC + 8 * q >= a.C_in;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const bool b = i >= SPT_A;
+      const int row = rbase + RSTEP * (b ? i - SPT_A : i);
+      const u32x4 v = zero ? (u32x4){0u, 0u, 0u, 0u} : r[i];
+      *(u32x4*)((b ? bs : as) + row * RS + 8 * q) = v;
+    }
   };
 
-  stage(0, As0, Bs0);
+  u32x4 ra[SPT], rb[SPT];
+  fetch(0, ra);
+  if (n_chunks > 1) fetch(1, rb);
+  stash(0, ra, As0, Bs0);
   __syncthreads();
   for (int c = 0; c < n_chunks; c += 2) {
-    if (c + 1 < n_chunks) stage(c + 1, As1, Bs1);
+    // stage 0 holds chunk c; rb holds chunk c+1
+    if (c + 2 < n_chunks) fetch(c + 2, ra);
     compute(As0, Bs0);
+    if (c + 1 < n_chunks) stash(c + 1, rb, As1, Bs1);
     __syncthreads();
     if (c + 1 >= n_chunks) break;
-    if (c + 2 < n_chunks) stage(c + 2, As0, Bs0);
+    // stage 1 holds chunk c+1; ra holds chunk c+2
+    if (c + 3 < n_chunks) fetch(c + 3, rb);
     compute(As1, Bs1);
+    if (c + 2 < n_chunks) stash(c + 2, ra, As0, Bs0);
     __syncthreads();
   }
 
@@ -214,7 +230,10 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
     __syncthreads();
     if (tid < BN) {
       const int64_t nn = n0 + tid;
-      if (nn < a.N) a.part[nn * a.n_ctiles + ctile] = fminf(red[tid], red[BN + tid]);
+      float m = red[tid];
+#pragma unroll
+      for (int w = 1; w < WGC; ++w) m = fminf(m, red[w * BN + tid]);
+      if (nn < a.N) a.part[nn * a.n_ctiles + ctile] = m;
     }
   }
 }
