@@ -144,15 +144,16 @@ __global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
                                                    uint32_t cpg) {
   const uint32_t step = gridDim.x * NT;
   if (VEC) {
+    // UNR independent 16-byte loads in flight per thread per iteration
+    constexpr int UNR = 4;
     const uint32_t nv = total >> 2;
-    for (uint32_t v = blockIdx.x * NT + threadIdx.x; v < nv; v += step) {
+    auto one = [&](uint32_t v, const f32x4& yv) {
       const uint32_t e = v << 2;
       const uint32_t row = divL.div(e);
       const uint32_t l = e - row * L;
       const uint32_t n = divC.div(row);
       const uint32_t c = row - n * C;
       const float ga = gamma ? gamma[c] : 1.f, be = beta ? beta[c] : 0.f;
-      const f32x4 yv = *(const f32x4*)(y + e);
       f32x4 z;
       if (MODE == 1) {
         const uint32_t sidx = n * G + c / cpg;
@@ -165,8 +166,17 @@ __global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = (yv[i] - mu[i]) * (rs[i] * ga) + be;
       }
-      *(f32x4*)(out + e) = z;
+      __builtin_nontemporal_store(z, (f32x4*)(out + e));
+    };
+    uint32_t v = blockIdx.x * NT + threadIdx.x;
+    for (; v + (UNR - 1) * step < nv; v += UNR * step) {
+      f32x4 yv[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) yv[u] = __builtin_nontemporal_load((const f32x4*)(y + ((v + u * step) << 2)));
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) one(v + u * step, yv[u]);
     }
+    for (; v < nv; v += step) one(v, *(const f32x4*)(y + (v << 2)));
   } else {
     for (uint32_t e = blockIdx.x * NT + threadIdx.x; e < total; e += step) {
       const uint32_t row = divL.div(e);
