@@ -76,8 +76,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < WNT; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const int arow = wc * WMT * 16 + lr, brow = wnn * WNT * 16 + lr;
-  // mid(): the LDS writes of the next chunk, issued between the two K-steps
-  auto compute = [&](const u16* as, const u16* bs, auto&& mid) {
+  auto compute = [&](const u16* as, const u16* bs) {
     bf16x8 av[WMT], bv[WNT];
 #pragma unroll
     for (int ks = 0; ks < KC / 32; ++ks) {
@@ -92,10 +91,6 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < WNT; ++j) acc[i][j] = mfma16x16x32bf16(av[i], bv[j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);  // one K-step's operands live at a time
-      if (ks == 0) {
-        mid();
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
   };
   // Staging: thread tid owns slots tid + NTHR*i of a chunk (A rows first, then
@@ -145,12 +140,14 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
   for (int c = 0; c < n_chunks; c += 2) {
     // stage 0 holds chunk c; rb holds chunk c+1
     if (c + 2 < n_chunks) fetch(c + 2, ra);
-    compute(As0, Bs0, [&] { if (c + 1 < n_chunks) stash(c + 1, rb, As1, Bs1); });
+    compute(As0, Bs0);
+    if (c + 1 < n_chunks) stash(c + 1, rb, As1, Bs1);
     __syncthreads();
     if (c + 1 >= n_chunks) break;
     // stage 1 holds chunk c+1; ra holds chunk c+2
     if (c + 3 < n_chunks) fetch(c + 3, rb);
-    compute(As1, Bs1, [&] { if (c + 2 < n_chunks) stash(c + 2, ra, As0, Bs0); });
+    compute(As1, Bs1);
+    if (c + 2 < n_chunks) stash(c + 2, ra, As0, Bs0);
     __syncthreads();
   }
 
