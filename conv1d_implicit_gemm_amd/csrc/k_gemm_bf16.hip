@@ -7,10 +7,20 @@
 // MFMA view (v_mfma_f32_16x16x32_bf16): A = w (rows c), B = x^T (columns n);
 // both operands are contiguous along the reduction, so each 64-element chunk
 // of a row is loaded with 16-byte loads (two chunks ahead, into registers) and
-// written to LDS rows of 144 bytes (72 bf16, the last 16 bytes unused) so the
-// 16-byte operand reads of 8 consecutive rows hit 8 distinct bank groups.  Workgroup: 512 threads = 4x2
-// waves, tile 256 (c) x 128 (n), wave tile 64 x 64 = 4 x 4 MFMA tiles;
-// two LDS stages (one is read while the other is written from registers).
+// written to LDS rows of 160 bytes (80 bf16, the last 32 bytes unused).  The
+// LDS has 64 four-byte banks and serves a 16-byte-per-lane read in four passes
+// of 16 lanes (lanes 0-7 with 16-23, 8-15 with 24-31, and so on); an operand
+// read puts rows r..r+7 and two adjacent 16-byte columns in one pass, and with
+// a 160-byte stride those 16 pieces fall on 16 disjoint groups of 4 banks
+// (a 144-byte stride would make two of them collide).
+// Workgroup: 512 threads, tile 256 (c) x 128 (n), two LDS stages (one is read
+// while the other is written from registers).  The eight waves form a 2 x 2
+// grid of 128 x 64 wave tiles (8 x 4 MFMA tiles) times two halves of each
+// chunk's reduction: the two waves of a SIMD own the same output tile and take
+// alternate 32-wide K-steps, so each wave reads 12 KB of operands from LDS per
+// 32 MFMAs (a 64 x 64 wave tile would need 16 KB per 16) while a second wave
+// per SIMD still hides LDS latency.  The two halves are summed through LDS once
+// at the end, in a fixed order.
 // Workgroups are mapped so that each XCD works on a compact block of tiles and
 // its L2 serves the shared rows of w and x.
 //
@@ -30,30 +40,46 @@
 namespace c1g {
 namespace {
 
-constexpr int WGC = 4, WGNN = 2;  // waves along c and along n
-constexpr int NWAVE = WGC * WGNN;
+constexpr int WGC = 2, WGNN = 2;  // spatial waves along c and along n
+constexpr int KSPLIT = 2;         // waves sharing one output tile (one per K-step)
+constexpr int NWAVE = WGC * WGNN * KSPLIT;
 constexpr int NTHR = NWAVE * 64;
 constexpr int BM = 256;        // channels per tile (A rows)
 constexpr int BN = 128;        // samples per tile (B rows)
 constexpr int KC = 64;         // reduction chunk (two MFMA K-steps)
-constexpr int RS = KC + 8;     // LDS row stride in bf16 (144 bytes)
+constexpr int RS = KC + 16;    // LDS row stride in bf16 (160 bytes)
 constexpr int QPR = KC / 8;    // 16-byte slots of data per row
 constexpr int NSLOT = (BM + BN) * QPR;           // slots per chunk (A rows, then B rows)
 constexpr int SPT = NSLOT / NTHR;                // slots per thread
 static_assert(NSLOT % NTHR == 0, "whole slots per thread");
-constexpr int WMT = BM / (16 * WGC), WNT = BN / (16 * WGNN);  // 4 x 4 MFMA tiles per wave
+static_assert(KC / 32 == KSPLIT, "one K-step per wave per chunk");
+constexpr int WMT = BM / (16 * WGC), WNT = BN / (16 * WGNN);  // 8 x 4 MFMA tiles per wave
+constexpr int STAGE = (BM + BN) * RS;            // bf16 per LDS stage
+// the K-half reduction moves half of a wave's accumulators per round
+constexpr int RED_ROUND_BYTES = WGC * WGNN * (WMT / 2) * WNT * 64 * 16;
+static_assert(RED_ROUND_BYTES <= 2 * STAGE * 2, "reduction round fits in the stages");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint16_t u16;
 
+// Source of the zero padding past C_in in the last reduction chunk: loads of
+// those columns read these 16 bytes instead of the matrix, so the staged
+// registers go to LDS without a select.
+__device__ __attribute__((aligned(16))) u16 g_zero16[8];
+
 template <int EPI>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 As0[BM * RS], As1[BM * RS];
-  __shared__ __attribute__((aligned(16))) u16 Bs0[BN * RS], Bs1[BN * RS];
+  __shared__ __attribute__((aligned(16))) u16 smem[2 * STAGE];
+  u16* const As0 = smem;
+  u16* const Bs0 = smem + BM * RS;
+  u16* const As1 = smem + STAGE;
+  u16* const Bs1 = smem + STAGE + BM * RS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wc = wave % WGC, wnn = wave / WGC;
+  const int wslot = wave & 3;                 // spatial position of the wave
+  const int kh = wave >> 2;                   // K-step of each chunk it takes
+  const int wc = wslot % WGC, wnn = wslot / WGC;
   const int lr = lane & 15, kq = lane >> 4;
 
   // XCD-aware tile order: blocks round-robin over 8 XCDs; give XCD x the
@@ -79,80 +105,130 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
   auto compute = [&](const u16* as, const u16* bs) {
     bf16x8 av[WMT], bv[WNT];
 #pragma unroll
-    for (int ks = 0; ks < KC / 32; ++ks) {
+    for (int j = 0; j < WNT; ++j)
+      bv[j] = *(const bf16x8*)(bs + (brow + 16 * j) * RS + 32 * kh + 8 * kq);
 #pragma unroll
-      for (int i = 0; i < WMT; ++i)
-        av[i] = *(const bf16x8*)(as + (arow + 16 * i) * RS + 32 * ks + 8 * kq);
+    for (int i = 0; i < WMT; ++i)
+      av[i] = *(const bf16x8*)(as + (arow + 16 * i) * RS + 32 * kh + 8 * kq);
 #pragma unroll
-      for (int j = 0; j < WNT; ++j)
-        bv[j] = *(const bf16x8*)(bs + (brow + 16 * j) * RS + 32 * ks + 8 * kq);
+    for (int i = 0; i < WMT; ++i)
 #pragma unroll
-      for (int i = 0; i < WMT; ++i)
-#pragma unroll
-        for (int j = 0; j < WNT; ++j) acc[i][j] = mfma16x16x32bf16(av[i], bv[j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);  // one K-step's operands live at a time
-    }
+      for (int j = 0; j < WNT; ++j) acc[i][j] = mfma16x16x32bf16(av[i], bv[j], acc[i][j]);
   };
   // Staging: thread tid owns slots tid + NTHR*i of a chunk (A rows first, then
   // B rows; slot = row * QPR + 16-byte column group), so slot i of every thread
-  // is an A slot for i < SPT_A and a B slot after.  Loads are unconditional
-  // (rows past the matrix read its last row, reduction columns past C_in read
-  // column 0) and the zero padding of the reduction tail is applied when the
-  // registers are written to LDS; chunk c+2 is loaded while chunk c+1 waits in
-  // registers.
+  // is an A slot for i < SPT_A and a B slot after.  Loads are unconditional:
+  // rows past the matrix read its last row (their products land in outputs
+  // that are never stored), and reduction columns past C_in read zeros.
   constexpr int SPT_A = BM * QPR / NTHR;
   static_assert(BM * QPR % NTHR == 0, "A slots fill whole thread rounds");
   const int q = tid % QPR;
   const int rbase = tid / QPR;                 // row of slot 0 (A) / slot SPT_A (B)
   constexpr int RSTEP = NTHR / QPR;            // rows between a thread's slots
-  const bool ktail = (a.C_in % KC) != 0;
-  auto slot_src = [&](int i, int64_t k0) -> const u16* {
+  const u16* slot_base[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
     const bool b = i >= SPT_A;
     const int row = rbase + RSTEP * (b ? i - SPT_A : i);
     int64_t gr = (b ? n0 : c0) + row;
     const int64_t R = b ? a.N : a.C_out;
     if (gr > R - 1) gr = R - 1;
-    int64_t k = k0 + 8 * q;
-    if (ktail && k >= a.C_in) k = 0;
-    return (b ? x : w) + gr * a.C_in + k;
-  };
+    slot_base[i] = (b ? x : w) + gr * a.C_in + 8 * q;
+  }
+  const uintptr_t zaddr = (uintptr_t)g_zero16;
   auto fetch = [&](int chunk, u32x4 (&r)[SPT]) {
     const int64_t k0 = (int64_t)chunk * KC;
+    // all-ones where this thread's 16 bytes lie past C_in (C_in % 8 == 0, so
+    // a slot is either wholly inside or wholly outside); the address is
+    // blended arithmetically so the loads stay branch-free
+    const uintptr_t pad = (uintptr_t)0 - (uintptr_t)(k0 + 8 * q >= a.C_in);
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) r[i] = *(const u32x4*)slot_src(i, k0);
+    for (int i = 0; i < SPT; ++i) {
+      const uintptr_t src = (uintptr_t)(slot_base[i] + k0);
+      r[i] = *(const __attribute__((address_space(1))) u32x4*)(src ^ ((src ^ zaddr) & pad));
+    }
   };
-  auto stash = [&](int chunk, const u32x4 (&r)[SPT], u16* as, u16* bs) {
-    const bool zero = ktail && (int64_t)chunk * KC + 8 * q >= a.C_in;
+  auto stash = [&](const u32x4 (&r)[SPT], u16* as, u16* bs) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const bool b = i >= SPT_A;
       const int row = rbase + RSTEP * (b ? i - SPT_A : i);
-      const u32x4 v = zero ? (u32x4){0u, 0u, 0u, 0u} : r[i];
-      *(u32x4*)((b ? bs : as) + row * RS + 8 * q) = v;
+      *(u32x4*)((b ? bs : as) + row * RS + 8 * q) = r[i];
     }
   };
 
+  // The prefetch and stash run unconditionally, on chunk indices clamped to
+  // the last chunk (the surplus copies land in a stage nobody reads again):
+  // with no branch around them the compiler can count the loads in flight
+  // exactly, so the write of chunk c+1 waits only for its own loads and the
+  // loads of chunk c+2 stay in flight across the barrier.
+  const int last = n_chunks - 1;
+  auto cl = [&](int c) { return c < last ? c : last; };
   u32x4 ra[SPT], rb[SPT];
   fetch(0, ra);
-  if (n_chunks > 1) fetch(1, rb);
-  stash(0, ra, As0, Bs0);
+  fetch(cl(1), rb);
+  stash(ra, As0, Bs0);
   __syncthreads();
+  // Issue order within a chunk: the 12 operand reads, then the MFMAs with one
+  // global load and one LDS write (of the other stage, free since the last
+  // barrier) after every 4 MFMAs, so the loads reach the address unit spread
+  // over the chunk instead of in one burst that stalls the issuing waves.
+  auto schedule = [] {
+    __builtin_amdgcn_sched_group_barrier(0x100, WMT + WNT, 0);  // DS reads
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);        // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);        // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);        // DS write
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, WMT * WNT - 4 * SPT, 0);
+  };
   for (int c = 0; c < n_chunks; c += 2) {
     // stage 0 holds chunk c; rb holds chunk c+1
-    if (c + 2 < n_chunks) fetch(c + 2, ra);
+    fetch(cl(c + 2), ra);
     compute(As0, Bs0);
-    if (c + 1 < n_chunks) stash(c + 1, rb, As1, Bs1);
+    stash(rb, As1, Bs1);
+    schedule();
     __syncthreads();
     if (c + 1 >= n_chunks) break;
     // stage 1 holds chunk c+1; ra holds chunk c+2
-    if (c + 3 < n_chunks) fetch(c + 3, rb);
+    fetch(cl(c + 3), rb);
     compute(As1, Bs1);
-    if (c + 2 < n_chunks) stash(c + 2, ra, As0, Bs0);
+    stash(ra, As0, Bs0);
+    schedule();
     __syncthreads();
   }
 
+  // K-half reduction: the kh = 1 wave of each spatial slot adds its partial
+  // sums into the kh = 0 wave's, half of the tile per round (lane-contiguous
+  // 16-byte slots, so the LDS traffic is conflict-free).
+  {
+    f32x4* red = (f32x4*)smem;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < WMT / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+          f32x4* slot = red + ((wslot * (WMT / 2) + i) * WNT + j) * 64 + lane;
+          if (kh == 1) *slot = acc[h * (WMT / 2) + i][j];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < WMT / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WNT; ++j) {
+          const f32x4* slot = red + ((wslot * (WMT / 2) + i) * WNT + j) * 64 + lane;
+          if (kh == 0) acc[h * (WMT / 2) + i][j] += *slot;
+        }
+      __syncthreads();
+    }
+  }
+
   // ------------------------------------------------------------------ epilogue
+  // (kh = 0 waves hold the complete tile; kh = 1 waves only join the barriers)
   if (EPI == GEMM_STORE) {
+    if (kh != 0) return;
     const bool vec = (a.C_out % 4 == 0) && ((((uintptr_t)a.y) & 15) == 0);
 #pragma unroll
     for (int i = 0; i < WMT; ++i) {
@@ -177,14 +253,14 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
   } else {  // GEMM_GN_ROWMIN: groups of 16 channels = one tile column block
-    float* red = (float*)As0;  // free after the last barrier
+    float* red = (float*)smem;  // free after the reduction's last barrier
     float rmin[WNT];
 #pragma unroll
     for (int j = 0; j < WNT; ++j) rmin[j] = __builtin_inff();
 #pragma unroll
     for (int i = 0; i < WMT; ++i) {
       const int64_t cg = c0 + wc * WMT * 16 + 16 * i;  // first channel of the group
-      const bool gvalid = cg < a.C_out;
+      const bool gvalid = cg < a.C_out && kh == 0;
       const int64_t c = cg + 4 * kq;
       f32x4 ga = {1.f, 1.f, 1.f, 1.f}, be = {0.f, 0.f, 0.f, 0.f}, bi = {0.f, 0.f, 0.f, 0.f};
       if (gvalid) {
@@ -225,7 +301,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       float m = rmin[j];
       m = fminf(m, shfl_xor(m, 16));
       m = fminf(m, shfl_xor(m, 32));
-      if (kq == 0) red[wc * BN + wnn * WNT * 16 + 16 * j + lr] = m;
+      if (kq == 0 && kh == 0) red[wc * BN + wnn * WNT * 16 + 16 * j + lr] = m;
     }
     __syncthreads();
     if (tid < BN) {
