@@ -62,10 +62,6 @@ static_assert(RED_ROUND_BYTES <= 2 * STAGE * 2, "reduction round fits in the sta
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint16_t u16;
 
-// Source of the zero padding past C_in in the last reduction chunk: loads of
-// those columns read these 16 bytes instead of the matrix, so the staged
-// registers go to LDS without a select.
-__device__ __attribute__((aligned(16))) u16 g_zero16[8];
 
 template <int EPI>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
@@ -117,15 +113,16 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
   };
   // Staging: thread tid owns slots tid + NTHR*i of a chunk (A rows first, then
   // B rows; slot = row * QPR + 16-byte column group), so slot i of every thread
-  // is an A slot for i < SPT_A and a B slot after.  Loads are unconditional:
-  // rows past the matrix read its last row (their products land in outputs
-  // that are never stored), and reduction columns past C_in read zeros.
+  // is an A slot for i < SPT_A and a B slot after.  Rows past the matrix read
+  // its last row (their products land in outputs that are never stored).  Each
+  // slot keeps a 32-bit byte offset from the matrix base (rows * C_in < 2^31
+  // elements on this route), so a load is one uniform base plus one register.
   constexpr int SPT_A = BM * QPR / NTHR;
   static_assert(BM * QPR % NTHR == 0, "A slots fill whole thread rounds");
   const int q = tid % QPR;
   const int rbase = tid / QPR;                 // row of slot 0 (A) / slot SPT_A (B)
   constexpr int RSTEP = NTHR / QPR;            // rows between a thread's slots
-  const u16* slot_base[SPT];
+  uint32_t soff[SPT];
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const bool b = i >= SPT_A;
@@ -133,20 +130,16 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
     int64_t gr = (b ? n0 : c0) + row;
     const int64_t R = b ? a.N : a.C_out;
     if (gr > R - 1) gr = R - 1;
-    slot_base[i] = (b ? x : w) + gr * a.C_in + 8 * q;
+    soff[i] = (uint32_t)((gr * a.C_in + 8 * q) * 2);
   }
-  const uintptr_t zaddr = (uintptr_t)g_zero16;
+  const char* const wbytes = (const char*)w;
+  const char* const xbytes = (const char*)x;
+  // whole chunks only (the reduction tail, if any, is handled after the loop)
   auto fetch = [&](int chunk, u32x4 (&r)[SPT]) {
-    const int64_t k0 = (int64_t)chunk * KC;
-    // all-ones where this thread's 16 bytes lie past C_in (C_in % 8 == 0, so
-    // a slot is either wholly inside or wholly outside); the address is
-    // blended arithmetically so the loads stay branch-free
-    const uintptr_t pad = (uintptr_t)0 - (uintptr_t)(k0 + 8 * q >= a.C_in);
+    const int64_t kb = (int64_t)chunk * KC * 2;
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const uintptr_t src = (uintptr_t)(slot_base[i] + k0);
-      r[i] = *(const __attribute__((address_space(1))) u32x4*)(src ^ ((src ^ zaddr) & pad));
-    }
+    for (int i = 0; i < SPT; ++i)
+      r[i] = *(const u32x4*)((i >= SPT_A ? xbytes : wbytes) + kb + soff[i]);
   };
   auto stash = [&](const u32x4 (&r)[SPT], u16* as, u16* bs) {
 #pragma unroll
@@ -157,18 +150,6 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
-  // The prefetch and stash run unconditionally, on chunk indices clamped to
-  // the last chunk (the surplus copies land in a stage nobody reads again):
-  // with no branch around them the compiler can count the loads in flight
-  // exactly, so the write of chunk c+1 waits only for its own loads and the
-  // loads of chunk c+2 stay in flight across the barrier.
-  const int last = n_chunks - 1;
-  auto cl = [&](int c) { return c < last ? c : last; };
-  u32x4 ra[SPT], rb[SPT];
-  fetch(0, ra);
-  fetch(cl(1), rb);
-  stash(ra, As0, Bs0);
-  __syncthreads();
   // Issue order within a chunk: the 12 operand reads, then the MFMAs with one
   // global load and one LDS write (of the other stage, free since the last
   // barrier) after every 4 MFMAs, so the loads reach the address unit spread
@@ -183,19 +164,58 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, WMT * WNT - 4 * SPT, 0);
   };
-  for (int c = 0; c < n_chunks; c += 2) {
-    // stage 0 holds chunk c; rb holds chunk c+1
-    fetch(cl(c + 2), ra);
-    compute(As0, Bs0);
-    stash(rb, As1, Bs1);
-    schedule();
-    __syncthreads();
-    if (c + 1 >= n_chunks) break;
-    // stage 1 holds chunk c+1; ra holds chunk c+2
-    fetch(cl(c + 3), rb);
-    compute(As1, Bs1);
+
+  // Main loop over pairs of whole chunks.  The prefetch and stash run
+  // unconditionally, on chunk indices clamped to the last whole chunk (the
+  // surplus copies land in a stage nobody reads again), and the loop body is
+  // one block with one back edge: the compiler then counts the loads in
+  // flight exactly, so each write of a staged chunk waits only for its own
+  // loads while the next chunk's loads stay in flight.
+  const int n_full = (int)(a.C_in / KC);
+  if (n_full > 0) {
+    const int last = n_full - 1;
+    auto cl = [&](int c) { return c < last ? c : last; };
+    u32x4 ra[SPT], rb[SPT];
+    fetch(0, ra);
+    fetch(cl(1), rb);
     stash(ra, As0, Bs0);
-    schedule();
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < n_full; c += 2) {
+      // stage 0 holds chunk c; rb holds chunk c+1
+      fetch(cl(c + 2), ra);
+      compute(As0, Bs0);
+      stash(rb, As1, Bs1);
+      schedule();
+      __syncthreads();
+      // stage 1 holds chunk c+1; ra holds chunk c+2
+      fetch(cl(c + 3), rb);
+      compute(As1, Bs1);
+      stash(ra, As0, Bs0);
+      schedule();
+      __syncthreads();
+    }
+    if (c < n_full) {  // odd count: the last whole chunk is in stage 0
+      compute(As0, Bs0);
+      __syncthreads();
+    }
+  }
+  // Reduction tail (C_in % 64 != 0; C_in % 8 == 0, so a 16-byte slot lies
+  // wholly inside or wholly past C_in): slots past C_in load column 0 of their
+  // row (in bounds) and are written as zeros.  Every stage is free here.
+  if (a.C_in % KC != 0) {
+    const int64_t k0 = (int64_t)n_full * KC;
+    const bool inside = k0 + 8 * q < a.C_in;
+    const int64_t kb = inside ? k0 * 2 : -(int64_t)(8 * q) * 2;
+    u32x4 rt[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const u32x4 v = *(const u32x4*)((i >= SPT_A ? xbytes : wbytes) + kb + soff[i]);
+      rt[i] = inside ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+    stash(rt, As0, Bs0);
+    __syncthreads();
+    compute(As0, Bs0);
     __syncthreads();
   }
 

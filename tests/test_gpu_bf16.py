@@ -48,6 +48,10 @@ GEMM_CASES = [
     W("gemm_ln", N=33, C_in=96, C_out=200, T=1, K=1, norm="layer_channels", **BF),
     W("gemm_only", N=50, C_in=64, C_out=300, T=1, K=1, norm=None, **BF),
     W("gemm_rowmin_only", N=20, C_in=64, C_out=48, T=1, K=1, norm=None, rowmin_bias=True, **BF),
+    # reduction shorter than one 64-wide chunk (tail only)
+    W("gemm_tail_only", N=17, C_in=40, C_out=64, T=1, K=1, G=4, rowmin_bias=True, **BF),
+    # odd number of whole chunks plus a tail
+    W("gemm_odd_chunks_tail", N=90, C_in=200, C_out=128, T=1, K=1, G=8, **BF),
 ]
 
 
