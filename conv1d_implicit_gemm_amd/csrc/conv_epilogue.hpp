@@ -15,6 +15,9 @@
 // deviations), xor-shuffle sums across lanes, then a fixed-order pairwise
 // merge across waves through LDS; every partial has one fixed slot (no
 // atomics), so the later merge is deterministic.
+//
+// Waves with active == false (extra waves of a workgroup whose results were
+// already folded into the active ones) store nothing but reach every barrier.
 #pragma once
 
 #include "common.hpp"
@@ -26,7 +29,7 @@ template <int WM, int WN, int WGM, int WGN>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
                                               f32x4 (&acc)[WM][WN], int64_t n, int64_t t0,
                                               int c0, int ttile, int ctile, int wm, int wn,
-                                              Stats* red) {
+                                              Stats* red, bool active = true) {
   constexpr int TM = WGM * WM * 16, TN = WGN * WN * 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -40,7 +43,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       acc[i][jn] += b;
-      if (c < a.C_out) {
+      if (active && c < a.C_out) {
         const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq;
         float* dst = a.y + (n * a.C_out + c) * T_out;
         if (vec_ok && t + 3 < T_out) {
@@ -80,7 +83,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
           if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
         }
       m2 = xor_sum<48>(m2);
-      if (kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
+      if (active && kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
     }
     __syncthreads();
     for (int cl = tid; cl < TN; cl += blockDim.x) {
@@ -115,7 +118,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
         }
         m2 = xor_sum<15>(m2);
         const int tl = wm * WM * 16 + i * 16 + 4 * kq + r;
-        if (lr == 0) red[wn * TM + tl] = Stats{cnt, mean, m2};
+        if (active && lr == 0) red[wn * TM + tl] = Stats{cnt, mean, m2};
       }
     __syncthreads();
     for (int tl = tid; tl < TM; tl += blockDim.x) {

@@ -6,20 +6,33 @@
 // one v_mfma_f32_16x16x32_bf16 K-step per tap.  The MFMA wants 8 consecutive
 // reduction values per lane, i.e. 8 consecutive input channels at one position,
 // while x is stored position-contiguous, so the input halo window of a tile is
-// transposed while it is staged: each thread loads an 8 (channels) x 8
-// (positions) block with 16-byte loads along t, transposes it in registers and
-// writes 8 rows of the LDS window Xt[t][ci] (80-byte rows: the 16-byte MFMA
-// operand reads of 8 consecutive rows hit 8 distinct bank groups).  Every tap
-// then reads the same window at a shifted row offset.  The weights are repacked
-// once per call into the exact LDS image of each (c-tile, chunk) and streamed
-// with direct global->LDS loads.
+// transposed while it is staged: a lane loads an 8 (channels) x 8 (positions)
+// block with 16-byte loads along t, transposes it in registers and writes 8
+// rows of the LDS window Xt[t][ci].  Every tap then reads the same window at a
+// shifted row offset.  The weights are repacked once per call into the exact
+// LDS image of each (c-tile, chunk) and streamed with direct global->LDS loads.
 //
-// Workgroup: WGM x 2 waves; tile TM = WGM*WM*16 (t) x 128 (c); wave tile
-// WM x 4 MFMA tiles (256 x 128 with 8 waves of 64 x 64 for unit stride and
-// short halos, 64 x 128 with 4 waves otherwise).  Two LDS stages: the next chunk's weights
-// stream in and its window is fetched into registers while the current chunk
-// is consumed.  Epilogue: shared with the fp32 kernel (store y, GroupNorm or
-// channel-LayerNorm partial statistics).
+// LDS rows are 64 bytes (32 bf16) with no padding; the 16-byte column of a row
+// is XOR-ed with 2 when bit 2 of the row index is set.  The LDS has 64
+// four-byte banks and serves a 16-byte-per-lane read in four passes of 16
+// lanes (lanes 0-7 with 16-23, and so on), so an operand read of rows r..r+7
+// and two adjacent columns touches 16 distinct groups of 4 banks for any r
+// (unit stride); without the XOR, rows r and r+4 would collide.
+//
+// Workgroup: 512 threads; tile TM (256 or 64) positions x 128 channels.  The
+// eight waves form a 2 x 2 grid of wave tiles (WM x 4 MFMA tiles, 128 x 64 for
+// TM = 256) times two halves of the taps: the two waves of a SIMD own the same
+// output tile and take taps [0, ceil(K/2)) and [ceil(K/2), K) of every chunk,
+// so each wave reads 12 KB of operands per 32 MFMAs while a second wave per
+// SIMD still hides LDS latency; the halves are summed through LDS at the end.
+// Two LDS stages: the next chunk's weights stream in and its window is loaded
+// into registers while the current chunk is consumed; the waves of the second
+// tap half (which has the fewer taps for odd K) do all of that staging.
+// Window blocks go to lanes channel-group fastest, so the 8 lanes of one
+// 16-byte LDS write pass (32 banks, 8 consecutive lanes per pass for writes)
+// cover two rows and all four columns: a 2-way conflict, the least possible
+// for rows that share their index modulo 8.  Epilogue: shared with
+// the fp32 kernel (store y, GroupNorm or channel-LayerNorm partial statistics).
 #include "common.hpp"
 #include "conv_epilogue.hpp"
 #include "launch.hpp"
@@ -29,13 +42,23 @@ namespace {
 
 constexpr int TN = ConvBf16Cfg::TN;  // 128 output channels per tile
 constexpr int CK = ConvBf16Cfg::CK;  // 32 input channels per chunk
-constexpr int RS = CK + 8;           // LDS row stride in bf16 (80 bytes)
+constexpr int RW = CK;               // LDS row: 32 bf16 (64 bytes)
 constexpr int KMAX = 5;              // taps (LDS budget of the weight stages)
 constexpr int WN = 4;                // MFMA tiles per wave along c
-constexpr int WGN = 2;               // waves along c (TN = WGN * WN * 16)
-constexpr int XCAP = 288;            // window positions per stage
+constexpr int WGN = 2;               // spatial waves along c (TN = WGN * WN * 16)
+constexpr int WGM = 2;               // spatial waves along t
+constexpr int KSPLIT = 2;            // tap halves
+constexpr int NWAVE = WGM * WGN * KSPLIT;
+constexpr int NTHR = NWAVE * 64;
+constexpr int XCAP = 288;            // window rows per stage
 constexpr int XTG = XCAP / 8;        // 8-position groups per window
 constexpr int XBLK = XTG * (CK / 8); // 8x8 blocks per window
+constexpr int NSTAGE_WAVES = NWAVE / KSPLIT;   // waves that stage (the second tap half)
+constexpr int XLANES = XBLK / NSTAGE_WAVES;      // lanes per staging wave, one block each
+static_assert(XBLK % NSTAGE_WAVES == 0 && XLANES <= 64, "window blocks spread over the waves");
+constexpr int XS_ELEMS = XCAP * RW;
+constexpr int WS_ELEMS = KMAX * TN * RW;
+static_assert(TN == 128, "weight rows keep bit 2 of c across taps");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint16_t u16;
@@ -43,6 +66,9 @@ typedef uint16_t u16;
 __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
+
+// 16-byte column swizzle of LDS row `row`
+__host__ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 2; }
 
 // 8x8 transpose of 16-bit values: in[r] holds row r (4 dwords, element 2k in
 // the low half of dword k); out[e] receives column e.
@@ -58,19 +84,20 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-template <int WGM, int WM, int KT, bool FAST>
-__global__ __launch_bounds__(WGM * WGN * 64) void conv_bf16_kernel(ConvArgs a, int epi) {
-  constexpr int NTHR = WGM * WGN * 64, NWAVE = WGM * WGN;
+template <int WM, int KT, bool FAST>
+__global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   constexpr int TM = WGM * WM * 16;
-  constexpr int XB = (XBLK + NTHR - 1) / NTHR;
-  __shared__ __attribute__((aligned(16))) u16 Xs0[XCAP * RS];
-  __shared__ __attribute__((aligned(16))) u16 Xs1[XCAP * RS];
-  __shared__ __attribute__((aligned(16))) u16 Ws0[KMAX * TN * RS];
-  __shared__ __attribute__((aligned(16))) u16 Ws1[KMAX * TN * RS];
+  constexpr int KH = (KT + 1) / 2;   // taps of the first half
+  __shared__ __attribute__((aligned(16))) u16 Xs0[XS_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 Xs1[XS_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 Ws0[WS_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 Ws1[WS_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WGM, wn = wave / WGM;
+  const int wslot = wave & 3;          // spatial position of the wave
+  const int kh = wave >> 2;            // tap half it takes
+  const int wm = wslot % WGM, wn = wslot / WGM;
   const int lr = lane & 15, kq = lane >> 4;
   // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
   // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
@@ -95,54 +122,58 @@ __global__ __launch_bounds__(WGM * WGN * 64) void conv_bf16_kernel(ConvArgs a, i
   const int64_t tal = (tbase >= 0) ? (tbase & ~(int64_t)7) : -(((-tbase) + 7) & ~(int64_t)7);
   const int shift = (int)(tbase - tal);
 
-  // ---- input window: thread -> 8x8 block (position group fastest)
-  u32x4 xr[XB][8];
-  auto fetch_x = [&](int chunk) {
-    const int64_t ci0 = (int64_t)chunk * CK;
+  // ---- input window: lanes 0..XLANES-1 of the staging waves own one 8x8
+  // block (8 positions of 8 channels), channel group fastest
+  const bool stager = kh == 1;
+  const bool xown = stager && lane < XLANES;
+  const int blk = (stager ? wave - NSTAGE_WAVES : 0) * XLANES + (xown ? lane : 0);
+  const int tg = blk >> 2, cg = blk & 3;
+  const int64_t tx = tal + 8 * tg;
+  u32x4 xr[8];
+  auto fetch_x = [&](int chunk) __attribute__((always_inline)) {
+    const int64_t ci0 = (int64_t)chunk * CK + 8 * cg;
 #pragma unroll
-    for (int b = 0; b < XB; ++b) {
-      const int blk = tid + NTHR * b;
-      const int tg = blk % XTG, cg = blk / XTG;
-      const int64_t t = tal + 8 * tg;
+    for (int r = 0; r < 8; ++r) {
+      const int64_t ci = ci0 + r;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (xown && ci < a.C_in) {
+        const u16* src = xn + ci * T;
+        if (FAST) {
+          // T % 8 == 0 and the group is 8-aligned: wholly inside or outside
+          if (tx >= 0 && tx < T) v = *(const u32x4*)(src + tx);
+        } else {
+          u16 e8[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int64_t ci = ci0 + 8 * cg + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (blk < XBLK && ci < a.C_in) {
-          const u16* src = xn + ci * T;
-          if (FAST) {
-            if (t >= 0 && t + 7 < T) v = *(const u32x4*)(src + t);
-          } else {
-            u16 e8[8];
+          for (int e = 0; e < 8; ++e) e8[e] = (tx + e >= 0 && tx + e < T) ? src[tx + e] : (u16)0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) e8[e] = (t + e >= 0 && t + e < T) ? src[t + e] : (u16)0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = (uint32_t)e8[2 * k] | ((uint32_t)e8[2 * k + 1] << 16);
-          }
+          for (int k = 0; k < 4; ++k) v[k] = (uint32_t)e8[2 * k] | ((uint32_t)e8[2 * k + 1] << 16);
         }
-        xr[b][r] = v;
+      }
+      xr[r] = v;
+    }
+  };
+  auto stash_x = [&](u16* xs) __attribute__((always_inline)) {
+    if (xown) {
+      u32x4 tr[8];
+      transpose8x8(xr, tr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = 8 * tg + e;
+        *(u32x4*)(xs + row * RW + 8 * (cg ^ swz(row))) = tr[e];
       }
     }
   };
-  auto stash_x = [&](u16* xs) {
+  // ---- weights: direct copy of the packed LDS image of (ctile, chunk),
+  // KT * 8 pieces of 1 KB spread over the staging waves
+  auto dma_w = [&](int chunk, u16* ws) __attribute__((always_inline)) {
+    if (!stager) return;
+    const char* src = (const char*)(wp + ((int64_t)ctile * a.n_chunks + chunk) * (int64_t)(KT * TN * RW));
+    const int sw = wave - NSTAGE_WAVES;
 #pragma unroll
-    for (int b = 0; b < XB; ++b) {
-      const int blk = tid + NTHR * b;
-      if (blk < XBLK) {
-        const int tg = blk % XTG, cg = blk / XTG;
-        u32x4 tr[8];
-        transpose8x8(xr[b], tr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x4*)(xs + (8 * tg + e) * RS + 8 * cg) = tr[e];
-      }
+    for (int p = 0; p < (KT * 8 + NSTAGE_WAVES - 1) / NSTAGE_WAVES; ++p) {
+      const int piece = sw + NSTAGE_WAVES * p;
+      if (piece < KT * 8) dma16(src + piece * 1024 + lane * 16, (char*)ws + piece * 1024);
     }
-  };
-  // ---- weights: direct copy of the packed LDS image of (ctile, chunk)
-  const int wbytes = KT * TN * RS * 2;
-  auto dma_w = [&](int chunk, u16* ws) {
-    const char* src = (const char*)(wp + ((int64_t)ctile * a.n_chunks + chunk) * (int64_t)(KT * TN * RS));
-    for (int p = wave; p * 1024 < wbytes; p += NWAVE)
-      dma16(src + p * 1024 + lane * 16, (char*)ws + p * 1024);
   };
 
   f32x4 acc[WM][WN];
@@ -151,94 +182,136 @@ __global__ __launch_bounds__(WGM * WGN * 64) void conv_bf16_kernel(ConvArgs a, i
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int arow = (wm * WM * 16 + lr) * s + shift;   // window row of subtile 0, tap 0
-  const int brow = wn * WN * 16 + lr;
-  auto compute = [&](const u16* xs, const u16* ws) {
+  const int arow0 = (wm * WM * 16 + lr) * s + shift;  // window row of subtile 0, tap 0
+  const int bcol = 8 * (kq ^ swz(lr));                // weight rows: bit 2 of c = bit 2 of lr
+  auto tap = [&](const u16* xs, const u16* ws, int j) __attribute__((always_inline)) {
+    const int r0 = arow0 + j * d;                       // rows r0 + 16*s*i keep bit 2
+    const u16* xa = xs + r0 * RW + 8 * (kq ^ swz(r0));
+    const u16* wb = ws + (j * TN + wn * WN * 16 + lr) * RW + bcol;
+    bf16x8 av[WM], bv[WN];
 #pragma unroll
-    for (int j = 0; j < KT; ++j) {
-      bf16x8 av[WM], bv[WN];
+    for (int jn = 0; jn < WN; ++jn) bv[jn] = *(const bf16x8*)(wb + jn * 16 * RW);
 #pragma unroll
-      for (int i = 0; i < WM; ++i)
-        av[i] = *(const bf16x8*)(xs + (arow + i * 16 * s + j * d) * RS + 8 * kq);
+    for (int i = 0; i < WM; ++i) av[i] = *(const bf16x8*)(xa + i * 16 * s * RW);
 #pragma unroll
-      for (int jn = 0; jn < WN; ++jn)
-        bv[jn] = *(const bf16x8*)(ws + (j * TN + brow + jn * 16) * RS + 8 * kq);
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
-      // one tap's operands live at a time (keeps the 256-position tile in registers)
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
+    __builtin_amdgcn_sched_barrier(0);  // one tap's operands live at a time
+  };
+  // this wave's taps of every chunk: [0, KH) or [KH, KT) (uniform per wave);
+  // one tap body in a runtime loop keeps a single copy of it in registers
+  const int jbeg = kh == 0 ? 0 : KH, jend = kh == 0 ? KH : KT;
+  auto compute = [&](const u16* xs, const u16* ws) __attribute__((always_inline)) {
+#pragma nounroll
+    for (int j = jbeg; j < jend; ++j) tap(xs, ws, j);
   };
 
-  const int n_chunks = a.n_chunks;
+  // Pairs of chunks per iteration, loads clamped to the last chunk and issued
+  // unconditionally (surplus copies land in a stage nobody reads again), so
+  // the loop body is one block; every load of a chunk completes before the
+  // barrier that ends the half in which it was issued.
+  const int n_chunks = a.n_chunks, last = n_chunks - 1;
+  auto cl = [&](int c) { return c < last ? c : last; };
   dma_w(0, Ws0);
   fetch_x(0);
   stash_x(Xs0);
   __syncthreads();
-  for (int c = 0; c < n_chunks; c += 2) {
-    if (c + 1 < n_chunks) {
-      dma_w(c + 1, Ws1);
-      fetch_x(c + 1);
-    }
+  int c = 0;
+  for (; c + 1 < n_chunks; c += 2) {
+    // stage 0 holds chunk c
+    dma_w(c + 1, Ws1);
+    fetch_x(c + 1);
     compute(Xs0, Ws0);
-    if (c + 1 < n_chunks) stash_x(Xs1);
+    stash_x(Xs1);
     __syncthreads();
-    if (c + 1 >= n_chunks) break;
-    if (c + 2 < n_chunks) {
-      dma_w(c + 2, Ws0);
-      fetch_x(c + 2);
-    }
+    // stage 1 holds chunk c+1
+    dma_w(cl(c + 2), Ws0);
+    fetch_x(cl(c + 2));
     compute(Xs1, Ws1);
-    if (c + 2 < n_chunks) stash_x(Xs0);
+    stash_x(Xs0);
+    __syncthreads();
+  }
+  if (c < n_chunks) {  // odd count: the last chunk is in stage 0
+    compute(Xs0, Ws0);
     __syncthreads();
   }
 
-  conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
+  // Tap-half reduction: the kh = 1 wave of each spatial slot adds its partial
+  // sums into the kh = 0 wave's, RF tiles per round split over the two weight
+  // stages (lane-contiguous 16-byte slots: conflict-free).
+  {
+    constexpr int NF = WM * WN, RF = NF >= 16 ? 16 : NF, HF = RF / 2;
+    static_assert(4 * HF * 64 * 16 <= WS_ELEMS * 2, "reduction round fits a weight stage");
+    f32x4* red0 = (f32x4*)Ws0;
+    f32x4* red1 = (f32x4*)Ws1;
+#pragma unroll
+    for (int rnd = 0; rnd < NF / RF; ++rnd) {
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        const int idx = rnd * RF + f, i = idx / WN, jn = idx % WN;
+        f32x4* slot = (f < HF ? red0 : red1) + (wslot * HF + f % HF) * 64 + lane;
+        if (kh == 1) *slot = acc[i][jn];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < RF; ++f) {
+        const int idx = rnd * RF + f, i = idx / WN, jn = idx % WN;
+        const f32x4* slot = (f < HF ? red0 : red1) + (wslot * HF + f % HF) * 64 + lane;
+        if (kh == 0) acc[i][jn] += *slot;
+      }
+      __syncthreads();
+    }
+  }
+
+  conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0,
+                                  kh == 0);
 }
 
-// Weight image: one block of KT*TN*RS bf16 per (ctile, chunk), laid out
-// [j][c][r] with r < 32 the input channel inside the chunk and r >= 32 padding:
-//   wp[(((ctile*n_chunks + chunk)*K + j)*TN + c)*RS + r] = w[ctile*TN + c][chunk*32 + r][j]
+// Weight image: one block of K*TN*RW bf16 per (ctile, chunk), laid out
+// [j][c][32] with the input channels of the chunk in four 16-byte columns,
+// column q of row c stored at column q ^ swz(c):
+//   wp[(((ctile*n_chunks + chunk)*K + j)*TN + c)*RW + 8*(q ^ swz(c)) + e]
+//     = w[ctile*TN + c][chunk*32 + 8*q + e][j]      (0 outside the tensor)
 __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict__ wp,
                                       int64_t C_in, int64_t C_out, int K, int n_chunks,
                                       int64_t total) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int r = (int)(idx % RS);
-  int64_t rest = idx / RS;
+  const int e = (int)(idx % 8);
+  const int pq = (int)((idx / 8) % (RW / 8));
+  int64_t rest = idx / RW;
   const int c = (int)(rest % TN);
   rest /= TN;
   const int j = (int)(rest % K);
   rest /= K;
   const int chunk = (int)(rest % n_chunks);
   const int64_t ctile = rest / n_chunks;
+  const int q = pq ^ swz(c);
   const int64_t co = ctile * TN + c;
-  const int64_t ci = (int64_t)chunk * CK + r;
-  wp[idx] = (r < CK && co < C_out && ci < C_in) ? w[(co * C_in + ci) * K + j] : (u16)0;
+  const int64_t ci = (int64_t)chunk * CK + 8 * q + e;
+  wp[idx] = (co < C_out && ci < C_in) ? w[(co * C_in + ci) * K + j] : (u16)0;
 }
 
-template <int WGM, int WM, int KT>
+template <int WM, int KT>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
-  constexpr int nthr = WGM * WGN * 64;
   const bool fast = (a.T % 8 == 0) && ((((uintptr_t)a.x) & 15) == 0);
   if (fast)
-    hipLaunchKernelGGL((conv_bf16_kernel<WGM, WM, KT, true>), grid, dim3(nthr), 0, st, a, epi);
+    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, true>), grid, dim3(NTHR), 0, st, a, epi);
   else
-    hipLaunchKernelGGL((conv_bf16_kernel<WGM, WM, KT, false>), grid, dim3(nthr), 0, st, a, epi);
+    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, false>), grid, dim3(NTHR), 0, st, a, epi);
   return hipGetLastError();
 }
 
-template <int WGM, int WM>
+template <int WM>
 hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st) {
   switch (a.K) {
-    case 1: return launch_wk<WGM, WM, 1>(a, epi, st);
-    case 2: return launch_wk<WGM, WM, 2>(a, epi, st);
-    case 3: return launch_wk<WGM, WM, 3>(a, epi, st);
-    case 4: return launch_wk<WGM, WM, 4>(a, epi, st);
-    case 5: return launch_wk<WGM, WM, 5>(a, epi, st);
+    case 1: return launch_wk<WM, 1>(a, epi, st);
+    case 2: return launch_wk<WM, 2>(a, epi, st);
+    case 3: return launch_wk<WM, 3>(a, epi, st);
+    case 4: return launch_wk<WM, 4>(a, epi, st);
+    case 5: return launch_wk<WM, 5>(a, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -259,7 +332,7 @@ int conv_bf16_tile_m(int stride, int K, int dilation) {
 
 size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K) {
   const int64_t n_chunks = (C_in + CK - 1) / CK, n_ctiles = (C_out + TN - 1) / TN;
-  return (size_t)(n_ctiles * n_chunks * K * TN * RS) * sizeof(u16);
+  return (size_t)(n_ctiles * n_chunks * K * TN * RW) * sizeof(u16);
 }
 
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
@@ -274,8 +347,8 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
 
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
-  if (tm == 256) return launch_w<4, 4>(a, epi, s);  // 8 waves, 64 x 64 each
-  if (tm == 64) return launch_w<2, 2>(a, epi, s);   // 4 waves, 32 x 64 each
+  if (tm == 256) return launch_w<8>(a, epi, s);  // wave tiles 128 x 64
+  if (tm == 64) return launch_w<2>(a, epi, s);   // wave tiles 32 x 64
   return hipErrorInvalidValue;
 }
 
