@@ -36,10 +36,18 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t T_out = a.T_out;
   const bool vec_ok = ((T_out & 3) == 0) && ((((uintptr_t)a.y) & 15) == 0);
+  // all bias loads before the first store: a load issued between stores would
+  // make its wait also wait for every store before it
+  float bias[WN];
 #pragma unroll
   for (int jn = 0; jn < WN; ++jn) {
     const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-    const float b = (a.bias != nullptr && c < a.C_out) ? a.bias[c] : 0.f;
+    bias[jn] = (a.bias != nullptr && c < a.C_out) ? a.bias[c] : 0.f;
+  }
+#pragma unroll
+  for (int jn = 0; jn < WN; ++jn) {
+    const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+    const float b = bias[jn];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       acc[i][jn] += b;
