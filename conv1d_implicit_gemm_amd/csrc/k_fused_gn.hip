@@ -5,9 +5,10 @@
 // GroupNorm slab of its groups ("Kimi-K2.6 l2_p35": statistics over C_out/G
 // channels x T_out per (n, group); its single-pass design keeps a group's
 // whole output on chip so the normalised result is written once).  Here the
-// slab stays in MFMA accumulator registers: 8 waves, each owning MQ 16-row
-// subtiles of positions x 16 channels (v_mfma_f32_16x16x4_f32), so y never
-// goes to HBM and is never re-read.
+// slab stays in MFMA accumulator registers: 16 waves (4 per SIMD, which
+// measured faster than 2), each owning MQ 16-row subtiles of positions x 16
+// channels (v_mfma_f32_16x16x4_f32), so y never goes to HBM and is never
+// re-read.
 //
 // K loop: per chunk of 16 input channels (all taps) the input halo window of
 // the whole sequence and the chunk's weights are staged in LDS, and every tap
@@ -36,7 +37,7 @@
 namespace c1g {
 namespace {
 
-constexpr int NW = 8;              // waves per workgroup
+constexpr int NW = 16;             // waves per workgroup (4 per SIMD)
 constexpr int NTHR = NW * 64;
 constexpr int CB = 16;             // channels per workgroup
 constexpr int CK = 16;             // input channels per K-chunk
@@ -413,7 +414,7 @@ hipError_t launch_mq(const FusedArgs& a, hipStream_t s) {
 
 int fused_gn_max_tout(int stride, int K, int dilation) {
   if (stride != 1 || K < 1 || K > KMAX || (int64_t)(K - 1) * dilation > HALO_MAX) return 0;
-  return NW * 8 * 16;
+  return NW * 4 * 16;
 }
 
 bool fused_gn_supported(int64_t C_in, int64_t C_out, int32_t G, int64_t T_out, int stride,
@@ -430,7 +431,6 @@ hipError_t fused_gn_launch(const FusedArgs& a, hipStream_t s) {
   if (t <= NW * 16 * 1) return launch_mq<1>(a, s);
   if (t <= NW * 16 * 2) return launch_mq<2>(a, s);
   if (t <= NW * 16 * 4) return launch_mq<4>(a, s);
-  if (t <= NW * 16 * 8) return launch_mq<8>(a, s);
   return hipErrorInvalidValue;
 }
 
