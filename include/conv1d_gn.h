@@ -72,7 +72,8 @@ enum c1g_status {
   C1G_ERR_INVALID_ARG = 1,     /* bad size, NULL required pointer, C_out % G != 0 ...  */
   C1G_ERR_UNSUPPORTED = 2,     /* valid but not built (e.g. window wider than a tile)  */
   C1G_ERR_WORKSPACE = 3,       /* workspace NULL or smaller than the size query       */
-  C1G_ERR_MISALIGNED = 4,      /* a tensor pointer not aligned to its element size    */
+  C1G_ERR_MISALIGNED = 4,      /* a tensor pointer not aligned to its element size,   */
+                               /* or x / w not 16-byte aligned on the gemm_rows route */
   C1G_ERR_HIP = 5              /* the HIP runtime reported an error at launch         */
 };
 
@@ -164,8 +165,18 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
                       const float* bias2, float* out, float* mean_out, float* rstd_out,
                       void* ws, size_t ws_bytes, void* stream);
 
-/* Name of the kernel route conv1d_gn_forward takes for these arguments
- * ("fused_lds", "split", "gemm_rows", ...), or "invalid".  Pure host function. */
+/* Name of the kernel route conv1d_gn_forward takes for these arguments, or
+ * "invalid".  Pure host function.  Routes:
+ *   "conv_only"          norm == C1G_NORM_NONE and no epilogue: the convolution
+ *   "fused_single_pass"  fp32, stride 1, GroupNorm with C_out/G dividing 16,
+ *                        T_out <= 1024, (K-1)*dilation <= 28: one launch, the
+ *                        output slab of a group never leaves the chip
+ *   "gemm_rows"          bf16, K = 1, T = 1, no padding, C_in % 8 == 0 (a Linear
+ *                        layer): an MFMA GEMM whose epilogue applies GroupNorm
+ *                        and the row-min when C_out/G == 16; needs x and w
+ *                        16-byte aligned (C1G_ERR_MISALIGNED otherwise)
+ *   "split"              everything else: conv with a partial-statistics
+ *                        epilogue, a fixed-order merge, then the apply pass */
 const char* c1g_route(const c1g_conv_desc* d, const c1g_norm_desc* norm);
 
 /* Static string describing a status code. */
