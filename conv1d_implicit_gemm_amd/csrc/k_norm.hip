@@ -144,8 +144,11 @@ __global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
                                                    uint32_t cpg) {
   const uint32_t step = gridDim.x * NT;
   if (VEC) {
-    // UNR independent 16-byte loads in flight per thread per iteration
-    constexpr int UNR = 4;
+    // Block-contiguous batches: per iteration a workgroup owns UNR * NT
+    // consecutive 16-byte vectors (UNR loads in flight per thread, all before
+    // any store); measured on this GPU, contiguous per-workgroup spans stream
+    // ~10% faster than a grid-strided interleave.
+    constexpr int UNR = 2;
     const uint32_t nv = total >> 2;
     auto one = [&](uint32_t v, const f32x4& yv) {
       const uint32_t e = v << 2;
@@ -168,15 +171,36 @@ __global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
       }
       __builtin_nontemporal_store(z, (f32x4*)(out + e));
     };
-    uint32_t v = blockIdx.x * NT + threadIdx.x;
-    for (; v + (UNR - 1) * step < nv; v += UNR * step) {
+    if (MODE == 2) {
+      // three loads per vector (y, mean, rstd): a grid-strided loop with four
+      // vectors in flight per thread measured faster here
+      constexpr int U2 = 4;
+      uint32_t v = blockIdx.x * NT + threadIdx.x;
+      for (; v + (U2 - 1) * step < nv; v += U2 * step) {
+        f32x4 yv[U2];
+#pragma unroll
+        for (int u = 0; u < U2; ++u)
+          yv[u] = __builtin_nontemporal_load((const f32x4*)(y + ((size_t)(v + u * step) << 2)));
+#pragma unroll
+        for (int u = 0; u < U2; ++u) one(v + u * step, yv[u]);
+      }
+      for (; v < nv; v += step) one(v, *(const f32x4*)(y + ((size_t)v << 2)));
+      return;
+    }
+    const uint32_t batch = UNR * NT;
+    for (uint32_t base = blockIdx.x * batch; base < nv; base += gridDim.x * batch) {
       f32x4 yv[UNR];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) yv[u] = __builtin_nontemporal_load((const f32x4*)(y + ((v + u * step) << 2)));
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t v = base + u * NT + threadIdx.x;
+        if (v < nv) yv[u] = __builtin_nontemporal_load((const f32x4*)(y + ((size_t)v << 2)));
+      }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) one(v + u * step, yv[u]);
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t v = base + u * NT + threadIdx.x;
+        if (v < nv) one(v, yv[u]);
+      }
     }
-    for (; v < nv; v += step) one(v, *(const f32x4*)(y + (v << 2)));
   } else {
     for (uint32_t e = blockIdx.x * NT + threadIdx.x; e < total; e += step) {
       const uint32_t row = divL.div(e);
@@ -288,7 +312,10 @@ hipError_t apply_launch(const float* y, const float* mean, const float* rstd,
   const bool vec = (L % 4 == 0) && ((((uintptr_t)y) & 15) == 0) && ((((uintptr_t)out) & 15) == 0) &&
                    (MODE == 1 || ((((uintptr_t)mean) & 15) == 0 && (((uintptr_t)rstd) & 15) == 0));
   if (vec) {
-    hipLaunchKernelGGL((apply_kernel<MODE, true>), dim3(grid_for(total / 4)), dim3(NT), 0, s, y,
+    const uint64_t batches = (total / 4 + 2 * NT - 1) / (2 * NT);
+    const unsigned grid = MODE == 2 ? grid_for(total / 4)
+                                    : (unsigned)(batches < 8192 ? (batches < 1 ? 1 : batches) : 8192);
+    hipLaunchKernelGGL((apply_kernel<MODE, true>), dim3(grid), dim3(NT), 0, s, y,
                        mean, rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
                        (uint32_t)L, (uint32_t)G, cpg);
   } else {
