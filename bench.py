@@ -66,15 +66,28 @@ def stored_traffic(workload, route):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, inp, flops, budget_s=10.0):
     """The oracle, as it stands, on the full workload, repeated until about
-    budget_s seconds of wall time have passed (at least once)."""
+    budget_s seconds of wall time have passed (at least once), on all host
+    threads; then once on one thread over the first sample only (the work per
+    sample is the same for every sample), scaled to the same unit."""
     import oracle
     from conv1d_implicit_gemm_amd.workloads import to_f64_numpy as f
     args = dict(stride=wl.stride, dilation=wl.dilation, pad_left=wl.pad_left,
                 pad_right=wl.pad_right, norm=wl.norm, G=wl.G, eps=wl.eps,
                 gamma=f(inp["gamma"]), beta=f(inp["beta"]), bias2=f(inp["bias2"]))
     x, w, b = f(inp["x"]), f(inp["w"]), f(inp["bias"])
+    threads = oracle.num_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.forward(x, w, b, **args)
@@ -82,9 +95,38 @@ def cpu_baseline(wl, inp, flops, budget_s=10.0):
         el = time.perf_counter() - t0
         if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
             break
-    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.forward(x[:1].copy(), w, b, **args)
+        el1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": "full workload (all %d samples), %d run(s) in %.1f s, fp64" % (wl.N, reps, el)}
+            "sample": "full workload (all %d samples), %d run(s) in %.1f s, fp64" % (wl.N, reps, el),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": flops / wl.N / el1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": "sample 0 of %d, one run in %.2f s, fp64" % (wl.N, el1)}}
+
+
+def cold_timing(op, stream, reps=10, flush_bytes=1 << 30):
+    """Per-step time with the L2 and Infinity Cache flushed before each step
+    (a 1 GiB buffer is overwritten first); median over reps, in ms."""
+    import torch
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    times = []
+    for _ in range(reps):
+        buf.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        op()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del buf
+    times.sort()
+    return times[len(times) // 2], times[0]
 
 
 def copy_mode(args):
@@ -188,6 +230,11 @@ def main():
                      "traffic": traffic, "kernel_ms": round(kern_ms, 5),
                      "algorithmic_flops_per_launch": flops},
     }
+    cold_ms, cold_min = cold_timing(op, stream)
+    res["cold"] = {"ms_per_step_median": round(cold_ms, 5), "ms_per_step_min": round(cold_min, 5),
+                   "value": round(flops / (cold_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                   "note": "L2 and Infinity Cache flushed (1 GiB written) before each of 10 steps; "
+                           "value/ms_per_step above are warm back-to-back steps"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp, flops)
     print(json.dumps(res), flush=True)

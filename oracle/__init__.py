@@ -74,6 +74,8 @@ class Oracle:
     def __init__(self, lib_path: str):
         lib = ctypes.CDLL(lib_path)
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_out_len.restype = _I64
         lib.oracle_out_len.argtypes = [_I64] * 6
         lib.oracle_conv1d.restype = None
@@ -92,6 +94,10 @@ class Oracle:
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Set the OpenMP thread count of the following calls (n >= 1)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def out_len(self, T, K, stride=1, dilation=1, pad_left=0, pad_right=0) -> int:
         """T_out = floor((T + pad_left + pad_right - dilation*(K-1) - 1)/stride) + 1, or -1.
@@ -196,6 +202,10 @@ def default() -> Oracle:
 
 def num_threads():
     return default().num_threads()
+
+
+def set_num_threads(n):
+    return default().set_num_threads(n)
 
 
 def out_len(*a, **k):

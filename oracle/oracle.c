@@ -45,6 +45,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the following parallel loops use (n >= 1); no effect without OpenMP. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Output length of a 1-D convolution with left/right zero padding
  * ("Kimi-K2.6 l2_p35", T_out derivation; symmetric padding p gives
  * pad_left = pad_right = p).  Returns -1 if there is no valid output. */
