@@ -19,19 +19,19 @@
 // and two adjacent columns touches 16 distinct groups of 4 banks for any r
 // (unit stride); without the XOR, rows r and r+4 would collide.
 //
-// Workgroup: 512 threads; tile TM (256 or 64) positions x 128 channels.  The
-// eight waves form a 2 x 2 grid of wave tiles (WM x 4 MFMA tiles, 128 x 64 for
-// TM = 256) times two halves of the taps: the two waves of a SIMD own the same
-// output tile and take taps [0, ceil(K/2)) and [ceil(K/2), K) of every chunk,
-// so each wave reads 12 KB of operands per 32 MFMAs while a second wave per
-// SIMD still hides LDS latency; the halves are summed through LDS at the end.
+// Workgroup: 512 threads; tile TM (512 or 128) positions x 128 channels.  The
+// eight waves form a 4 x 2 grid of wave tiles of WM x 4 MFMA tiles (128 x 64
+// for TM = 512), each running every tap, so a wave reads 12 KB of operands per
+// 32 MFMAs and two waves per SIMD hide LDS latency.  The tile is tall because
+// the L2 -> LDS path moves ~40 bytes per clock per CU (measured, the same for
+// direct loads and for register staging): a 512-position tile stages 75 KB per
+// chunk for 21 MFLOP, where a 256-position one needs 58 KB for half the work.
 // Two LDS stages: the next chunk's weights stream in and its window is loaded
-// into registers while the current chunk is consumed; the waves of the second
-// tap half (which has the fewer taps for odd K) do all of that staging.
-// Window blocks go to lanes channel-group fastest, so the 8 lanes of one
-// 16-byte LDS write pass (32 banks, 8 consecutive lanes per pass for writes)
-// cover two rows and all four columns: a 2-way conflict, the least possible
-// for rows that share their index modulo 8.  Epilogue: shared with
+// into registers while the current chunk is consumed; every wave takes a
+// share of the staging.  Window blocks go to lanes channel-group fastest, so
+// the 8 lanes of one 16-byte LDS write pass (32 banks, 8 consecutive lanes per
+// pass for writes) cover two rows and all four columns: a 2-way conflict, the
+// least possible for rows that share their index modulo 8.  Epilogue: shared with
 // the fp32 kernel (store y, GroupNorm or channel-LayerNorm partial statistics).
 #include "common.hpp"
 #include "conv_epilogue.hpp"
@@ -45,17 +45,15 @@ constexpr int CK = ConvBf16Cfg::CK;  // 32 input channels per chunk
 constexpr int RW = CK;               // LDS row: 32 bf16 (64 bytes)
 constexpr int KMAX = 5;              // taps (LDS budget of the weight stages)
 constexpr int WN = 4;                // MFMA tiles per wave along c
-constexpr int WGN = 2;               // spatial waves along c (TN = WGN * WN * 16)
-constexpr int WGM = 2;               // spatial waves along t
-constexpr int KSPLIT = 2;            // tap halves
-constexpr int NWAVE = WGM * WGN * KSPLIT;
+constexpr int WGN = 2;               // waves along c (TN = WGN * WN * 16)
+constexpr int WGM = 4;               // waves along t
+constexpr int NWAVE = WGM * WGN;
 constexpr int NTHR = NWAVE * 64;
-constexpr int XCAP = 288;            // window rows per stage
+constexpr int XCAP = 544;            // window rows per stage
 constexpr int XTG = XCAP / 8;        // 8-position groups per window
 constexpr int XBLK = XTG * (CK / 8); // 8x8 blocks per window
-constexpr int NSTAGE_WAVES = NWAVE / KSPLIT;   // waves that stage (the second tap half)
-constexpr int XLANES = XBLK / NSTAGE_WAVES;      // lanes per staging wave, one block each
-static_assert(XBLK % NSTAGE_WAVES == 0 && XLANES <= 64, "window blocks spread over the waves");
+constexpr int XLANES = XBLK / NWAVE; // lanes per wave that stage one block each
+static_assert(XBLK % NWAVE == 0 && XLANES <= 64, "window blocks spread over the waves");
 constexpr int XS_ELEMS = XCAP * RW;
 constexpr int WS_ELEMS = KMAX * TN * RW;
 static_assert(TN == 128, "weight rows keep bit 2 of c across taps");
@@ -87,7 +85,6 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 template <int WM, int KT, bool FAST>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   constexpr int TM = WGM * WM * 16;
-  constexpr int KH = (KT + 1) / 2;   // taps of the first half
   __shared__ __attribute__((aligned(16))) u16 Xs0[XS_ELEMS];
   __shared__ __attribute__((aligned(16))) u16 Xs1[XS_ELEMS];
   __shared__ __attribute__((aligned(16))) u16 Ws0[WS_ELEMS];
@@ -95,9 +92,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wslot = wave & 3;          // spatial position of the wave
-  const int kh = wave >> 2;            // tap half it takes
-  const int wm = wslot % WGM, wn = wslot / WGM;
+  const int wm = wave % WGM, wn = wave / WGM;
   const int lr = lane & 15, kq = lane >> 4;
   // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
   // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
@@ -122,11 +117,10 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   const int64_t tal = (tbase >= 0) ? (tbase & ~(int64_t)7) : -(((-tbase) + 7) & ~(int64_t)7);
   const int shift = (int)(tbase - tal);
 
-  // ---- input window: lanes 0..XLANES-1 of the staging waves own one 8x8
-  // block (8 positions of 8 channels), channel group fastest
-  const bool stager = kh == 1;
-  const bool xown = stager && lane < XLANES;
-  const int blk = (stager ? wave - NSTAGE_WAVES : 0) * XLANES + (xown ? lane : 0);
+  // ---- input window: lanes 0..XLANES-1 of every wave own one 8x8 block
+  // (8 positions of 8 channels), channel group fastest
+  const bool xown = lane < XLANES;
+  const int blk = wave * XLANES + (xown ? lane : 0);
   const int tg = blk >> 2, cg = blk & 3;
   const int64_t tx = tal + 8 * tg;
   u32x4 xr[8];
@@ -164,14 +158,12 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
     }
   };
   // ---- weights: direct copy of the packed LDS image of (ctile, chunk),
-  // KT * 8 pieces of 1 KB spread over the staging waves
+  // KT * 8 pieces of 1 KB spread over the waves
   auto dma_w = [&](int chunk, u16* ws) __attribute__((always_inline)) {
-    if (!stager) return;
     const char* src = (const char*)(wp + ((int64_t)ctile * a.n_chunks + chunk) * (int64_t)(KT * TN * RW));
-    const int sw = wave - NSTAGE_WAVES;
 #pragma unroll
-    for (int p = 0; p < (KT * 8 + NSTAGE_WAVES - 1) / NSTAGE_WAVES; ++p) {
-      const int piece = sw + NSTAGE_WAVES * p;
+    for (int p = 0; p < (KT * 8 + NWAVE - 1) / NWAVE; ++p) {
+      const int piece = wave + NWAVE * p;
       if (piece < KT * 8) dma16(src + piece * 1024 + lane * 16, (char*)ws + piece * 1024);
     }
   };
@@ -199,12 +191,11 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
       for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
     __builtin_amdgcn_sched_barrier(0);  // one tap's operands live at a time
   };
-  // this wave's taps of every chunk: [0, KH) or [KH, KT) (uniform per wave);
-  // one tap body in a runtime loop keeps a single copy of it in registers
-  const int jbeg = kh == 0 ? 0 : KH, jend = kh == 0 ? KH : KT;
+  // every tap of the chunk; one tap body in a runtime loop keeps a single copy
+  // of it in registers
   auto compute = [&](const u16* xs, const u16* ws) __attribute__((always_inline)) {
 #pragma nounroll
-    for (int j = jbeg; j < jend; ++j) tap(xs, ws, j);
+    for (int j = 0; j < KT; ++j) tap(xs, ws, j);
   };
 
   // Pairs of chunks per iteration, loads clamped to the last chunk and issued
@@ -237,35 +228,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
     __syncthreads();
   }
 
-  // Tap-half reduction: the kh = 1 wave of each spatial slot adds its partial
-  // sums into the kh = 0 wave's, RF tiles per round split over the two weight
-  // stages (lane-contiguous 16-byte slots: conflict-free).
-  {
-    constexpr int NF = WM * WN, RF = NF >= 16 ? 16 : NF, HF = RF / 2;
-    static_assert(4 * HF * 64 * 16 <= WS_ELEMS * 2, "reduction round fits a weight stage");
-    f32x4* red0 = (f32x4*)Ws0;
-    f32x4* red1 = (f32x4*)Ws1;
-#pragma unroll
-    for (int rnd = 0; rnd < NF / RF; ++rnd) {
-#pragma unroll
-      for (int f = 0; f < RF; ++f) {
-        const int idx = rnd * RF + f, i = idx / WN, jn = idx % WN;
-        f32x4* slot = (f < HF ? red0 : red1) + (wslot * HF + f % HF) * 64 + lane;
-        if (kh == 1) *slot = acc[i][jn];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int f = 0; f < RF; ++f) {
-        const int idx = rnd * RF + f, i = idx / WN, jn = idx % WN;
-        const f32x4* slot = (f < HF ? red0 : red1) + (wslot * HF + f % HF) * 64 + lane;
-        if (kh == 0) acc[i][jn] += *slot;
-      }
-      __syncthreads();
-    }
-  }
-
-  conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0,
-                                  kh == 0);
+  conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
 }
 
 // Weight image: one block of K*TN*RW bf16 per (ctile, chunk), laid out
@@ -325,8 +288,8 @@ int64_t window(int tm, int stride, int K, int dilation) {
 
 int conv_bf16_tile_m(int stride, int K, int dilation) {
   if (K < 1 || K > KMAX) return 0;
-  if (window(256, stride, K, dilation) <= XCAP) return 256;
-  if (window(64, stride, K, dilation) <= XCAP) return 64;
+  if (window(512, stride, K, dilation) <= XCAP) return 512;
+  if (window(128, stride, K, dilation) <= XCAP) return 128;
   return 0;
 }
 
@@ -347,8 +310,8 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
 
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
-  if (tm == 256) return launch_w<8>(a, epi, s);  // wave tiles 128 x 64
-  if (tm == 64) return launch_w<2>(a, epi, s);   // wave tiles 32 x 64
+  if (tm == 512) return launch_w<8>(a, epi, s);  // wave tiles 128 x 64
+  if (tm == 128) return launch_w<2>(a, epi, s);  // wave tiles 32 x 64
   return hipErrorInvalidValue;
 }
 

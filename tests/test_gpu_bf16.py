@@ -14,15 +14,19 @@ pytestmark = pytest.mark.gpu
 
 W = Workload
 BF = dict(dtype="bf16")
-# conv tiles: 128 (or 64 for wide windows) positions x 128 channels, 32 input
+# conv tiles: 512 (or 128 for wide windows) positions x 128 channels, 32 input
 # channels per chunk; shapes span several tiles and end in ragged tails
 CONV_CASES = [
+    W("bf16_conv_gn_k5d2_3tiles", N=2, C_in=72, C_out=160, T=1300, K=5, dilation=2,
+      pad_left=2, pad_right=2, G=8, **BF),
+    W("bf16_conv_ln_3tiles", N=1, C_in=40, C_out=272, T=1300, K=5, dilation=2, pad_left=2,
+      pad_right=2, norm="layer_channels", **BF),
     W("bf16_conv_gn_k5d2", N=2, C_in=72, C_out=160, T=300, K=5, dilation=2, pad_left=2,
       pad_right=2, G=8, **BF),
     W("bf16_conv_gn_causal", N=2, C_in=64, C_out=96, T=264, K=4, pad_left=3, G=12, **BF),
     W("bf16_conv_gn_odd_T", N=2, C_in=40, C_out=64, T=203, K=3, pad_left=1, pad_right=1,
       G=4, **BF),
-    W("bf16_conv_gn_stride3_tile64", N=2, C_in=33, C_out=48, T=401, K=3, stride=3,
+    W("bf16_conv_gn_stride3_small_tile", N=2, C_in=33, C_out=48, T=401, K=3, stride=3,
       pad_left=1, pad_right=1, G=6, **BF),
     W("bf16_conv_only", N=3, C_in=48, C_out=130, T=256, K=2, norm=None, **BF),
     W("bf16_conv_ln", N=2, C_in=64, C_out=200, T=140, K=5, dilation=2, pad_left=2,
