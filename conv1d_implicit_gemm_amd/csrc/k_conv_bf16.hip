@@ -43,19 +43,23 @@ namespace {
 constexpr int TN = ConvBf16Cfg::TN;  // 128 output channels per tile
 constexpr int CK = ConvBf16Cfg::CK;  // 32 input channels per chunk
 constexpr int RW = CK;               // LDS row: 32 bf16 (64 bytes)
-constexpr int KMAX = 5;              // taps (LDS budget of the weight stages)
+constexpr int KMAX = 8;              // taps: up to 5 on 512-position tiles, 8 on 128
 constexpr int WN = 4;                // MFMA tiles per wave along c
 constexpr int WGN = 2;               // waves along c (TN = WGN * WN * 16)
 constexpr int WGM = 4;               // waves along t
 constexpr int NWAVE = WGM * WGN;
 constexpr int NTHR = NWAVE * 64;
-constexpr int XCAP = 544;            // window rows per stage
-constexpr int XTG = XCAP / 8;        // 8-position groups per window
-constexpr int XBLK = XTG * (CK / 8); // 8x8 blocks per window
-constexpr int XLANES = XBLK / NWAVE; // lanes per wave that stage one block each
-static_assert(XBLK % NWAVE == 0 && XLANES <= 64, "window blocks spread over the waves");
-constexpr int XS_ELEMS = XCAP * RW;
-constexpr int WS_ELEMS = KMAX * TN * RW;
+// LDS per workgroup: two stages of (window XC rows + weight image of the taps)
+// of 64-byte rows.  XC = 544 rows with up to 5 taps (150 KB), or 224 rows with
+// 6 to 8 taps on 128-position tiles (156 KB); gfx950 allows 160 KB.
+constexpr int XCAP_WIDE = 544, XCAP_TAPS = 224;
+template <int XC>
+struct XGeom {
+  static constexpr int XTG = XC / 8;        // 8-position groups per window
+  static constexpr int XBLK = XTG * (CK / 8); // 8x8 blocks per window
+  static constexpr int XLANES = XBLK / NWAVE; // lanes per wave that stage one block each
+  static_assert(XBLK % NWAVE == 0 && XLANES <= 64, "window blocks spread over the waves");
+};
 static_assert(TN == 128, "weight rows keep bit 2 of c across taps");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -82,13 +86,16 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-template <int WM, int KT, bool FAST>
+template <int WM, int KT, bool FAST, int XC>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
+  constexpr int XLANES = XGeom<XC>::XLANES;
+  // the weight stage also holds the epilogue's cross-wave merge (<= 12 KB)
+  constexpr int WSK = KT < 2 ? 2 : KT;
   constexpr int TM = WGM * WM * 16;
-  __shared__ __attribute__((aligned(16))) u16 Xs0[XS_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 Xs1[XS_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 Ws0[WS_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 Ws1[WS_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 Xs0[XC * RW];
+  __shared__ __attribute__((aligned(16))) u16 Xs1[XC * RW];
+  __shared__ __attribute__((aligned(16))) u16 Ws0[WSK * TN * RW];
+  __shared__ __attribute__((aligned(16))) u16 Ws1[WSK * TN * RW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -256,25 +263,32 @@ __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict
   wp[idx] = (co < C_out && ci < C_in) ? w[(co * C_in + ci) * K + j] : (u16)0;
 }
 
-template <int WM, int KT>
+template <int WM, int KT, int XC>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
   const bool fast = (a.T % 8 == 0) && ((((uintptr_t)a.x) & 15) == 0);
   if (fast)
-    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, true>), grid, dim3(NTHR), 0, st, a, epi);
+    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, true, XC>), grid, dim3(NTHR), 0, st, a, epi);
   else
-    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, false>), grid, dim3(NTHR), 0, st, a, epi);
+    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, false, XC>), grid, dim3(NTHR), 0, st, a, epi);
   return hipGetLastError();
 }
 
 template <int WM>
 hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st) {
   switch (a.K) {
-    case 1: return launch_wk<WM, 1>(a, epi, st);
-    case 2: return launch_wk<WM, 2>(a, epi, st);
-    case 3: return launch_wk<WM, 3>(a, epi, st);
-    case 4: return launch_wk<WM, 4>(a, epi, st);
-    case 5: return launch_wk<WM, 5>(a, epi, st);
+    case 1: return launch_wk<WM, 1, XCAP_WIDE>(a, epi, st);
+    case 2: return launch_wk<WM, 2, XCAP_WIDE>(a, epi, st);
+    case 3: return launch_wk<WM, 3, XCAP_WIDE>(a, epi, st);
+    case 4: return launch_wk<WM, 4, XCAP_WIDE>(a, epi, st);
+    case 5: return launch_wk<WM, 5, XCAP_WIDE>(a, epi, st);
+    default: break;
+  }
+  if (WM != 2) return hipErrorInvalidValue;
+  switch (a.K) {
+    case 6: return launch_wk<2, 6, XCAP_TAPS>(a, epi, st);
+    case 7: return launch_wk<2, 7, XCAP_TAPS>(a, epi, st);
+    case 8: return launch_wk<2, 8, XCAP_TAPS>(a, epi, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -288,8 +302,8 @@ int64_t window(int tm, int stride, int K, int dilation) {
 
 int conv_bf16_tile_m(int stride, int K, int dilation) {
   if (K < 1 || K > KMAX) return 0;
-  if (window(512, stride, K, dilation) <= XCAP) return 512;
-  if (window(128, stride, K, dilation) <= XCAP) return 128;
+  if (K <= 5 && window(512, stride, K, dilation) <= XCAP_WIDE) return 512;
+  if (window(128, stride, K, dilation) <= (K <= 5 ? XCAP_WIDE : XCAP_TAPS)) return 128;
   return 0;
 }
 

@@ -117,8 +117,15 @@ def test_unsupported_sizes():
     assert c1g.check(_desc(K=9, pad_left=4, pad_right=4)) == 2
     # input window wider than any tile variant
     assert c1g.check(_desc(stride=8, T=4096)) == 2
-    # bf16 convolution: taps beyond the weight stages
-    assert c1g.check(_desc(K=6, pad_left=2, pad_right=3, dtype=c1g.C1G_BF16)) == 2
+    # bf16 convolution: up to 8 taps (6..8 on 128-position tiles), not 9
+    assert c1g.check(_desc(K=8, pad_left=3, pad_right=4, dtype=c1g.C1G_BF16)) == 0
+    assert c1g.check(_desc(K=9, pad_left=4, pad_right=4, dtype=c1g.C1G_BF16)) == 2
+    # bf16, 8 taps: the window of a 128-position tile, 127 + 7*dilation + 1 rows
+    # plus up to 7 of alignment, must fit 224 rows
+    assert c1g.check(_desc(K=8, dilation=12, pad_left=0, pad_right=0, T=4096,
+                           dtype=c1g.C1G_BF16)) == 0
+    assert c1g.check(_desc(K=8, dilation=13, pad_left=0, pad_right=0, T=4096,
+                           dtype=c1g.C1G_BF16)) == 2
 
 
 def test_binding_rejects_cpu_tensors():

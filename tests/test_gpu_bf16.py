@@ -33,6 +33,13 @@ CONV_CASES = [
       pad_right=2, norm="layer_channels", **BF),
     W("bf16_conv_gn_rowmin", N=2, C_in=32, C_out=64, T=96, K=3, pad_left=1, pad_right=1,
       G=4, rowmin_bias=True, **BF),
+    # 6..8 taps: 128-position tiles with an 8-tap weight stage
+    W("bf16_conv_gn_k8", N=2, C_in=48, C_out=144, T=300, K=8, pad_left=3, pad_right=4,
+      G=9, **BF),
+    W("bf16_conv_gn_k7d2_causal", N=2, C_in=40, C_out=64, T=270, K=7, dilation=2,
+      pad_left=12, G=8, **BF),
+    W("bf16_conv_ln_k6", N=1, C_in=64, C_out=130, T=200, K=6, pad_left=2, pad_right=3,
+      norm="layer_channels", **BF),
 ]
 
 
