@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
+                    help="element type of the output (bf16: rounded to nearest even)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -165,14 +167,16 @@ def main():
     from conv1d_implicit_gemm_amd.workloads import HEADLINE, WORKLOADS, make_inputs
 
     name = args.workload or HEADLINE
-    wl = WORKLOADS[name]
+    wl = WORKLOADS[name].replace(out_dtype=args.out_dtype)
     dev = "cuda:0"
     inp = make_inputs(wl, 0)
     d = {k: (v.to(dev).contiguous() if v is not None else None) for k, v in inp.items()}
     op = c1g.PreparedConv1dGN(d["x"], d["w"], d["bias"], stride=wl.stride,
                               dilation=wl.dilation, pad_left=wl.pad_left,
                               pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
-                              gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"])
+                              gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"],
+                              out_dtype=torch.bfloat16 if wl.out_dtype == "bf16"
+                              else torch.float32)
     T_out = op.T_out
     flops = 2 * wl.N * T_out * wl.C_out * wl.C_in * wl.K
     stream = torch.cuda.current_stream(dev)
@@ -212,8 +216,9 @@ def main():
     bound, peak, unit = PEAKS[wl.dtype]
     achieved = flops / (kern_ms * 1e-3) / 1e12
     algo_bytes = (wl.N * wl.C_in * wl.T * wl.elem_bytes + wl.C_out * wl.C_in * wl.K *
-                  wl.elem_bytes + wl.N * wl.C_out * T_out * 4)
-    traffic = stored_traffic(name, op.route)
+                  wl.elem_bytes + wl.N * wl.C_out * T_out * (2 if wl.out_dtype == "bf16" else 4))
+    # stored counters were taken with an fp32 output
+    traffic = stored_traffic(name, op.route) if wl.out_dtype == "f32" else None
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -222,7 +227,8 @@ def main():
         "config": {"workload": name, "N": wl.N, "C_in": wl.C_in, "C_out": wl.C_out, "T": wl.T,
                    "T_out": T_out, "K": wl.K, "stride": wl.stride, "dilation": wl.dilation,
                    "pad_left": wl.pad_left, "pad_right": wl.pad_right, "norm": wl.norm,
-                   "G": wl.G, "rowmin_bias": wl.rowmin_bias, "route": op.route,
+                   "G": wl.G, "rowmin_bias": wl.rowmin_bias, "out_dtype": wl.out_dtype,
+                   "route": op.route,
                    "parallelism": "single GPU"},
         "gbps_algorithmic": round(algo_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,

@@ -12,7 +12,9 @@ Entry points (same names as the C ABI):
     conv1d_gn_forward(x, w, bias=None, *, ..., norm, groups, eps, gamma, beta,
                       rowmin_bias=None, return_stats=False)
     gn_stats(y, groups, eps)        -> (mean[N,G], rstd[N,G])
-    gn_apply(y, mean, rstd, gamma, beta, groups, out=None)
+    gn_apply(y, mean, rstd, gamma, beta, groups, out=None)   (fp32, or bf16 -> gn_apply_bf16)
+Outputs are fp32 unless ``out_dtype=torch.bfloat16`` (or a bf16 ``out``) is
+given: values are computed in fp32 and rounded to nearest even on the store.
 Host-only helpers: out_len, route, workspace sizes, check.
 """
 from __future__ import annotations
@@ -35,7 +37,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 # every symbol include/conv1d_gn.h declares
 EXPORTS = ["c1g_out_len", "c1g_check", "c1g_conv1d_workspace_size", "conv1d_forward",
-           "c1g_gn_stats_workspace_size", "gn_stats", "gn_apply",
+           "c1g_gn_stats_workspace_size", "gn_stats", "gn_apply", "gn_apply_bf16",
            "c1g_conv1d_gn_workspace_size", "conv1d_gn_forward", "c1g_route",
            "c1g_status_string"]
 
@@ -44,7 +46,8 @@ class ConvDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("C_in", ctypes.c_int64), ("C_out", ctypes.c_int64),
                 ("T", ctypes.c_int64), ("K", ctypes.c_int32), ("stride", ctypes.c_int32),
                 ("dilation", ctypes.c_int32), ("pad_left", ctypes.c_int32),
-                ("pad_right", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("pad_right", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
 
 
 class NormDesc(ctypes.Structure):
@@ -89,6 +92,8 @@ def load_library():
         lib.gn_stats.argtypes = [i64, i64, i64, i32, ctypes.c_float, P, P, P, P, sz, P]
         lib.gn_apply.restype = ctypes.c_int
         lib.gn_apply.argtypes = [i64, i64, i64, i32, P, P, P, P, P, P, P]
+        lib.gn_apply_bf16.restype = ctypes.c_int
+        lib.gn_apply_bf16.argtypes = [i64, i64, i64, i32, P, P, P, P, P, P, P]
         lib.c1g_conv1d_gn_workspace_size.restype = sz
         lib.c1g_conv1d_gn_workspace_size.argtypes = [PD, PN]
         lib.conv1d_gn_forward.restype = ctypes.c_int
@@ -114,9 +119,20 @@ def _pads(K, dilation, padding, pad_left, pad_right, causal):
 
 
 def make_desc(N, C_in, C_out, T, K, *, stride=1, dilation=1, padding=0, pad_left=None,
-              pad_right=None, causal=False, dtype=C1G_F32) -> ConvDesc:
+              pad_right=None, causal=False, dtype=C1G_F32, out_dtype=C1G_F32) -> ConvDesc:
     pl, pr = _pads(K, dilation, padding, pad_left, pad_right, causal)
-    return ConvDesc(N, C_in, C_out, T, K, stride, dilation, pl, pr, dtype)
+    return ConvDesc(N, C_in, C_out, T, K, stride, dilation, pl, pr, dtype, out_dtype)
+
+
+_DT_CODE = {torch.float32: C1G_F32, torch.bfloat16: C1G_BF16}
+
+
+def _out_dtype(out, out_dtype):
+    """The output's torch dtype: that of ``out`` when given, else out_dtype."""
+    dt = out.dtype if out is not None else out_dtype
+    if dt not in _DT_CODE:
+        raise TypeError("outputs must be float32 or bfloat16, got %s" % (dt,))
+    return dt
 
 
 def make_norm(norm=None, groups=0, eps=1e-5, rowmin=False) -> NormDesc:
@@ -177,7 +193,8 @@ def _raise(status, where):
         raise C1GError(status, where)
 
 
-def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation):
+def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
+                out_dtype=torch.float32):
     if x.dim() != 3 or w.dim() != 3:
         raise ValueError("x must be [N, C_in, T] and w [C_out, C_in, K]")
     if not x.is_cuda:
@@ -195,23 +212,26 @@ def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation):
     if C_in_w != C_in:
         raise ValueError("x and w disagree on C_in")
     desc = make_desc(N, C_in, C_out, T, K, stride=stride, dilation=dilation, padding=padding,
-                     pad_left=pad_left, pad_right=pad_right, causal=causal, dtype=dt)
+                     pad_left=pad_left, pad_right=pad_right, causal=causal, dtype=dt,
+                     out_dtype=_DT_CODE[out_dtype])
     return desc
 
 
 # ----------------------------------------------------------------- entry points
 def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
-                   causal=False, dilation=1, out=None, workspace=None):
-    """y = conv1d(x, w) + bias, fp32 output [N, C_out, T_out]."""
+                   causal=False, dilation=1, out=None, out_dtype=torch.float32,
+                   workspace=None):
+    """y = conv1d(x, w) + bias, output [N, C_out, T_out] (fp32 or bf16)."""
     lib = load_library()
-    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation)
+    odt = _out_dtype(out, out_dtype)
+    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt)
     _need(bias, "bias", torch.float32, x.device)
     T_out = lib.c1g_out_len(ctypes.byref(desc))
     if T_out < 1:
         _raise(1, "conv1d_forward")
     if out is None:
-        out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=torch.float32)
-    _need(out, "out", torch.float32, x.device)
+        out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=odt)
+    _need(out, "out", odt, x.device)
     ws_bytes = lib.c1g_conv1d_workspace_size(ctypes.byref(desc))
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
@@ -225,14 +245,15 @@ def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_r
 def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                       causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                       beta=None, rowmin_bias=None, return_stats=False, out=None,
-                      workspace=None):
+                      out_dtype=torch.float32, workspace=None):
     """conv -> GroupNorm / LayerNorm over channels / none -> optional row-min + bias.
 
-    Returns out [N, C_out, T_out] (fp32), or (out, mean, rstd) with
-    return_stats=True (mean/rstd [N, G] for GroupNorm, [N, T_out] for the
-    channel LayerNorm)."""
+    Returns out [N, C_out, T_out] (fp32, or bf16 with out_dtype=torch.bfloat16
+    or a bf16 ``out``), or (out, mean, rstd) with return_stats=True (fp32
+    mean/rstd [N, G] for GroupNorm, [N, T_out] for the channel LayerNorm)."""
     lib = load_library()
-    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation)
+    odt = _out_dtype(out, out_dtype)
+    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt)
     nd = make_norm(norm, groups, eps, rowmin_bias is not None)
     for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
         _need(t, nm, torch.float32, x.device)
@@ -240,8 +261,8 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
     if T_out < 1:
         _raise(1, "conv1d_gn_forward")
     if out is None:
-        out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=torch.float32)
-    _need(out, "out", torch.float32, x.device)
+        out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=odt)
+    _need(out, "out", odt, x.device)
     mean = rstd = None
     if return_stats and nd.norm != NORM_NONE:
         shp = (desc.N, groups) if nd.norm == NORM_GROUP else (desc.N, T_out)
@@ -278,21 +299,26 @@ def gn_stats(y, groups, eps=1e-5):
 
 def gn_apply(y, mean, rstd, gamma=None, beta=None, groups=None, out=None):
     """out = (y - mean) * rstd * gamma + beta with per-(n, group) statistics.
+    y and out are both fp32 (gn_apply) or both bf16 (gn_apply_bf16).
     ``out=y`` normalises in place."""
     lib = load_library()
     if y.dim() != 3 or not y.is_cuda:
         raise ValueError("y must be a [N, C, L] device tensor")
-    _need(y, "y", torch.float32, y.device)
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    _need(y, "y", y.dtype, y.device)
     N, C, L = y.shape
     G = groups if groups is not None else mean.shape[1]
     for t, nm in ((mean, "mean"), (rstd, "rstd"), (gamma, "gamma"), (beta, "beta")):
         _need(t, nm, torch.float32, y.device)
     if out is None:
         out = torch.empty_like(y)
-    _need(out, "out", torch.float32, y.device)
-    st = lib.gn_apply(N, C, L, G, _ptr(y), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(beta),
-                      _ptr(out), _stream(y.device))
-    _raise(st, "gn_apply")
+    _need(out, "out", y.dtype, y.device)
+    fn, name = ((lib.gn_apply, "gn_apply") if y.dtype == torch.float32
+                else (lib.gn_apply_bf16, "gn_apply_bf16"))
+    st = fn(N, C, L, G, _ptr(y), _ptr(mean), _ptr(rstd), _ptr(gamma), _ptr(beta), _ptr(out),
+            _stream(y.device))
+    _raise(st, name)
     return out
 
 
@@ -306,9 +332,12 @@ class PreparedConv1dGN:
 
     def __init__(self, x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                  causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
-                 beta=None, rowmin_bias=None, out=None, mean=None, rstd=None):
+                 beta=None, rowmin_bias=None, out=None, out_dtype=torch.float32, mean=None,
+                 rstd=None):
         lib = load_library()
-        self.desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation)
+        odt = _out_dtype(out, out_dtype)
+        self.desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
+                                odt)
         self.norm = make_norm(norm, groups, eps, rowmin_bias is not None)
         for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"),
                       (rowmin_bias, "rowmin_bias"), (mean, "mean"), (rstd, "rstd")):
@@ -318,8 +347,8 @@ class PreparedConv1dGN:
             _raise(1, "PreparedConv1dGN")
         if out is None:
             out = torch.empty((self.desc.N, self.desc.C_out, self.T_out), device=x.device,
-                              dtype=torch.float32)
-        _need(out, "out", torch.float32, x.device)
+                              dtype=odt)
+        _need(out, "out", odt, x.device)
         ws_bytes = lib.c1g_conv1d_gn_workspace_size(ctypes.byref(self.desc),
                                                    ctypes.byref(self.norm))
         self.workspace = (torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)

@@ -20,11 +20,12 @@ struct Plan {
   int status = C1G_OK;
   int route = R_INVALID;
   int64_t T_out = -1;
-  bool bf16 = false;
+  bool bf16 = false;      // x and w are bf16
+  bool out_bf16 = false;  // y / out are bf16
   int norm = C1G_NORM_NONE, epi = C1G_EPI_NONE;
   int n_chunks = 0, n_ttiles = 0, n_ctiles = 0, tm = 0, tn = 0;
   bool gemm_fused = false;  // R_GEMM: GroupNorm + row-min inside the GEMM epilogue
-  size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, total = 0;
+  size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, off_y = 0, total = 0;
 };
 
 constexpr size_t kAlign = 256;
@@ -48,6 +49,11 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   if (p.T_out < 1) { p.status = C1G_ERR_INVALID_ARG; return p; }
   if (d->dtype != C1G_F32 && d->dtype != C1G_BF16) { p.status = C1G_ERR_UNSUPPORTED; return p; }
   p.bf16 = d->dtype == C1G_BF16;
+  if (d->out_dtype != C1G_F32 && d->out_dtype != C1G_BF16) {
+    p.status = C1G_ERR_UNSUPPORTED;
+    return p;
+  }
+  p.out_bf16 = d->out_dtype == C1G_BF16;
   if (nd) {
     p.norm = nd->norm;
     p.epi = nd->epilogue;
@@ -97,6 +103,10 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
     off = align_up(off + stat * sizeof(float));
     p.off_rstd = off;
     off = align_up(off + stat * sizeof(float));
+    // a bf16 out of the unfused epilogues: fp32 y in the workspace, so the
+    // statistics and the affine read unrounded values
+    p.off_y = off;
+    if (p.out_bf16 && !p.gemm_fused) off = align_up(off + (size_t)d->N * d->C_out * sizeof(float));
     p.total = conv_only ? 0 : off;
     return p;
   }
@@ -152,7 +162,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? C1G_OK : C1G_ERR_HIP; }
 
 // Convolution into y (with the requested statistics epilogue); packs weights first.
 int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w,
-             const float* bias, float* y, char* ws, int epi, hipStream_t s) {
+             const float* bias, void* y, char* ws, int epi, hipStream_t s) {
   ConvArgs a;
   a.x = x;
   a.wp = ws + p.off_pack;
@@ -171,6 +181,7 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
   a.n_chunks = p.n_chunks;
   a.n_ttiles = p.n_ttiles;
   a.n_ctiles = p.n_ctiles;
+  a.y_bf16 = p.out_bf16;
   hipError_t e;
   if (p.bf16) {
     e = conv_bf16_pack((const uint16_t*)w, (uint16_t*)(ws + p.off_pack), d->C_in, d->C_out,
@@ -186,16 +197,22 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
 // K = 1, T = 1 bf16 GEMM route: y[n][c] (== out viewed as [N, C_out, 1]).
 int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
              const void* w, const float* bias, const float* gamma, const float* beta,
-             const float* bias2, float* out, float* mean_out, float* rstd_out, char* ws,
+             const float* bias2, void* out, float* mean_out, float* rstd_out, char* ws,
              hipStream_t s) {
   if (!aligned(x, 16) || !aligned(w, 16)) return C1G_ERR_MISALIGNED;
+  const bool conv_only = !nd || (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE);
+  const int out_dt = p.out_bf16 ? C1G_BF16 : C1G_F32;
   GemmArgs g;
   g.x = x;
   g.w = w;
   g.bias = bias;
   g.gamma = gamma;
   g.beta = beta;
-  g.y = out;
+  // y: out itself, except ahead of an unfused epilogue into a bf16 out (then
+  // fp32 y in the workspace)
+  float* y = (!conv_only && p.out_bf16) ? (float*)(ws + p.off_y) : (float*)out;
+  g.y = conv_only ? out : (void*)y;
+  g.y_bf16 = conv_only && p.out_bf16;
   g.part = (float*)(ws + p.off_part);
   g.mean_out = mean_out;
   g.rstd_out = rstd_out;
@@ -209,32 +226,35 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
   if (p.gemm_fused) {
     hipError_t e = gemm_bf16_launch(g, GEMM_GN_ROWMIN, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
-    return hip_status(rowmin_bcast_launch(g.part, d->N, p.n_ctiles, bias2, out, d->C_out, s));
+    return hip_status(
+        rowmin_bcast_launch(g.part, d->N, p.n_ctiles, bias2, out, p.out_bf16, d->C_out, s));
   }
   hipError_t e = gemm_bf16_launch(g, GEMM_STORE, s);
   if (e != hipSuccess) return C1G_ERR_HIP;
-  if (!nd || (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE)) return C1G_OK;
+  if (conv_only) return C1G_OK;
   // y is [N, C_out, 1]: a group's values are contiguous, as are a row's channels
   float* mean = mean_out ? mean_out : (float*)(ws + p.off_mean);
   float* rstd = rstd_out ? rstd_out : (float*)(ws + p.off_rstd);
   if (p.norm == C1G_NORM_GROUP) {
-    e = gn_stats_launch(out, d->N, d->C_out, 1, nd->G, nd->eps, mean, rstd, s);
+    e = gn_stats_launch(y, d->N, d->C_out, 1, nd->G, nd->eps, mean, rstd, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     e = (p.epi == C1G_EPI_NONE)
-            ? gn_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, 1, nd->G, s)
-            : rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, 1,
-                                 nd->G, 1, s);
+            ? gn_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, out_dt, d->N, d->C_out,
+                              1, nd->G, s)
+            : rowmin_bias_launch(y, C1G_F32, mean, rstd, gamma, beta, bias2, out, out_dt, d->N,
+                                 d->C_out, 1, nd->G, 1, s);
   } else if (p.norm == C1G_NORM_LAYER_CHANNELS) {
     // LayerNorm over the channels of one position == GroupNorm with one group
-    e = gn_stats_launch(out, d->N, d->C_out, 1, 1, nd->eps, mean, rstd, s);
+    e = gn_stats_launch(y, d->N, d->C_out, 1, 1, nd->eps, mean, rstd, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     e = (p.epi == C1G_EPI_NONE)
-            ? ln_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, 1, s)
-            : rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, 1, 0,
-                                 2, s);
+            ? ln_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, out_dt, d->N, d->C_out,
+                              1, s)
+            : rowmin_bias_launch(y, C1G_F32, mean, rstd, gamma, beta, bias2, out, out_dt, d->N,
+                                 d->C_out, 1, 0, 2, s);
   } else {
-    e = rowmin_bias_launch(out, nullptr, nullptr, nullptr, nullptr, bias2, out, d->N, d->C_out,
-                           1, 0, 0, s);
+    e = rowmin_bias_launch(y, C1G_F32, nullptr, nullptr, nullptr, nullptr, bias2, out, out_dt,
+                           d->N, d->C_out, 1, 0, 0, s);
   }
   return hip_status(e);
 }
@@ -282,13 +302,13 @@ size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc*
 }
 
 int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
-                   float* y, void* ws, size_t ws_bytes, void* stream) {
+                   void* y, void* ws, size_t ws_bytes, void* stream) {
   if (!d) return C1G_ERR_INVALID_ARG;
   const Plan p = make_plan(d, nullptr);
   if (p.status != C1G_OK) return p.status;
   if (!x || !w || !y) return C1G_ERR_INVALID_ARG;
-  const size_t es = p.bf16 ? 2 : 4;
-  if (!aligned(x, es) || !aligned(w, es) || !aligned(y, 4) || (bias && !aligned(bias, 4)))
+  const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(w, es) || !aligned(y, os) || (bias && !aligned(bias, 4)))
     return C1G_ERR_MISALIGNED;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
   if (p.route == R_GEMM)
@@ -323,21 +343,35 @@ int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const f
   if (!aligned(y, 4) || !aligned(out, 4) || !aligned(mean, 4) || !aligned(rstd, 4) ||
       (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
     return C1G_ERR_MISALIGNED;
-  return hip_status(
-      gn_apply_launch(y, mean, rstd, gamma, beta, out, N, C, L, G, (hipStream_t)stream));
+  return hip_status(gn_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, C1G_F32, N, C, L,
+                                   G, (hipStream_t)stream));
+}
+
+int gn_apply_bf16(int64_t N, int64_t C, int64_t L, int32_t G, const uint16_t* y,
+                  const float* mean, const float* rstd, const float* gamma, const float* beta,
+                  uint16_t* out, void* stream) {
+  if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
+  if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
+  if ((uint64_t)N * C * L >= (1ull << 32) || C > (1ll << 31) || L > (1ll << 31))
+    return C1G_ERR_UNSUPPORTED;
+  if (!aligned(y, 2) || !aligned(out, 2) || !aligned(mean, 4) || !aligned(rstd, 4) ||
+      (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
+    return C1G_ERR_MISALIGNED;
+  return hip_status(gn_apply_launch(y, C1G_BF16, mean, rstd, gamma, beta, out, C1G_BF16, N, C,
+                                   L, G, (hipStream_t)stream));
 }
 
 int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
                       const void* w, const float* bias, const float* gamma, const float* beta,
-                      const float* bias2, float* out, float* mean_out, float* rstd_out,
+                      const float* bias2, void* out, float* mean_out, float* rstd_out,
                       void* ws, size_t ws_bytes, void* stream) {
   if (!d || !nd) return C1G_ERR_INVALID_ARG;
   const Plan p = make_plan(d, nd);
   if (p.status != C1G_OK) return p.status;
   if (!x || !w || !out) return C1G_ERR_INVALID_ARG;
   if (p.epi == C1G_EPI_ROWMIN_BIAS && !bias2) return C1G_ERR_INVALID_ARG;
-  const size_t es = p.bf16 ? 2 : 4;
-  if (!aligned(x, es) || !aligned(w, es) || !aligned(out, 4) || (bias && !aligned(bias, 4)) ||
+  const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(w, es) || !aligned(out, os) || (bias && !aligned(bias, 4)) ||
       (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)) ||
       (bias2 && !aligned(bias2, 4)) || (mean_out && !aligned(mean_out, 4)) ||
       (rstd_out && !aligned(rstd_out, 4)))
@@ -367,6 +401,7 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
     a.pad_left = d->pad_left;
     a.G = nd->G;
     a.eps = nd->eps;
+    a.out_bf16 = p.out_bf16;
     return hip_status(fused_gn_launch(a, s));
   }
   if (p.route == R_GEMM)
@@ -374,7 +409,8 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
   if (p.route == R_CONV_ONLY)
     return run_conv(p, d, x, w, bias, out, wsb, EPI_STORE, s);
 
-  // split route: conv (+ partial statistics) into out, merge, then in-place passes
+  // split route: conv (+ partial statistics from the fp32 accumulators) into
+  // out in out's type, merge, then in-place passes
   const int conv_epi = p.norm == C1G_NORM_GROUP ? EPI_GN_PART
                        : p.norm == C1G_NORM_LAYER_CHANNELS ? EPI_LN_PART : EPI_STORE;
   int st = run_conv(p, d, x, w, bias, out, wsb, conv_epi, s);
@@ -382,27 +418,30 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
   float* mean = mean_out ? mean_out : (float*)(wsb + p.off_mean);
   float* rstd = rstd_out ? rstd_out : (float*)(wsb + p.off_rstd);
   const float* part = (const float*)(wsb + p.off_part);
+  const int dt = p.out_bf16 ? C1G_BF16 : C1G_F32;
   hipError_t e = hipSuccess;
   if (p.norm == C1G_NORM_GROUP) {
     e = gn_merge_launch(part, d->N, d->C_out, p.T_out, nd->G, p.n_ttiles, p.tm, nd->eps, mean,
                         rstd, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     if (p.epi == C1G_EPI_NONE)
-      e = gn_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, p.T_out, nd->G, s);
+      e = gn_apply_launch(out, dt, mean, rstd, gamma, beta, out, dt, d->N, d->C_out, p.T_out,
+                          nd->G, s);
     else
-      e = rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, p.T_out,
-                             nd->G, 1, s);
+      e = rowmin_bias_launch(out, dt, mean, rstd, gamma, beta, bias2, out, dt, d->N, d->C_out,
+                             p.T_out, nd->G, 1, s);
   } else if (p.norm == C1G_NORM_LAYER_CHANNELS) {
     e = ln_merge_launch(part, d->N, d->C_out, p.T_out, p.n_ctiles, p.tn, nd->eps, mean, rstd, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     if (p.epi == C1G_EPI_NONE)
-      e = ln_apply_launch(out, mean, rstd, gamma, beta, out, d->N, d->C_out, p.T_out, s);
+      e = ln_apply_launch(out, dt, mean, rstd, gamma, beta, out, dt, d->N, d->C_out, p.T_out,
+                          s);
     else
-      e = rowmin_bias_launch(out, mean, rstd, gamma, beta, bias2, out, d->N, d->C_out, p.T_out,
-                             0, 2, s);
+      e = rowmin_bias_launch(out, dt, mean, rstd, gamma, beta, bias2, out, dt, d->N, d->C_out,
+                             p.T_out, 0, 2, s);
   } else {  // no norm, row-min epilogue only
-    e = rowmin_bias_launch(out, nullptr, nullptr, nullptr, nullptr, bias2, out, d->N, d->C_out,
-                           p.T_out, 0, 0, s);
+    e = rowmin_bias_launch(out, dt, nullptr, nullptr, nullptr, nullptr, bias2, out, dt, d->N,
+                           d->C_out, p.T_out, 0, 0, s);
   }
   return hip_status(e);
 }

@@ -11,7 +11,9 @@ namespace c1g {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -64,5 +66,24 @@ __device__ __forceinline__ float xor_sum(float v) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32, two values per instruction).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ u32x2 f32x4_to_bf16(f32x4 v) {
+  return __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+}
+
+// Element access for the two output types: float, or bf16 held as its bits
+// in uint16_t.  Values are always computed in fp32 and rounded on the store.
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+// four consecutive elements; p aligned to 4 elements
+__device__ __forceinline__ void store_elem4(float* p, f32x4 v) { *(f32x4*)p = v; }
+__device__ __forceinline__ void store_elem4(uint16_t* p, f32x4 v) { *(u32x2*)p = f32x4_to_bf16(v); }
 
 }  // namespace c1g

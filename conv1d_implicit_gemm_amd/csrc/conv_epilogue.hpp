@@ -5,13 +5,14 @@
 // (lr = lane%16, kq = lane/16) holding rows t = 4*kq + r (r = 0..3) of column
 // c = lr of each tile.
 //
-//   EPI_STORE    y = acc + bias
+//   EPI_STORE    y = acc + bias, stored as fp32 or (y_bf16) rounded to bf16
 //   EPI_GN_PART  also, per channel, (mean, M2) over the tile's valid
 //                positions -> part[(n*C_out + c)*n_ttiles + ttile]
 //   EPI_LN_PART  also, per position, (mean, M2) over the tile's valid
 //                channels  -> part[(n*n_ctiles + ctile)*T_out + t]
 //
-// Partial statistics: two passes over the registers (mean, then squared
+// Partial statistics are taken from the fp32 values, before any rounding of
+// the stored y.  Two passes over the registers (mean, then squared
 // deviations), xor-shuffle sums across lanes, then a fixed-order pairwise
 // merge across waves through LDS; every partial has one fixed slot (no
 // atomics), so the later merge is deterministic.
@@ -25,6 +26,35 @@
 
 namespace c1g {
 
+// y = acc (bias already added) in the output type TO (float, or bf16 bits);
+// four consecutive positions of one channel per lane and tile.
+template <typename TO, int WM, int WN, int WGM, int WGN>
+__device__ __forceinline__ void conv_store(const ConvArgs& a, const f32x4 (&acc)[WM][WN],
+                                           int64_t n, int64_t t0, int c0, int wm, int wn) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int64_t T_out = a.T_out;
+  TO* y = (TO*)a.y;
+  const bool vec_ok = ((T_out & 3) == 0) && ((((uintptr_t)y) & (4 * sizeof(TO) - 1)) == 0);
+#pragma unroll
+  for (int jn = 0; jn < WN; ++jn) {
+    const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+    if (c >= a.C_out) continue;
+    TO* dst = y + (n * a.C_out + c) * T_out;
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq;
+      if (vec_ok && t + 3 < T_out) {
+        store_elem4(dst + t, acc[i][jn]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t + r < T_out) store_elem(dst + t + r, acc[i][jn][r]);
+      }
+    }
+  }
+}
+
 template <int WM, int WN, int WGM, int WGN>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
                                               f32x4 (&acc)[WM][WN], int64_t n, int64_t t0,
@@ -35,7 +65,6 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
   const int lane = tid & 63;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t T_out = a.T_out;
-  const bool vec_ok = ((T_out & 3) == 0) && ((((uintptr_t)a.y) & 15) == 0);
   // all bias loads before the first store: a load issued between stores would
   // make its wait also wait for every store before it
   float bias[WN];
@@ -45,24 +74,14 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
     bias[jn] = (a.bias != nullptr && c < a.C_out) ? a.bias[c] : 0.f;
   }
 #pragma unroll
-  for (int jn = 0; jn < WN; ++jn) {
-    const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-    const float b = bias[jn];
+  for (int jn = 0; jn < WN; ++jn)
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      acc[i][jn] += b;
-      if (active && c < a.C_out) {
-        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq;
-        float* dst = a.y + (n * a.C_out + c) * T_out;
-        if (vec_ok && t + 3 < T_out) {
-          *(f32x4*)(dst + t) = acc[i][jn];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (t + r < T_out) dst[t + r] = acc[i][jn][r];
-        }
-      }
-    }
+    for (int i = 0; i < WM; ++i) acc[i][jn] += bias[jn];
+  if (active) {
+    if (a.y_bf16)
+      conv_store<uint16_t, WM, WN, WGM, WGN>(a, acc, n, t0, c0, wm, wn);
+    else
+      conv_store<float, WM, WN, WGM, WGN>(a, acc, n, t0, c0, wm, wn);
   }
   if (epi == EPI_STORE) return;
 

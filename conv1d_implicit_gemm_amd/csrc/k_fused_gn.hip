@@ -174,22 +174,30 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
     const float ga = a.gamma ? a.gamma[c] : 1.f;
     const float be = a.beta ? a.beta[c] : 0.f;
     const float sc = rstd * ga;
-    float* dst = a.out + (n * a.C_out + c) * T_out;
-    const bool vec_ok = ((T_out & 3) == 0) && ((((uintptr_t)a.out) & 15) == 0);
+    // out as fp32, or rounded to bf16 (out_bf16)
+    auto store = [&](auto* out) __attribute__((always_inline)) {
+      auto* dst = out + (n * a.C_out + c) * T_out;
+      const bool vec_ok =
+          ((T_out & 3) == 0) && ((((uintptr_t)out) & (4 * sizeof(*out) - 1)) == 0);
 #pragma unroll
-    for (int m = 0; m < MQ; ++m) {
-      const int64_t t = t_lane + m * 16;
-      f32x4 z;
+      for (int m = 0; m < MQ; ++m) {
+        const int64_t t = t_lane + m * 16;
+        f32x4 z;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = (acc[m][r] - mean) * sc + be;
-      if (vec_ok && t + 3 < T_out) {
-        *(f32x4*)(dst + t) = z;
-      } else {
+        for (int r = 0; r < 4; ++r) z[r] = (acc[m][r] - mean) * sc + be;
+        if (vec_ok && t + 3 < T_out) {
+          store_elem4(dst + t, z);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t + r < T_out) dst[t + r] = z[r];
+          for (int r = 0; r < 4; ++r)
+            if (t + r < T_out) store_elem(dst + t + r, z[r]);
+        }
       }
-    }
+    };
+    if (a.out_bf16)
+      store((uint16_t*)a.out);
+    else
+      store((float*)a.out);
     if (wave == 0 && kq == 0 && (lr % cpg) == 0) {
       const int64_t g = c / cpg;
       if (a.mean_out) a.mean_out[n * a.G + g] = mean;

@@ -249,29 +249,36 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
   // (kh = 0 waves hold the complete tile; kh = 1 waves only join the barriers)
   if (EPI == GEMM_STORE) {
     if (kh != 0) return;
-    const bool vec = (a.C_out % 4 == 0) && ((((uintptr_t)a.y) & 15) == 0);
+    // y as fp32, or rounded to bf16 (y_bf16)
+    auto store = [&](auto* y) __attribute__((always_inline)) {
+      const bool vec = (a.C_out % 4 == 0) && ((((uintptr_t)y) & (4 * sizeof(*y) - 1)) == 0);
 #pragma unroll
-    for (int i = 0; i < WMT; ++i) {
-      const int64_t c = c0 + wc * WMT * 16 + 16 * i + 4 * kq;
-      f32x4 b = {0.f, 0.f, 0.f, 0.f};
-      if (a.bias)
+      for (int i = 0; i < WMT; ++i) {
+        const int64_t c = c0 + wc * WMT * 16 + 16 * i + 4 * kq;
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+        if (a.bias)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[r] = (c + r < a.C_out) ? a.bias[c + r] : 0.f;
+          for (int r = 0; r < 4; ++r) b[r] = (c + r < a.C_out) ? a.bias[c + r] : 0.f;
 #pragma unroll
-      for (int j = 0; j < WNT; ++j) {
-        const int64_t nn = n0 + wnn * WNT * 16 + 16 * j + lr;
-        if (nn >= a.N) continue;
-        const f32x4 v = acc[i][j] + b;
-        float* dst = a.y + nn * a.C_out + c;
-        if (vec && c + 3 < a.C_out) {
-          *(f32x4*)dst = v;
-        } else {
+        for (int j = 0; j < WNT; ++j) {
+          const int64_t nn = n0 + wnn * WNT * 16 + 16 * j + lr;
+          if (nn >= a.N) continue;
+          const f32x4 v = acc[i][j] + b;
+          auto* dst = y + nn * a.C_out + c;
+          if (vec && c + 3 < a.C_out) {
+            store_elem4(dst, v);
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (c + r < a.C_out) dst[r] = v[r];
+            for (int r = 0; r < 4; ++r)
+              if (c + r < a.C_out) store_elem(dst + r, v[r]);
+          }
         }
       }
-    }
+    };
+    if (a.y_bf16)
+      store((uint16_t*)a.y);
+    else
+      store((float*)a.y);
   } else {  // GEMM_GN_ROWMIN: groups of 16 channels = one tile column block
     float* red = (float*)smem;  // free after the reduction's last barrier
     float rmin[WNT];
@@ -334,22 +341,25 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-// out[n][c] = min over c-tiles of part[n][*] + bias2[c]; one workgroup per row
+// out[n][c] = min over c-tiles of part[n][*] + bias2[c]; one workgroup per row;
+// TO is float, or bf16 bits (rounded to nearest even)
+template <typename TO>
 __global__ __launch_bounds__(NTHR) void rowmin_bcast_kernel(const float* __restrict__ part,
                                                             int n_ctiles,
                                                             const float* __restrict__ bias2,
-                                                            float* out, int64_t C) {
+                                                            TO* out, int64_t C) {
   const int64_t n = blockIdx.x;
   float m = __builtin_inff();
   for (int t = 0; t < n_ctiles; ++t) m = fminf(m, part[n * n_ctiles + t]);
-  float* row = out + n * C;
-  if ((C % 4) == 0 && (((uintptr_t)out) & 15) == 0 && (((uintptr_t)bias2) & 15) == 0) {
+  TO* row = out + n * C;
+  if ((C % 4) == 0 && (((uintptr_t)out) & (4 * sizeof(TO) - 1)) == 0 &&
+      (((uintptr_t)bias2) & 15) == 0) {
     for (int64_t q = threadIdx.x; q < C / 4; q += NTHR) {
       const f32x4 b = *(const f32x4*)(bias2 + 4 * q);
-      *(f32x4*)(row + 4 * q) = b + m;
+      store_elem4(row + 4 * q, b + m);
     }
   } else {
-    for (int64_t c = threadIdx.x; c < C; c += NTHR) row[c] = m + bias2[c];
+    for (int64_t c = threadIdx.x; c < C; c += NTHR) store_elem(row + c, m + bias2[c]);
   }
 }
 
@@ -365,9 +375,13 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s) {
 }
 
 hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const float* bias2,
-                               float* out, int64_t C, hipStream_t s) {
-  hipLaunchKernelGGL(rowmin_bcast_kernel, dim3((unsigned)N), dim3(NTHR), 0, s, part, n_ctiles,
-                     bias2, out, C);
+                               void* out, bool out_bf16, int64_t C, hipStream_t s) {
+  if (out_bf16)
+    hipLaunchKernelGGL(rowmin_bcast_kernel<uint16_t>, dim3((unsigned)N), dim3(NTHR), 0, s, part,
+                       n_ctiles, bias2, (uint16_t*)out, C);
+  else
+    hipLaunchKernelGGL(rowmin_bcast_kernel<float>, dim3((unsigned)N), dim3(NTHR), 0, s, part,
+                       n_ctiles, bias2, (float*)out, C);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 //   gn_merge   per-(n, c, t-tile) partials -> GroupNorm mean/rstd per (n, g)
 //   gn_stats   GroupNorm mean/rstd straight from an fp32 y (one pass)
 //   gn_apply   out = (y - mean) * rstd * gamma + beta, per (n, g) statistics
+//              (y and out fp32 or bf16; arithmetic in fp32)
 //   ln_merge   per-(n, c-tile, t) partials -> LayerNorm-over-channels mean/rstd
 //   ln_apply   the same affine with per-(n, t) statistics
 //   rowmin     min over channels of the normalised value, plus bias2 broadcast
@@ -132,26 +133,73 @@ __global__ __launch_bounds__(NT) void gn_stats_kernel(const float* __restrict__ 
   }
 }
 
-// mode 1: statistics per (n, g); mode 2: per (n, l)
-template <int MODE, bool VEC>
-__global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
+// The 4 values of unit u of a raw 16-byte vector of TI (fp32: one unit;
+// bf16: two units, element order preserved).
+template <typename TI>
+__device__ __forceinline__ f32x4 unit_values(u32x4 raw, int u) {
+  if constexpr (sizeof(TI) == 4) {
+    return __builtin_bit_cast(f32x4, raw);
+  } else {
+    const uint32_t lo = raw[2 * u], hi = raw[2 * u + 1];
+    return f32x4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                 __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+  }
+}
+
+// Store VU units (4 * VU consecutive elements) of the output type TO.
+template <int VU>
+__device__ __forceinline__ void store_units(float* p, const f32x4 (&z)[VU]) {
+#pragma unroll
+  for (int u = 0; u < VU; ++u) __builtin_nontemporal_store(z[u], (f32x4*)(p + 4 * u));
+}
+template <int VU>
+__device__ __forceinline__ void store_units(uint16_t* p, const f32x4 (&z)[VU]) {
+  if constexpr (VU == 2) {
+    const u32x2 a = f32x4_to_bf16(z[0]), b = f32x4_to_bf16(z[1]);
+    __builtin_nontemporal_store(u32x4{a[0], a[1], b[0], b[1]}, (u32x4*)p);
+  } else {
+#pragma unroll
+    for (int u = 0; u < VU; ++u)
+      __builtin_nontemporal_store(f32x4_to_bf16(z[u]), (u32x2*)(p + 4 * u));
+  }
+}
+
+// mode 1: statistics per (n, g); mode 2: per (n, l).  TI / TO: element types
+// of y and out (float, or bf16 bits in uint16_t); arithmetic in fp32, out
+// rounded to nearest even when bf16.
+template <int MODE, bool VEC, typename TI, typename TO>
+__global__ __launch_bounds__(NT) void apply_kernel(const TI* __restrict__ y,
                                                    const float* __restrict__ mean,
                                                    const float* __restrict__ rstd,
                                                    const float* __restrict__ gamma,
-                                                   const float* __restrict__ beta, float* out,
+                                                   const float* __restrict__ beta, TO* out,
                                                    uint32_t total, FastDiv divL, FastDiv divC,
                                                    uint32_t C, uint32_t L, uint32_t G,
                                                    uint32_t cpg) {
   const uint32_t step = gridDim.x * NT;
+  // one element, all index math from scratch
+  auto scalar = [&](uint32_t e) __attribute__((always_inline)) {
+    const uint32_t row = divL.div(e);
+    const uint32_t l = e - row * L;
+    const uint32_t n = divC.div(row);
+    const uint32_t c = row - n * C;
+    const float ga = gamma ? gamma[c] : 1.f, be = beta ? beta[c] : 0.f;
+    float mu, rs;
+    if (MODE == 1) {
+      mu = mean[n * G + c / cpg];
+      rs = rstd[n * G + c / cpg];
+    } else {
+      mu = mean[(size_t)n * L + l];
+      rs = rstd[(size_t)n * L + l];
+    }
+    store_elem(out + e, (load_elem(y + e) - mu) * (rs * ga) + be);
+  };
   if (VEC) {
-    // Block-contiguous batches: per iteration a workgroup owns UNR * NT
-    // consecutive 16-byte vectors (UNR loads in flight per thread, all before
-    // any store); measured on this GPU, contiguous per-workgroup spans stream
-    // ~10% faster than a grid-strided interleave.
-    constexpr int UNR = 2;
-    const uint32_t nv = total >> 2;
-    auto one = [&](uint32_t v, const f32x4& yv) {
-      const uint32_t e = v << 2;
+    // 16-byte vectors of y: EPV elements, VU units of 4 (a unit never
+    // crosses a row: L % 4 == 0)
+    constexpr uint32_t EPV = 16 / sizeof(TI), VU = EPV / 4;
+    const uint32_t nv = total / EPV;
+    auto unit = [&](uint32_t e, const f32x4& yv) __attribute__((always_inline)) {
       const uint32_t row = divL.div(e);
       const uint32_t l = e - row * L;
       const uint32_t n = divC.div(row);
@@ -169,31 +217,47 @@ __global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
 #pragma unroll
         for (int i = 0; i < 4; ++i) z[i] = (yv[i] - mu[i]) * (rs[i] * ga) + be;
       }
-      __builtin_nontemporal_store(z, (f32x4*)(out + e));
+      return z;
     };
+    auto one = [&](uint32_t v, const u32x4& raw) __attribute__((always_inline)) {
+      const uint32_t e = v * EPV;
+      f32x4 z[VU];
+#pragma unroll
+      for (uint32_t u = 0; u < VU; ++u) z[u] = unit(e + 4 * u, unit_values<TI>(raw, u));
+      store_units<VU>(out + e, z);
+    };
+    auto load = [&](uint32_t v) __attribute__((always_inline)) {
+      return __builtin_nontemporal_load((const u32x4*)(y + (size_t)v * EPV));
+    };
+    // elements past the last whole vector (bf16 y with total % 8 == 4)
+    for (uint32_t e = nv * EPV + blockIdx.x * NT + threadIdx.x; e < total; e += step) scalar(e);
     if (MODE == 2) {
-      // three loads per vector (y, mean, rstd): a grid-strided loop with four
+      // three loads per unit (y, mean, rstd): a grid-strided loop with four
       // vectors in flight per thread measured faster here
       constexpr int U2 = 4;
       uint32_t v = blockIdx.x * NT + threadIdx.x;
       for (; v + (U2 - 1) * step < nv; v += U2 * step) {
-        f32x4 yv[U2];
+        u32x4 yv[U2];
 #pragma unroll
-        for (int u = 0; u < U2; ++u)
-          yv[u] = __builtin_nontemporal_load((const f32x4*)(y + ((size_t)(v + u * step) << 2)));
+        for (int u = 0; u < U2; ++u) yv[u] = load(v + u * step);
 #pragma unroll
         for (int u = 0; u < U2; ++u) one(v + u * step, yv[u]);
       }
-      for (; v < nv; v += step) one(v, *(const f32x4*)(y + ((size_t)v << 2)));
+      for (; v < nv; v += step) one(v, load(v));
       return;
     }
+    // Block-contiguous batches: per iteration a workgroup owns UNR * NT
+    // consecutive 16-byte vectors (UNR loads in flight per thread, all before
+    // any store); measured on this GPU, contiguous per-workgroup spans stream
+    // ~10% faster than a grid-strided interleave.
+    constexpr int UNR = 2;
     const uint32_t batch = UNR * NT;
     for (uint32_t base = blockIdx.x * batch; base < nv; base += gridDim.x * batch) {
-      f32x4 yv[UNR];
+      u32x4 yv[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const uint32_t v = base + u * NT + threadIdx.x;
-        if (v < nv) yv[u] = __builtin_nontemporal_load((const f32x4*)(y + ((size_t)v << 2)));
+        if (v < nv) yv[u] = load(v);
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
@@ -202,22 +266,7 @@ __global__ __launch_bounds__(NT) void apply_kernel(const float* __restrict__ y,
       }
     }
   } else {
-    for (uint32_t e = blockIdx.x * NT + threadIdx.x; e < total; e += step) {
-      const uint32_t row = divL.div(e);
-      const uint32_t l = e - row * L;
-      const uint32_t n = divC.div(row);
-      const uint32_t c = row - n * C;
-      const float ga = gamma ? gamma[c] : 1.f, be = beta ? beta[c] : 0.f;
-      float mu, rs;
-      if (MODE == 1) {
-        mu = mean[n * G + c / cpg];
-        rs = rstd[n * G + c / cpg];
-      } else {
-        mu = mean[(size_t)n * L + l];
-        rs = rstd[(size_t)n * L + l];
-      }
-      out[e] = (y[e] - mu) * (rs * ga) + be;
-    }
+    for (uint32_t e = blockIdx.x * NT + threadIdx.x; e < total; e += step) scalar(e);
   }
 }
 
@@ -251,11 +300,11 @@ __device__ __forceinline__ float normed(float v, const float* mean, const float*
 }
 
 // one thread per (n, l): two passes over the channels
-template <int KIND>
-__global__ __launch_bounds__(NT) void rowmin_kernel(const float* __restrict__ y,
+template <int KIND, typename TI, typename TO>
+__global__ __launch_bounds__(NT) void rowmin_kernel(const TI* __restrict__ y,
                                                     const float* mean, const float* rstd,
                                                     const float* gamma, const float* beta,
-                                                    const float* __restrict__ bias2, float* out,
+                                                    const float* __restrict__ bias2, TO* out,
                                                     int64_t N, int64_t C, int64_t L, int64_t G) {
   const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
   if (idx >= N * L) return;
@@ -263,26 +312,27 @@ __global__ __launch_bounds__(NT) void rowmin_kernel(const float* __restrict__ y,
   const int64_t cpg = G > 0 ? C / G : 1;
   float m = __builtin_inff();
   for (int64_t c = 0; c < C; ++c) {
-    const float z = normed<KIND>(y[(n * C + c) * L + l], mean, rstd, gamma, beta, n, c, l, L,
-                                 G, cpg);
+    const float z = normed<KIND>(load_elem(y + (n * C + c) * L + l), mean, rstd, gamma, beta, n,
+                                 c, l, L, G, cpg);
     m = z < m ? z : m;
   }
-  for (int64_t c = 0; c < C; ++c) out[(n * C + c) * L + l] = m + bias2[c];
+  for (int64_t c = 0; c < C; ++c) store_elem(out + (n * C + c) * L + l, m + bias2[c]);
 }
 
 // L == 1: one workgroup per row n, threads over channels
-template <int KIND>
-__global__ __launch_bounds__(NT) void rowmin_l1_kernel(const float* __restrict__ y,
+template <int KIND, typename TI, typename TO>
+__global__ __launch_bounds__(NT) void rowmin_l1_kernel(const TI* __restrict__ y,
                                                        const float* mean, const float* rstd,
                                                        const float* gamma, const float* beta,
                                                        const float* __restrict__ bias2,
-                                                       float* out, int64_t C, int64_t G) {
+                                                       TO* out, int64_t C, int64_t G) {
   __shared__ float sh[NT];
   const int64_t n = blockIdx.x;
   const int64_t cpg = G > 0 ? C / G : 1;
   float m = __builtin_inff();
   for (int64_t c = threadIdx.x; c < C; c += NT) {
-    const float z = normed<KIND>(y[n * C + c], mean, rstd, gamma, beta, n, c, 0, 1, G, cpg);
+    const float z = normed<KIND>(load_elem(y + n * C + c), mean, rstd, gamma, beta, n, c, 0, 1,
+                                 G, cpg);
     m = z < m ? z : m;
   }
   sh[threadIdx.x] = m;
@@ -292,7 +342,7 @@ __global__ __launch_bounds__(NT) void rowmin_l1_kernel(const float* __restrict__
     __syncthreads();
   }
   m = sh[0];
-  for (int64_t c = threadIdx.x; c < C; c += NT) out[n * C + c] = m + bias2[c];
+  for (int64_t c = threadIdx.x; c < C; c += NT) store_elem(out + n * C + c, m + bias2[c]);
 }
 
 unsigned grid_for(uint64_t work) {
@@ -301,29 +351,79 @@ unsigned grid_for(uint64_t work) {
   return (unsigned)(b < 1 ? 1 : (b > cap ? cap : b));
 }
 
-template <int MODE>
-hipError_t apply_launch(const float* y, const float* mean, const float* rstd,
-                        const float* gamma, const float* beta, float* out, int64_t N, int64_t C,
-                        int64_t L, int32_t G, hipStream_t s) {
+template <int MODE, typename TI, typename TO>
+hipError_t apply_launch_t(const TI* y, const float* mean, const float* rstd, const float* gamma,
+                          const float* beta, TO* out, int64_t N, int64_t C, int64_t L,
+                          int32_t G, hipStream_t s) {
   const uint64_t total = (uint64_t)N * C * L;
   if (total >= (1ull << 32)) return hipErrorInvalidValue;
   const FastDiv dl = FastDiv::make((uint32_t)L), dc = FastDiv::make((uint32_t)C);
   const uint32_t cpg = (MODE == 1) ? (uint32_t)(C / G) : 1u;
-  const bool vec = (L % 4 == 0) && ((((uintptr_t)y) & 15) == 0) && ((((uintptr_t)out) & 15) == 0) &&
+  // out is written VU units of 4 at a time per 16-byte vector of y
+  constexpr uintptr_t out_align = (16 / sizeof(TI) / 4) * 4 * sizeof(TO);
+  const bool vec = (L % 4 == 0) && ((((uintptr_t)y) & 15) == 0) &&
+                   ((((uintptr_t)out) & (out_align - 1)) == 0) &&
                    (MODE == 1 || ((((uintptr_t)mean) & 15) == 0 && (((uintptr_t)rstd) & 15) == 0));
   if (vec) {
-    const uint64_t batches = (total / 4 + 2 * NT - 1) / (2 * NT);
-    const unsigned grid = MODE == 2 ? grid_for(total / 4)
+    const uint64_t nvec = total / (16 / sizeof(TI));
+    const uint64_t batches = (nvec + 2 * NT - 1) / (2 * NT);
+    const unsigned grid = MODE == 2 ? grid_for(nvec)
                                     : (unsigned)(batches < 8192 ? (batches < 1 ? 1 : batches) : 8192);
-    hipLaunchKernelGGL((apply_kernel<MODE, true>), dim3(grid), dim3(NT), 0, s, y,
-                       mean, rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
+    hipLaunchKernelGGL((apply_kernel<MODE, true, TI, TO>), dim3(grid), dim3(NT), 0, s, y, mean,
+                       rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
                        (uint32_t)L, (uint32_t)G, cpg);
   } else {
-    hipLaunchKernelGGL((apply_kernel<MODE, false>), dim3(grid_for(total)), dim3(NT), 0, s, y,
-                       mean, rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
+    hipLaunchKernelGGL((apply_kernel<MODE, false, TI, TO>), dim3(grid_for(total)), dim3(NT), 0,
+                       s, y, mean, rstd, gamma, beta, out, (uint32_t)total, dl, dc, (uint32_t)C,
                        (uint32_t)L, (uint32_t)G, cpg);
   }
   return hipGetLastError();
+}
+
+// element types: 0 fp32, 1 bf16 (enum c1g_dtype)
+template <int MODE>
+hipError_t apply_launch(const void* y, int y_dt, const float* mean, const float* rstd,
+                        const float* gamma, const float* beta, void* out, int out_dt, int64_t N,
+                        int64_t C, int64_t L, int32_t G, hipStream_t s) {
+  if (y_dt == 0 && out_dt == 0)
+    return apply_launch_t<MODE>((const float*)y, mean, rstd, gamma, beta, (float*)out, N, C, L,
+                                G, s);
+  if (y_dt == 1 && out_dt == 1)
+    return apply_launch_t<MODE>((const uint16_t*)y, mean, rstd, gamma, beta, (uint16_t*)out, N,
+                                C, L, G, s);
+  if (y_dt == 0 && out_dt == 1)
+    return apply_launch_t<MODE>((const float*)y, mean, rstd, gamma, beta, (uint16_t*)out, N, C,
+                                L, G, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename TI, typename TO>
+void rowmin_launch_t(const TI* y, const float* mean, const float* rstd, const float* gamma,
+                     const float* beta, const float* bias2, TO* out, int64_t N, int64_t C,
+                     int64_t L, int32_t G, int norm_kind, hipStream_t s) {
+  if (L == 1) {
+    dim3 grid((unsigned)N);
+    if (norm_kind == 1)
+      hipLaunchKernelGGL((rowmin_l1_kernel<1, TI, TO>), grid, dim3(NT), 0, s, y, mean, rstd,
+                         gamma, beta, bias2, out, C, (int64_t)G);
+    else if (norm_kind == 2)
+      hipLaunchKernelGGL((rowmin_l1_kernel<2, TI, TO>), grid, dim3(NT), 0, s, y, mean, rstd,
+                         gamma, beta, bias2, out, C, (int64_t)G);
+    else
+      hipLaunchKernelGGL((rowmin_l1_kernel<0, TI, TO>), grid, dim3(NT), 0, s, y, mean, rstd,
+                         gamma, beta, bias2, out, C, (int64_t)G);
+  } else {
+    dim3 grid((unsigned)((N * L + NT - 1) / NT));
+    if (norm_kind == 1)
+      hipLaunchKernelGGL((rowmin_kernel<1, TI, TO>), grid, dim3(NT), 0, s, y, mean, rstd, gamma,
+                         beta, bias2, out, N, C, L, (int64_t)G);
+    else if (norm_kind == 2)
+      hipLaunchKernelGGL((rowmin_kernel<2, TI, TO>), grid, dim3(NT), 0, s, y, mean, rstd, gamma,
+                         beta, bias2, out, N, C, L, (int64_t)G);
+    else
+      hipLaunchKernelGGL((rowmin_kernel<0, TI, TO>), grid, dim3(NT), 0, s, y, mean, rstd, gamma,
+                         beta, bias2, out, N, C, L, (int64_t)G);
+  }
 }
 
 }  // namespace
@@ -343,10 +443,10 @@ hipError_t gn_stats_launch(const float* y, int64_t N, int64_t C, int64_t L, int3
   return hipGetLastError();
 }
 
-hipError_t gn_apply_launch(const float* y, const float* mean, const float* rstd,
-                           const float* gamma, const float* beta, float* out, int64_t N,
-                           int64_t C, int64_t L, int32_t G, hipStream_t s) {
-  return apply_launch<1>(y, mean, rstd, gamma, beta, out, N, C, L, G, s);
+hipError_t gn_apply_launch(const void* y, int y_dt, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, void* out, int out_dt,
+                           int64_t N, int64_t C, int64_t L, int32_t G, hipStream_t s) {
+  return apply_launch<1>(y, y_dt, mean, rstd, gamma, beta, out, out_dt, N, C, L, G, s);
 }
 
 hipError_t ln_merge_launch(const float* part, int64_t N, int64_t C, int64_t L,
@@ -358,39 +458,27 @@ hipError_t ln_merge_launch(const float* part, int64_t N, int64_t C, int64_t L,
   return hipGetLastError();
 }
 
-hipError_t ln_apply_launch(const float* y, const float* mean, const float* rstd,
-                           const float* gamma, const float* beta, float* out, int64_t N,
-                           int64_t C, int64_t L, hipStream_t s) {
-  return apply_launch<2>(y, mean, rstd, gamma, beta, out, N, C, L, 1, s);
+hipError_t ln_apply_launch(const void* y, int y_dt, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, void* out, int out_dt,
+                           int64_t N, int64_t C, int64_t L, hipStream_t s) {
+  return apply_launch<2>(y, y_dt, mean, rstd, gamma, beta, out, out_dt, N, C, L, 1, s);
 }
 
-hipError_t rowmin_bias_launch(const float* y, const float* mean, const float* rstd,
+hipError_t rowmin_bias_launch(const void* y, int y_dt, const float* mean, const float* rstd,
                               const float* gamma, const float* beta, const float* bias2,
-                              float* out, int64_t N, int64_t C, int64_t L, int32_t G,
-                              int norm_kind, hipStream_t s) {
-  if (L == 1) {
-    dim3 grid((unsigned)N);
-    if (norm_kind == 1)
-      hipLaunchKernelGGL(rowmin_l1_kernel<1>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
-                         bias2, out, C, (int64_t)G);
-    else if (norm_kind == 2)
-      hipLaunchKernelGGL(rowmin_l1_kernel<2>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
-                         bias2, out, C, (int64_t)G);
-    else
-      hipLaunchKernelGGL(rowmin_l1_kernel<0>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
-                         bias2, out, C, (int64_t)G);
-  } else {
-    dim3 grid((unsigned)((N * L + NT - 1) / NT));
-    if (norm_kind == 1)
-      hipLaunchKernelGGL(rowmin_kernel<1>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
-                         bias2, out, N, C, L, (int64_t)G);
-    else if (norm_kind == 2)
-      hipLaunchKernelGGL(rowmin_kernel<2>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
-                         bias2, out, N, C, L, (int64_t)G);
-    else
-      hipLaunchKernelGGL(rowmin_kernel<0>, grid, dim3(NT), 0, s, y, mean, rstd, gamma, beta,
-                         bias2, out, N, C, L, (int64_t)G);
-  }
+                              void* out, int out_dt, int64_t N, int64_t C, int64_t L,
+                              int32_t G, int norm_kind, hipStream_t s) {
+  if (y_dt == 0 && out_dt == 0)
+    rowmin_launch_t((const float*)y, mean, rstd, gamma, beta, bias2, (float*)out, N, C, L, G,
+                    norm_kind, s);
+  else if (y_dt == 1 && out_dt == 1)
+    rowmin_launch_t((const uint16_t*)y, mean, rstd, gamma, beta, bias2, (uint16_t*)out, N, C,
+                    L, G, norm_kind, s);
+  else if (y_dt == 0 && out_dt == 1)
+    rowmin_launch_t((const float*)y, mean, rstd, gamma, beta, bias2, (uint16_t*)out, N, C, L,
+                    G, norm_kind, s);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

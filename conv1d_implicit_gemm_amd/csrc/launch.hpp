@@ -21,13 +21,14 @@ struct ConvArgs {
   const void* x;       // [N, C_in, T] fp32 or bf16
   const void* wp;      // packed weights (layout owned by the kernel file)
   const float* bias;   // [C_out] or nullptr
-  float* y;            // [N, C_out, T_out]
-  float* part;         // partial statistics (EPI_GN_PART / EPI_LN_PART)
+  void* y;             // [N, C_out, T_out], fp32 or (y_bf16) bf16
+  float* part;         // partial statistics (EPI_GN_PART / EPI_LN_PART), from fp32 values
   int64_t N, C_in, C_out, T, T_out;
   int32_t K, stride, dilation, pad_left;
   int32_t n_chunks;    // ceil(C_in / CK)
   int32_t n_ttiles;    // ceil(T_out / TM)
   int32_t n_ctiles;    // ceil(C_out / TN)
+  int32_t y_bf16;      // y is stored as bf16 (rounded to nearest even)
 };
 
 // ---- fp32 split-path convolution (k_conv_f32.hip)
@@ -62,20 +63,21 @@ struct GemmArgs {
   const float* bias;   // [C_out] or nullptr
   const float* gamma;  // GN_ROWMIN: [C_out] or nullptr
   const float* beta;
-  float* y;            // STORE: [N, C_out]
+  void* y;             // STORE: [N, C_out], fp32 or (y_bf16) bf16
   float* part;         // GN_ROWMIN: [N, n_ctiles] per-tile row minima
   float* mean_out;     // GN_ROWMIN: [N, G] or nullptr
   float* rstd_out;
   int64_t N, C_in, C_out;
   int32_t G, n_ctiles, n_ntiles;
   float eps;
+  int32_t y_bf16;
 };
 int gemm_bf16_tile_c();
 int gemm_bf16_tile_n();
 hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s);
-// out[n][c] = min_t part[n][t] + bias2[c]
+// out[n][c] = min_t part[n][t] + bias2[c]; out fp32 or (out_bf16) bf16
 hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const float* bias2,
-                               float* out, int64_t C, hipStream_t s);
+                               void* out, bool out_bf16, int64_t C, hipStream_t s);
 
 // ---- fp32 fused conv + GroupNorm, one workgroup per (n, 16-channel block)
 // (k_fused_gn.hip).  Supported when C_out/G divides 16 and the whole
@@ -86,12 +88,13 @@ struct FusedArgs {
   const float* bias;
   const float* gamma;
   const float* beta;
-  float* out;
+  void* out;           // fp32 or (out_bf16) bf16
   float* mean_out;     // [N, G] or nullptr
   float* rstd_out;
   int64_t N, C_in, C_out, T, T_out;
   int32_t K, stride, dilation, pad_left, G;
   float eps;
+  int32_t out_bf16;
 };
 int fused_gn_max_tout(int stride, int K, int dilation);  // 0 if unsupported
 bool fused_gn_supported(int64_t C_in, int64_t C_out, int32_t G, int64_t T_out, int stride,
@@ -106,23 +109,25 @@ hipError_t gn_merge_launch(const float* part, int64_t N, int64_t C, int64_t L, i
 // GroupNorm statistics straight from y [N, C, L] -> mean/rstd [N, G]
 hipError_t gn_stats_launch(const float* y, int64_t N, int64_t C, int64_t L, int32_t G,
                            float eps, float* mean, float* rstd, hipStream_t s);
+// Element types of y and out in the passes below (values of enum c1g_dtype):
+// fp32 -> fp32, bf16 -> bf16 and fp32 -> bf16 are built; out may equal y.
 // out = (y - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c]
-hipError_t gn_apply_launch(const float* y, const float* mean, const float* rstd,
-                           const float* gamma, const float* beta, float* out, int64_t N,
-                           int64_t C, int64_t L, int32_t G, hipStream_t s);
+hipError_t gn_apply_launch(const void* y, int y_dt, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, void* out, int out_dt,
+                           int64_t N, int64_t C, int64_t L, int32_t G, hipStream_t s);
 // LayerNorm over channels: partials [N, n_ctiles, L] (mean, M2), tile width tn
 hipError_t ln_merge_launch(const float* part, int64_t N, int64_t C, int64_t L,
                            int32_t n_ctiles, int32_t tn, float eps, float* mean, float* rstd,
                            hipStream_t s);
-hipError_t ln_apply_launch(const float* y, const float* mean, const float* rstd,
-                           const float* gamma, const float* beta, float* out, int64_t N,
-                           int64_t C, int64_t L, hipStream_t s);
+hipError_t ln_apply_launch(const void* y, int y_dt, const float* mean, const float* rstd,
+                           const float* gamma, const float* beta, void* out, int out_dt,
+                           int64_t N, int64_t C, int64_t L, hipStream_t s);
 // Row-min epilogue: z = (y - mean) * rstd * gamma + beta with statistics per
 // (n, group) (norm_kind 1), per (n, l) (norm_kind 2) or none (norm_kind 0);
 // out[n,c,l] = min_c z[n,c,l] + bias2[c].
-hipError_t rowmin_bias_launch(const float* y, const float* mean, const float* rstd,
+hipError_t rowmin_bias_launch(const void* y, int y_dt, const float* mean, const float* rstd,
                               const float* gamma, const float* beta, const float* bias2,
-                              float* out, int64_t N, int64_t C, int64_t L, int32_t G,
-                              int norm_kind, hipStream_t s);
+                              void* out, int out_dt, int64_t N, int64_t C, int64_t L,
+                              int32_t G, int norm_kind, hipStream_t s);
 
 }  // namespace c1g

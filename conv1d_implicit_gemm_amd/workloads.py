@@ -40,6 +40,7 @@ class Workload:
     pad_left: int = 0
     pad_right: int = 0
     dtype: str = "f32"            # element type of x and w: "f32" or "bf16"
+    out_dtype: str = "f32"        # element type of the output: "f32" or "bf16"
     norm: Optional[str] = "group"  # "group", "layer_channels" or None
     G: int = 1
     eps: float = 1e-5

@@ -23,8 +23,11 @@
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major, contiguous, in device memory (HBM of the
- *     current HIP device).  x and w are fp32 or bf16 (c1g_dtype); every other
- *     tensor, and every output, is fp32.
+ *     current HIP device).  x and w are fp32 or bf16 (c1g_dtype); y / out are
+ *     fp32 or bf16 (c1g_conv_desc.out_dtype); every other tensor (bias,
+ *     gamma, beta, bias2, mean, rstd) is fp32.  bf16 tensors hold the raw
+ *     16-bit patterns; bf16 outputs are the fp32 results rounded to nearest
+ *     even (accumulation, statistics and the affine always run in fp32).
  *   - Ownership: the caller allocates and frees every buffer, including the
  *     workspace; the library never allocates, frees or synchronises.  Outputs
  *     must not overlap inputs unless an entry point says so.
@@ -51,7 +54,7 @@
 extern "C" {
 #endif
 
-/* element type of x and w */
+/* element type of x and w, and of y / out */
 enum c1g_dtype { C1G_F32 = 0, C1G_BF16 = 1 };
 
 /* normalisation applied to the convolution output y */
@@ -90,6 +93,8 @@ typedef struct c1g_conv_desc {
   int32_t K, stride, dilation;
   int32_t pad_left, pad_right;
   int32_t dtype;               /* enum c1g_dtype of x and w */
+  int32_t out_dtype;           /* enum c1g_dtype of y (conv1d_forward) and out
+                                  (conv1d_gn_forward); 0 = fp32 */
 } c1g_conv_desc;
 
 /* What follows the convolution in conv1d_gn_forward. */
@@ -117,11 +122,11 @@ size_t c1g_conv1d_workspace_size(const c1g_conv_desc* d);
  *   x    [N, C_in, T]        fp32 or bf16, device
  *   w    [C_out, C_in, K]    same type as x, device
  *   bias [C_out] fp32 or NULL (no bias)
- *   y    [N, C_out, T_out] fp32, device, written completely
+ *   y    [N, C_out, T_out] of d->out_dtype, device, written completely
  *   ws   device scratch of ws_bytes >= c1g_conv1d_workspace_size(d)
  *        (may be NULL when that size is 0); contents are clobbered. */
 int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
-                   float* y, void* ws, size_t ws_bytes, void* stream);
+                   void* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes gn_stats needs. */
 size_t c1g_gn_stats_workspace_size(int64_t N, int64_t C, int64_t L, int32_t G);
@@ -144,6 +149,14 @@ int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const f
              const float* rstd, const float* gamma, const float* beta, float* out,
              void* stream);
 
+/* gn_apply on bf16 tensors (the same definition): y, out [N, C, L] bf16
+ * device (out may equal y), everything else as gn_apply; computed in fp32,
+ * out rounded to nearest even.  The apply pass of a bf16 output moves half
+ * the bytes of the fp32 one. */
+int gn_apply_bf16(int64_t N, int64_t C, int64_t L, int32_t G, const uint16_t* y,
+                  const float* mean, const float* rstd, const float* gamma, const float* beta,
+                  uint16_t* out, void* stream);
+
 /* Workspace bytes conv1d_gn_forward needs. */
 size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc* norm);
 
@@ -152,17 +165,21 @@ size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc*
  *   gamma, beta    [C_out] fp32 or NULL (1 and 0): the normalisation's affine
  *                  (ignored when norm == C1G_NORM_NONE)
  *   bias2          [C_out] fp32, required iff epilogue == C1G_EPI_ROWMIN_BIAS
- *   out            [N, C_out, T_out] fp32 device, written completely
+ *   out            [N, C_out, T_out] of d->out_dtype, device, written completely
  *   mean_out, rstd_out  optional fp32 device outputs ([N,G] for GroupNorm,
  *                  [N,T_out] for LayerNorm over channels), or NULL
  *   ws             device scratch of ws_bytes >= c1g_conv1d_gn_workspace_size
+ * A bf16 out: on the "split" route the conv stores y already rounded to bf16
+ * (its statistics come from the fp32 accumulators) and the normalisation
+ * runs in place on those values; the other routes round only the final
+ * value.
  * GroupNorm: z = (y - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c]
  *   ("Kimi-K2.6 l2_p35"); LayerNorm over channels: the same formula with the
  *   statistics of y[n,:,t]; row-min: out = min over channels of z at (n,t)
  *   plus bias2[c] ("Kimi-K2.6 l2_p75"). */
 int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const void* x,
                       const void* w, const float* bias, const float* gamma, const float* beta,
-                      const float* bias2, float* out, float* mean_out, float* rstd_out,
+                      const float* bias2, void* out, float* mean_out, float* rstd_out,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Name of the kernel route conv1d_gn_forward takes for these arguments, or

@@ -12,6 +12,9 @@ from conv1d_implicit_gemm_amd.workloads import Workload, make_inputs, to_f64_num
 DEV = "cuda:0"
 TOL_F32 = 1e-4   # max-abs after normalisation, fp32 inputs
 TOL_BF16 = 2e-2  # max-abs after normalisation, bf16 inputs
+# unit roundoff of bf16 (8 significant bits, round to nearest even): a bf16
+# output adds at most BF16_U * |value| per rounding
+BF16_U = 2.0 ** -8
 
 
 def announce(*what):
@@ -32,7 +35,9 @@ def run_library(wl: Workload, inp: dict, *, return_stats=False, poison=True):
     T_out = c1g.out_len(c1g.make_desc(wl.N, wl.C_in, wl.C_out, wl.T, wl.K, stride=wl.stride,
                                       dilation=wl.dilation, pad_left=wl.pad_left,
                                       pad_right=wl.pad_right))
-    out = torch.full((wl.N, wl.C_out, T_out), float("nan") if poison else 0.0, device=DEV)
+    odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    out = torch.full((wl.N, wl.C_out, T_out), float("nan") if poison else 0.0, device=DEV,
+                     dtype=odt)
     if wl.norm is None and not wl.rowmin_bias:
         c1g.conv1d_forward(x, w, b, stride=wl.stride, dilation=wl.dilation,
                            pad_left=wl.pad_left, pad_right=wl.pad_right, out=out)
@@ -69,13 +74,65 @@ def tol_for(wl: Workload):
     return TOL_BF16 if wl.dtype == "bf16" else TOL_F32
 
 
+def library_route(wl: Workload):
+    desc = c1g.make_desc(wl.N, wl.C_in, wl.C_out, wl.T, wl.K, stride=wl.stride,
+                         dilation=wl.dilation, pad_left=wl.pad_left, pad_right=wl.pad_right,
+                         dtype=c1g.C1G_BF16 if wl.dtype == "bf16" else c1g.C1G_F32,
+                         out_dtype=c1g.C1G_BF16 if wl.out_dtype == "bf16" else c1g.C1G_F32)
+    return c1g.route(desc, c1g.make_norm(wl.norm, wl.G, wl.eps, wl.rowmin_bias))
+
+
+def bf16_out_bound(wl: Workload, inp: dict, ref: dict):
+    """Per-element bound on |out - oracle| for a bf16 output, derived from
+    the arithmetic: the fp32-output tolerance tol, plus one rounding of the
+    final value (BF16_U * (|ref| + tol)); on the split route y is stored
+    rounded to bf16 before the normalisation reads it, which adds
+    BF16_U * |y| * rstd * |gamma| (for the row-min, the largest such term over
+    the channels of the position)."""
+    tol = tol_for(wl)
+    out = ref["out"]
+    bound = tol + BF16_U * (np.abs(out) + tol)
+    if library_route(wl) != "split":
+        return bound
+    y = np.abs(ref["y"])
+    N, C, L = y.shape
+    gam = np.ones(C) if inp["gamma"] is None else np.abs(to_f64_numpy(inp["gamma"]))
+    if wl.norm == "group":
+        rs = np.repeat(ref["rstd"], C // wl.G, axis=1)[:, :, None]       # [N, C, 1]
+        scale = rs * gam[None, :, None]
+    elif wl.norm == "layer_channels":
+        scale = ref["rstd"][:, None, :] * gam[None, :, None]               # [N, C, L]
+    else:
+        scale = np.ones((1, C, 1))
+    yterm = BF16_U * y * scale * (1 + 1e-3)
+    if wl.rowmin_bias:
+        yterm = np.broadcast_to(yterm.max(axis=1, keepdims=True), out.shape)
+    return bound + yterm
+
+
+def check_bf16_out(wl: Workload, got, inp: dict, ref: dict):
+    """Element-wise |got - ref| <= bf16_out_bound; returns the worst ratio."""
+    g = got.detach().to("cpu").to(torch.float64).numpy()
+    assert g.shape == ref["out"].shape, (g.shape, ref["out"].shape)
+    assert np.isfinite(g).all(), "non-finite output (unwritten element?)"
+    ratio = np.abs(g - ref["out"]) / bf16_out_bound(wl, inp, ref)
+    worst = float(ratio.max())
+    assert worst <= 1.0, "%s: error %.3g x its bound at %s" % (
+        wl.name, worst, np.unravel_index(int(ratio.argmax()), ratio.shape))
+    return worst
+
+
 def check_parity(wl: Workload, seed=0):
     announce(wl.name, wl, "seed", seed)
     inp = make_inputs(wl, seed)
     got, mean, rstd = run_library(wl, inp, return_stats=True)
     ref = run_oracle(wl, inp)
-    err = max_abs_err(got, ref["out"])
-    assert err <= tol_for(wl), "%s: max abs err %.3g > %.3g" % (wl.name, err, tol_for(wl))
+    if wl.out_dtype == "bf16":
+        assert got.dtype == torch.bfloat16
+        err = check_bf16_out(wl, got, inp, ref)
+    else:
+        err = max_abs_err(got, ref["out"])
+        assert err <= tol_for(wl), "%s: max abs err %.3g > %.3g" % (wl.name, err, tol_for(wl))
     if mean is not None and ref["mean"] is not None:
         em = max_abs_err(mean, ref["mean"])
         er = float(np.max(np.abs(rstd.cpu().double().numpy() - ref["rstd"]) / ref["rstd"]))

@@ -49,11 +49,11 @@ def test_out_len_matches_oracle(T, K, s, d, pl, pr):
 
 def _desc(**kw):
     base = dict(N=2, C_in=16, C_out=32, T=256, K=3, stride=1, dilation=1, pad_left=1,
-                pad_right=1, dtype=c1g.C1G_F32)
+                pad_right=1, dtype=c1g.C1G_F32, out_dtype=c1g.C1G_F32)
     base.update(kw)
     return c1g.ConvDesc(base["N"], base["C_in"], base["C_out"], base["T"], base["K"],
                         base["stride"], base["dilation"], base["pad_left"], base["pad_right"],
-                        base["dtype"])
+                        base["dtype"], base["out_dtype"])
 
 
 @pytest.mark.parametrize("kw", [dict(N=0), dict(C_in=0), dict(C_out=0), dict(T=0), dict(K=0),
@@ -75,6 +75,8 @@ def test_invalid_norm_args():
     assert c1g.check(d, c1g.NormDesc(7, 8, 1e-5, 0)) == 1
     assert c1g.check(d, c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 9)) == 1
     assert c1g.check(_desc(dtype=7)) == 2
+    assert c1g.check(_desc(out_dtype=7)) == 2
+    assert c1g.check(_desc(out_dtype=c1g.C1G_BF16)) == 0
 
 
 def test_routes():
@@ -166,3 +168,34 @@ def test_pointer_checks_fail_before_any_launch():
     assert lib.gn_stats(2, 32, 10, 8, 1e-5, odd, good, good, None, 0, None) == 4
     assert lib.gn_apply(2, 32, 10, 8, good, good, good, None, None, None, None) == 1
     assert lib.gn_apply(2, 32, 10, 8, good, odd, good, None, None, good, None) == 4
+    # bf16 outputs need 2-byte alignment only
+    odd1 = P(0x10001)
+    db = _desc(out_dtype=c1g.C1G_BF16)
+    assert lib.conv1d_forward(ctypes.byref(db), good, good, None, odd1, good, 1 << 30, None) == 4
+    assert lib.conv1d_gn_forward(ctypes.byref(db), ctypes.byref(gn), good, good, None, None,
+                                 None, None, odd1, None, None, good, 1 << 30, None) == 4
+    assert lib.gn_apply_bf16(2, 32, 10, 5, good, good, good, None, None, good, None) == 1
+    assert lib.gn_apply_bf16(2, 32, 10, 8, None, good, good, None, None, good, None) == 1
+    assert lib.gn_apply_bf16(2, 32, 10, 8, odd1, good, good, None, None, good, None) == 4
+    assert lib.gn_apply_bf16(2, 32, 10, 8, good, odd, good, None, None, good, None) == 4
+
+
+def test_bf16_output_workspace():
+    """A bf16 out adds an fp32 y to the workspace only where an unfused
+    epilogue follows the Linear-layer GEMM; elsewhere y lives in out."""
+    lin = dict(N=64, C_in=256, C_out=512, T=1, K=1, pad_left=0, pad_right=0, dtype=c1g.C1G_BF16)
+    f32, b16 = _desc(**lin), _desc(out_dtype=c1g.C1G_BF16, **lin)
+    unfused = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)    # 64 channels per group
+    fused = c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 1)     # 16 per group + row-min
+    assert c1g.route(b16, unfused) == "gemm_rows"
+    extra = c1g.conv1d_gn_workspace_size(b16, unfused) - c1g.conv1d_gn_workspace_size(f32, unfused)
+    assert 64 * 512 * 4 <= extra < 64 * 512 * 4 + 256
+    assert c1g.conv1d_gn_workspace_size(b16, fused) == c1g.conv1d_gn_workspace_size(f32, fused)
+    assert c1g.conv1d_workspace_size(b16) == c1g.conv1d_workspace_size(f32) == 0
+    conv = dict(N=2, C_in=64, C_out=128, T=300, K=5, dilation=2, pad_left=2, pad_right=2)
+    for dt in (c1g.C1G_F32, c1g.C1G_BF16):
+        a, b = _desc(dtype=dt, **conv), _desc(dtype=dt, out_dtype=c1g.C1G_BF16, **conv)
+        for nd in (c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0),     # 32 channels per group
+                   c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 1)):
+            assert c1g.route(a, nd) == c1g.route(b, nd) == "split"
+            assert c1g.conv1d_gn_workspace_size(a, nd) == c1g.conv1d_gn_workspace_size(b, nd)
