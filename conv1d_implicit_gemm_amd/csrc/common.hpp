@@ -29,8 +29,49 @@ __device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int mask) {
-  return __shfl_xor(v, mask, kWave);
+// Cross-lane exchanges that stay in the vector ALU (no LDS crossbar round
+// trip): DPP within rows of 16 lanes, and gfx950's permlane swaps across rows.
+// Every lane must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
+// (v of lane l, v of lane l ^ 16) and (v of lane l, v of lane l ^ 32), in
+// lane order within each pair (the lower lane's value first)
+__device__ __forceinline__ f32x2 pair16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Sum over the lanes whose indices differ only in the MASK bits; the low four
+// mask bits must be contiguous from bit 0 (the row reduction pairs quads, then
+// halves, then mirrored halves of a row).  Every lane of a group ends with the
+// same bits (each step adds the same two partial sums; a + b == b + a).
+template <int MASK>
+__device__ __forceinline__ float lane_sum(float v) {
+  static_assert(((MASK & 15) & ((MASK & 15) + 1)) == 0, "row bits contiguous from bit 0");
+  if (MASK & 1) v += dpp<kDppXor1>(v);
+  if (MASK & 2) v += dpp<kDppXor2>(v);
+  if (MASK & 4) v += dpp<kDppHalfMirror>(v);
+  if (MASK & 8) v += dpp<kDppMirror>(v);
+  if (MASK & 16) { const f32x2 p = pair16(v); v = p[0] + p[1]; }
+  if (MASK & 32) { const f32x2 p = pair32(v); v = p[0] + p[1]; }
+  return v;
+}
+// Minimum over lanes differing in bits 16 and 32 of the lane index.
+__device__ __forceinline__ float lane_min48(float v) {
+  f32x2 p = pair16(v);
+  v = fminf(p[0], p[1]);
+  p = pair32(v);
+  return fminf(p[0], p[1]);
 }
 
 // Running statistics of a set of values: count, mean and the sum of squared
@@ -52,15 +93,6 @@ __device__ __forceinline__ Stats stats_merge(Stats a, Stats b) {
   r.mean = a.mean + delta * fb;
   r.m2 = a.m2 + b.m2 + delta * delta * a.n * fb;
   return r;
-}
-
-// Exact-count sum over lanes whose indices differ only in the given mask bits.
-template <int MASK>
-__device__ __forceinline__ float xor_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1)
-    if (MASK & m) v += shfl_xor(v, m);
-  return v;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

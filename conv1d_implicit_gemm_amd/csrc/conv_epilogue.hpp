@@ -13,7 +13,7 @@
 //
 // Partial statistics are taken from the fp32 values, before any rounding of
 // the stored y.  Two passes over the registers (mean, then squared
-// deviations), xor-shuffle sums across lanes, then a fixed-order pairwise
+// deviations), cross-lane sums (DPP and lane swaps), then a fixed-order pairwise
 // merge across waves through LDS; every partial has one fixed slot (no
 // atomics), so the later merge is deterministic.
 //
@@ -98,8 +98,8 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
           const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
           if (t < T_out) { sum += acc[i][jn][r]; cnt += 1.f; }
         }
-      sum = xor_sum<48>(sum);
-      cnt = xor_sum<48>(cnt);
+      sum = lane_sum<48>(sum);
+      cnt = lane_sum<48>(cnt);
       const float mean = cnt > 0.f ? sum / cnt : 0.f;
       float m2 = 0.f;
 #pragma unroll
@@ -109,7 +109,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
           const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
           if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
         }
-      m2 = xor_sum<48>(m2);
+      m2 = lane_sum<48>(m2);
       if (active && kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
     }
     __syncthreads();
@@ -134,8 +134,8 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
           const int c = c0 + wn * WN * 16 + jn * 16 + lr;
           if (c < a.C_out) { sum += acc[i][jn][r]; cnt += 1.f; }
         }
-        sum = xor_sum<15>(sum);
-        cnt = xor_sum<15>(cnt);
+        sum = lane_sum<15>(sum);
+        cnt = lane_sum<15>(cnt);
         const float mean = cnt > 0.f ? sum / cnt : 0.f;
         float m2 = 0.f;
 #pragma unroll
@@ -143,7 +143,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
           const int c = c0 + wn * WN * 16 + jn * 16 + lr;
           if (c < a.C_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
         }
-        m2 = xor_sum<15>(m2);
+        m2 = lane_sum<15>(m2);
         const int tl = wm * WM * 16 + i * 16 + 4 * kq + r;
         if (active && lr == 0) red[wn * TM + tl] = Stats{cnt, mean, m2};
       }

@@ -138,13 +138,13 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
       if (full || t_lane + m * 16 + r < T_out) sum += acc[m][r];
   }
   // lanes of one group differ in the low log2(cpg) bits of lr and in kq
+  // (cpg is 1, 2, 4, 8 or 16: a group is an aligned run of lr values)
   auto group_reduce = [&](float v) {
-#pragma unroll
-    for (int msk = 1; msk < 16; msk <<= 1)
-      if (msk < cpg) v += shfl_xor(v, msk);
-    v += shfl_xor(v, 16);
-    v += shfl_xor(v, 32);
-    return v;
+    if (cpg > 1) v += dpp<kDppXor1>(v);
+    if (cpg > 2) v += dpp<kDppXor2>(v);
+    if (cpg > 4) v += dpp<kDppHalfMirror>(v);
+    if (cpg > 8) v += dpp<kDppMirror>(v);
+    return lane_sum<48>(v);
   };
   auto block_total = [&](float v) {
     v = group_reduce(v);
