@@ -196,6 +196,8 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
+    __builtin_amdgcn_sched_group_barrier(0x100, WM + WN, 0);  // all operand reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, WM * WN, 0);  // then the MFMAs
     __builtin_amdgcn_sched_barrier(0);  // one tap's operands live at a time
   };
   // every tap of the chunk; one tap body in a runtime loop keeps a single copy
