@@ -26,6 +26,8 @@ struct Plan {
   int n_chunks = 0, n_ttiles = 0, n_ctiles = 0, tm = 0, tn = 0;
   bool gemm_fused = false;  // R_GEMM: GroupNorm + row-min inside the GEMM epilogue
   size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, off_y = 0, total = 0;
+  size_t off_ximg = 0;  // bf16 conv: channels-last input image
+  int64_t T_img = 0;
 };
 
 constexpr size_t kAlign = 256;
@@ -112,7 +114,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   }
   p.route = conv_only ? R_CONV_ONLY : R_SPLIT;
 
-  size_t pack_bytes;
+  size_t pack_bytes, ximg_bytes = 0;
   if (p.bf16) {
     const int tm = conv_bf16_tile_m(d->stride, d->K, d->dilation);
     if (tm == 0) { p.status = C1G_ERR_UNSUPPORTED; return p; }
@@ -120,6 +122,13 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
     p.tn = ConvBf16Cfg::TN;
     p.n_chunks = (int)((d->C_in + ConvBf16Cfg::CK - 1) / ConvBf16Cfg::CK);
     pack_bytes = conv_bf16_packed_bytes(d->C_in, d->C_out, d->K);
+    p.T_img = conv_bf16_image_rows(p.T_out, d->stride, d->K, d->dilation);
+    // row offsets into the image are 32-bit within a tile's window
+    if ((int64_t)p.n_chunks * ConvBf16Cfg::CK * 2 * 1024 >= (1ll << 31)) {
+      p.status = C1G_ERR_UNSUPPORTED;
+      return p;
+    }
+    ximg_bytes = conv_bf16_image_bytes(d->N, d->C_in, p.T_img);
   } else {
     if (d->K > 8) { p.status = C1G_ERR_UNSUPPORTED; return p; }
     const int64_t xw = (int64_t)(ConvF32Cfg::TM - 1) * d->stride +
@@ -138,6 +147,9 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   size_t off = 0;
   p.off_pack = off;
   off = align_up(off + pack_bytes);
+  p.off_ximg = off;
+  off = align_up(off + ximg_bytes);
+  const size_t conv_bytes = off;  // what the convolution alone needs
   size_t part_bytes = 0, stat_elems = 0;
   if (want_gn) {
     part_bytes = (size_t)d->N * d->C_out * p.n_ttiles * 2 * sizeof(float);
@@ -152,7 +164,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   off = align_up(off + stat_elems * sizeof(float));
   p.off_rstd = off;
   off = align_up(off + stat_elems * sizeof(float));
-  p.total = (p.route == R_CONV_ONLY) ? align_up(pack_bytes) : off;
+  p.total = (p.route == R_CONV_ONLY) ? conv_bytes : off;
   return p;
 }
 
@@ -166,6 +178,8 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
   ConvArgs a;
   a.x = x;
   a.wp = ws + p.off_pack;
+  a.ximg = ws + p.off_ximg;
+  a.T_img = p.T_img;
   a.bias = bias;
   a.y = y;
   a.part = (float*)(ws + p.off_part);
@@ -186,6 +200,9 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
   if (p.bf16) {
     e = conv_bf16_pack((const uint16_t*)w, (uint16_t*)(ws + p.off_pack), d->C_in, d->C_out,
                        d->K, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    e = conv_bf16_pack_x((const uint16_t*)x, (uint16_t*)(ws + p.off_ximg), d->N, d->C_in, d->T,
+                         d->pad_left, p.T_img, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     return hip_status(conv_bf16_launch(a, epi, s));
   }

@@ -4,35 +4,36 @@
 // N = C_out, K = C_in*K): row m = (n, t), column = output channel c; the
 // reduction runs over (tap j, input channel ci) in chunks of 32 input channels,
 // one v_mfma_f32_16x16x32_bf16 K-step per tap.  The MFMA wants 8 consecutive
-// reduction values per lane, i.e. 8 consecutive input channels at one position,
-// while x is stored position-contiguous, so the input halo window of a tile is
-// transposed while it is staged: a lane loads an 8 (channels) x 8 (positions)
-// block with 16-byte loads along t, transposes it in registers and writes 8
-// rows of the LDS window Xt[t][ci].  Every tap then reads the same window at a
-// shifted row offset.  The weights are repacked once per call into the exact
-// LDS image of each (c-tile, chunk) and streamed with direct global->LDS loads.
+// reduction values per lane, i.e. 8 consecutive input channels at one
+// position, while x is stored position-contiguous.  So x is first repacked
+// into a channels-last image in the workspace: per sample, rows of padded
+// position tp = t + pad_left, each row the channels of one position padded to
+// whole chunks, zero outside the tensor (the padding and the tail of the last
+// tile are explicit zero rows).  A tile's input window is then a contiguous
+// run of image rows, and both operands reach LDS by direct global -> LDS
+// copies (global_load_lds, 16 bytes per lane, no registers).  Every tap reads
+// the same window at a shifted row offset; the weights are repacked once per
+// call into the exact LDS image of each (c-tile, chunk).
 //
 // LDS rows are 64 bytes (32 bf16) with no padding; the 16-byte column of a row
 // is XOR-ed with 2 when bit 2 of the row index is set.  The LDS has 64
 // four-byte banks and serves a 16-byte-per-lane read in four passes of 16
 // lanes (lanes 0-7 with 16-23, and so on), so an operand read of rows r..r+7
 // and two adjacent columns touches 16 distinct groups of 4 banks for any r
-// (unit stride); without the XOR, rows r and r+4 would collide.
+// (unit stride); without the XOR, rows r and r+4 would collide.  The copies
+// write whole 1 KB runs, so a lane fetches the logical column that lands at
+// its physical slot.
 //
 // Workgroup: 512 threads; tile TM (512 or 128) positions x 128 channels.  The
 // eight waves form a 4 x 2 grid of wave tiles of WM x 4 MFMA tiles (128 x 64
 // for TM = 512), each running every tap, so a wave reads 12 KB of operands per
-// 32 MFMAs and two waves per SIMD hide LDS latency.  The tile is tall because
-// the L2 -> LDS path moves ~40 bytes per clock per CU (measured, the same for
-// direct loads and for register staging): a 512-position tile stages 75 KB per
-// chunk for 21 MFLOP, where a 256-position one needs 58 KB for half the work.
-// Two LDS stages: the next chunk's weights stream in and its window is loaded
-// into registers while the current chunk is consumed; every wave takes a
-// share of the staging.  Window blocks go to lanes channel-group fastest, so
-// the 8 lanes of one 16-byte LDS write pass (32 banks, 8 consecutive lanes per
-// pass for writes) cover two rows and all four columns: a 2-way conflict, the
-// least possible for rows that share their index modulo 8.  Epilogue: shared with
-// the fp32 kernel (store y, GroupNorm or channel-LayerNorm partial statistics).
+// 32 MFMAs.  Two LDS stages, one barrier per chunk: the next chunk's copies
+// run while the current chunk is consumed.  Within a chunk a wave reads each
+// tap's fragments while the previous tap's MFMAs run (a fragment register is
+// reloaded as soon as its last MFMA has issued), and across chunks the last
+// tap's MFMAs run after the barrier while the next chunk's first tap is read.
+// Epilogue: shared with the fp32 kernel (store y, GroupNorm or channel-
+// LayerNorm partial statistics).
 #include "common.hpp"
 #include "conv_epilogue.hpp"
 #include "launch.hpp"
@@ -49,17 +50,12 @@ constexpr int WGN = 2;               // waves along c (TN = WGN * WN * 16)
 constexpr int WGM = 4;               // waves along t
 constexpr int NWAVE = WGM * WGN;
 constexpr int NTHR = NWAVE * 64;
-// LDS per workgroup: two stages of (window XC rows + weight image of the taps)
-// of 64-byte rows.  XC = 544 rows with up to 5 taps (150 KB), or 224 rows with
-// 6 to 8 taps on 128-position tiles (156 KB); gfx950 allows 160 KB.
+// LDS per workgroup: two stages of (window XR rows + weight image of the
+// taps) of 64-byte rows.  XR = 544 rows with up to 5 taps (150 KB), or 224
+// rows with 6 to 8 taps on 128-position tiles (156 KB); gfx950 allows 160 KB.
+// A window of XR rows is 16-row copies (1 KB each).
 constexpr int XCAP_WIDE = 544, XCAP_TAPS = 224;
-template <int XC>
-struct XGeom {
-  static constexpr int XTG = XC / 8;        // 8-position groups per window
-  static constexpr int XBLK = XTG * (CK / 8); // 8x8 blocks per window
-  static constexpr int XLANES = XBLK / NWAVE; // lanes per wave that stage one block each
-  static_assert(XBLK % NWAVE == 0 && XLANES <= 64, "window blocks spread over the waves");
-};
+static_assert(XCAP_WIDE % 16 == 0 && XCAP_TAPS % 16 == 0, "whole 16-row copies");
 static_assert(TN == 128, "weight rows keep bit 2 of c across taps");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -69,31 +65,30 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
 }
 
+// s_waitcnt vmcnt(0) lgkmcnt(0) as a compiler builtin (gfx9 encoding, expcnt
+// left at its maximum), so the compiler knows every copy and LDS access of
+// this wave has completed
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(7 << 4); }
+
+// Workgroup barrier without the waits of __syncthreads() (which would also
+// wait for the copies of the next chunk issued after it in program order):
+// the caller waits first for what the barrier must cover; the memory clobber
+// keeps the compiler from moving any memory access across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // 16-byte column swizzle of LDS row `row`
 __host__ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 2; }
 
-// 8x8 transpose of 16-bit values: in[r] holds row r (4 dwords, element 2k in
-// the low half of dword k); out[e] receives column e.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int k = e >> 1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t lo = in[2 * m][k], hi = in[2 * m + 1][k];
-      out[e][m] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-  }
-}
-
-template <int WM, int KT, bool FAST, int XC>
+template <int WM, int KT, int XR>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
-  constexpr int XLANES = XGeom<XC>::XLANES;
   // the weight stage also holds the epilogue's cross-wave merge (<= 12 KB)
   constexpr int WSK = KT < 2 ? 2 : KT;
   constexpr int TM = WGM * WM * 16;
-  __shared__ __attribute__((aligned(16))) u16 Xs0[XC * RW];
-  __shared__ __attribute__((aligned(16))) u16 Xs1[XC * RW];
+  constexpr int XP = XR / 16;                         // window copies per chunk
+  constexpr int NPIECE = XP + KT * 8;                 // window + weight copies
+  constexpr int PPW = (NPIECE + NWAVE - 1) / NWAVE;   // copies per wave per chunk
+  __shared__ __attribute__((aligned(16))) u16 Xs0[XR * RW];
+  __shared__ __attribute__((aligned(16))) u16 Xs1[XR * RW];
   __shared__ __attribute__((aligned(16))) u16 Ws0[WSK * TN * RW];
   __shared__ __attribute__((aligned(16))) u16 Ws1[WSK * TN * RW];
 
@@ -113,65 +108,40 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   const int64_t t0 = (int64_t)ttile * TM;
   const int c0 = ctile * TN;
   const int s = a.stride, d = a.dilation;
-  const int64_t T = a.T;
 
-  const u16* __restrict__ x = (const u16*)a.x;
-  const u16* __restrict__ wp = (const u16*)a.wp;
-  const u16* xn = x + n * a.C_in * T;
-
-  // window of this tile, aligned down to 8 positions (16 bytes)
-  const int64_t tbase = t0 * s - a.pad_left;
-  const int64_t tal = (tbase >= 0) ? (tbase & ~(int64_t)7) : -(((-tbase) + 7) & ~(int64_t)7);
-  const int shift = (int)(tbase - tal);
-
-  // ---- input window: lanes 0..XLANES-1 of every wave own one 8x8 block
-  // (8 positions of 8 channels), channel group fastest
-  const bool xown = lane < XLANES;
-  const int blk = wave * XLANES + (xown ? lane : 0);
-  const int tg = blk >> 2, cg = blk & 3;
-  const int64_t tx = tal + 8 * tg;
-  u32x4 xr[8];
-  auto fetch_x = [&](int chunk) __attribute__((always_inline)) {
-    const int64_t ci0 = (int64_t)chunk * CK + 8 * cg;
+  // ---- copies of one chunk: pieces 0..XP-1 are 16-row runs of the window,
+  // XP.. the weight image (KT*8 runs of 16 rows); piece = wave + NWAVE * p.
+  // Every wave issues PPW copies per chunk (surplus slots repeat the last
+  // piece, writing the same bytes again).
+  const int64_t row_bytes = (int64_t)a.n_chunks * CK * 2;  // one image row
+  const char* const xwin = (const char*)a.ximg + (n * a.T_img + t0 * s) * row_bytes;
+  const char* const wimg =
+      (const char*)a.wp + (int64_t)ctile * a.n_chunks * (KT * TN * RW * 2);
+  uint32_t soff[PPW];  // byte offset of this lane's 16 bytes within chunk 0
+  int dst[PPW];        // byte offset of the copy within its stage buffer
+  bool isx[PPW];       // window (else weight) copy; uniform over the wave
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t ci = ci0 + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (xown && ci < a.C_in) {
-        const u16* src = xn + ci * T;
-        if (FAST) {
-          // T % 8 == 0 and the group is 8-aligned: wholly inside or outside
-          if (tx >= 0 && tx < T) v = *(const u32x4*)(src + tx);
-        } else {
-          u16 e8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) e8[e] = (tx + e >= 0 && tx + e < T) ? src[tx + e] : (u16)0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = (uint32_t)e8[2 * k] | ((uint32_t)e8[2 * k + 1] << 16);
-        }
-      }
-      xr[r] = v;
+  for (int p = 0; p < PPW; ++p) {
+    int piece = wave + NWAVE * p;
+    if (piece >= NPIECE) piece = NPIECE - 1;
+    isx[p] = piece < XP;
+    if (isx[p]) {
+      const int row = 16 * piece + (lane >> 2);
+      const int q = (lane & 3) ^ swz(row);  // logical column landing at slot lane % 4
+      soff[p] = (uint32_t)(row * row_bytes + 16 * q);
+      dst[p] = piece * 1024;
+    } else {
+      soff[p] = (uint32_t)((piece - XP) * 1024 + lane * 16);
+      dst[p] = (piece - XP) * 1024;
     }
-  };
-  auto stash_x = [&](u16* xs) __attribute__((always_inline)) {
-    if (xown) {
-      u32x4 tr[8];
-      transpose8x8(xr, tr);
+  }
+  auto stage = [&](int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = 8 * tg + e;
-        *(u32x4*)(xs + row * RW + 8 * (cg ^ swz(row))) = tr[e];
-      }
-    }
-  };
-  // ---- weights: direct copy of the packed LDS image of (ctile, chunk),
-  // KT * 8 pieces of 1 KB spread over the waves
-  auto dma_w = [&](int chunk, u16* ws) __attribute__((always_inline)) {
-    const char* src = (const char*)(wp + ((int64_t)ctile * a.n_chunks + chunk) * (int64_t)(KT * TN * RW));
-#pragma unroll
-    for (int p = 0; p < (KT * 8 + NWAVE - 1) / NWAVE; ++p) {
-      const int piece = wave + NWAVE * p;
-      if (piece < KT * 8) dma16(src + piece * 1024 + lane * 16, (char*)ws + piece * 1024);
+    for (int p = 0; p < PPW; ++p) {
+      if (isx[p])
+        dma16(xwin + (int64_t)chunk * (CK * 2) + soff[p], (char*)xs + dst[p]);
+      else
+        dma16(wimg + (int64_t)chunk * (KT * TN * RW * 2) + soff[p], (char*)ws + dst[p]);
     }
   };
 
@@ -181,61 +151,104 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int arow0 = (wm * WM * 16 + lr) * s + shift;  // window row of subtile 0, tap 0
-  const int bcol = 8 * (kq ^ swz(lr));                // weight rows: bit 2 of c = bit 2 of lr
-  auto tap = [&](const u16* xs, const u16* ws, int j) __attribute__((always_inline)) {
-    const int r0 = arow0 + j * d;                       // rows r0 + 16*s*i keep bit 2
-    const u16* xa = xs + r0 * RW + 8 * (kq ^ swz(r0));
-    const u16* wb = ws + (j * TN + wn * WN * 16 + lr) * RW + bcol;
-    bf16x8 av[WM], bv[WN];
+  // Operand fragments of one tap: A = 16 output positions x 32 channels
+  // (window rows (t - t0) * s + j * d), B = 32 channels x 16 output channels.
+  const int arow0 = (wm * WM * 16 + lr) * s;
+  const int bcol = 8 * (kq ^ swz(lr));  // weight rows: bit 2 of c = bit 2 of lr
+  bf16x8 av[WM], bv[WN];
+  auto xa_of = [&](const u16* xs, int j) __attribute__((always_inline)) {
+    const int r0 = arow0 + j * d;  // rows r0 + 16*s*i keep bit 2
+    return xs + r0 * RW + 8 * (kq ^ swz(r0));
+  };
+  auto wb_of = [&](const u16* ws, int j) __attribute__((always_inline)) {
+    return ws + (j * TN + wn * WN * 16 + lr) * RW + bcol;
+  };
+  auto read_tap = [&](const u16* xs, const u16* ws, int j) __attribute__((always_inline)) {
+    const u16* xa = xa_of(xs, j);
+    const u16* wb = wb_of(ws, j);
 #pragma unroll
     for (int jn = 0; jn < WN; ++jn) bv[jn] = *(const bf16x8*)(wb + jn * 16 * RW);
 #pragma unroll
     for (int i = 0; i < WM; ++i) av[i] = *(const bf16x8*)(xa + i * 16 * s * RW);
+  };
+  // The MFMAs of the tap whose fragments are in av/bv, each fragment replaced
+  // by its counterpart of tap j of (xs, ws) as soon as its last MFMA has
+  // issued (A row by row, then B within the last row).
+  auto mfma_reload = [&](const u16* xs, const u16* ws, int j) __attribute__((always_inline)) {
+    const u16* xa = xa_of(xs, j);
+    const u16* wb = wb_of(ws, j);
+#pragma unroll
+    for (int i = 0; i < WM - 1; ++i) {
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
+      av[i] = *(const bf16x8*)(xa + i * 16 * s * RW);
+    }
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      acc[WM - 1][jn] = mfma16x16x32bf16(av[WM - 1], bv[jn], acc[WM - 1][jn]);
+      bv[jn] = *(const bf16x8*)(wb + jn * 16 * RW);
+    }
+    av[WM - 1] = *(const bf16x8*)(xa + (WM - 1) * 16 * s * RW);
+#pragma unroll
+    for (int i = 0; i < WM - 1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mfma_only = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
-    __builtin_amdgcn_sched_group_barrier(0x100, WM + WN, 0);  // all operand reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, WM * WN, 0);  // then the MFMAs
-    __builtin_amdgcn_sched_barrier(0);  // one tap's operands live at a time
   };
-  // every tap of the chunk; one tap body in a runtime loop keeps a single copy
-  // of it in registers
-  auto compute = [&](const u16* xs, const u16* ws) __attribute__((always_inline)) {
+  // the MFMAs of taps 0..KT-2 of the chunk in (xs, ws) (tap 0's fragments
+  // already loaded), reading taps 1..KT-1 behind them; a runtime loop keeps
+  // one copy of the body
+  auto taps = [&](const u16* xs, const u16* ws) __attribute__((always_inline)) {
 #pragma nounroll
-    for (int j = 0; j < KT; ++j) tap(xs, ws, j);
+    for (int j = 1; j < KT; ++j) mfma_reload(xs, ws, j);
   };
 
-  // Pairs of chunks per iteration, loads clamped to the last chunk and issued
-  // unconditionally (surplus copies land in a stage nobody reads again), so
-  // the loop body is one block; every load of a chunk completes before the
-  // barrier that ends the half in which it was issued.
+  // Pairs of chunks per iteration.  Copies run unconditionally on chunk
+  // indices clamped to the last chunk (surplus copies land in a stage nobody
+  // reads again), so the loop body is one block.  Before each barrier every
+  // wave waits for all its copies: those of the next chunk, issued one chunk
+  // earlier.
   const int n_chunks = a.n_chunks, last = n_chunks - 1;
   auto cl = [&](int c) { return c < last ? c : last; };
-  dma_w(0, Ws0);
-  fetch_x(0);
-  stash_x(Xs0);
-  __syncthreads();
+  stage(0, Xs0, Ws0);
+  wait_all_mem();
+  lds_barrier();
+  stage(cl(1), Xs1, Ws1);
+  read_tap(Xs0, Ws0, 0);
   int c = 0;
   for (; c + 1 < n_chunks; c += 2) {
-    // stage 0 holds chunk c
-    dma_w(c + 1, Ws1);
-    fetch_x(c + 1);
-    compute(Xs0, Ws0);
-    stash_x(Xs1);
-    __syncthreads();
-    // stage 1 holds chunk c+1
-    dma_w(cl(c + 2), Ws0);
-    fetch_x(cl(c + 2));
-    compute(Xs1, Ws1);
-    stash_x(Xs0);
-    __syncthreads();
+    // stage 0 holds chunk c, its tap 0 in the fragments; stage 1 is loading c+1
+    taps(Xs0, Ws0);
+    wait_all_mem();
+    lds_barrier();
+    stage(cl(c + 2), Xs0, Ws0);
+    mfma_reload(Xs1, Ws1, 0);  // chunk c's last tap; chunk c+1's tap 0
+    // stage 1 holds chunk c+1; stage 0 is loading c+2
+    taps(Xs1, Ws1);
+    wait_all_mem();
+    lds_barrier();
+    stage(cl(c + 3), Xs1, Ws1);
+    mfma_reload(Xs0, Ws0, 0);
   }
   if (c < n_chunks) {  // odd count: the last chunk is in stage 0
-    compute(Xs0, Ws0);
-    __syncthreads();
+    taps(Xs0, Ws0);
+    mfma_only();
   }
+  wait_all_mem();  // surplus copies land before the epilogue reuses the LDS
+  __syncthreads();
 
   conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
 }
@@ -265,14 +278,72 @@ __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict
   wp[idx] = (co < C_out && ci < C_in) ? w[(co * C_in + ci) * K + j] : (u16)0;
 }
 
-template <int WM, int KT, int XC>
+// 8x8 transpose of 16-bit values: in[r] holds row r (4 dwords, element 2k in
+// the low half of dword k); out[e] receives column e.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = e >> 1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t lo = in[2 * m][k], hi = in[2 * m + 1][k];
+      out[e][m] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+  }
+}
+
+// Input image: ximg[n][tp][cp] = x[n][cp][tp - pad_left] for 0 <= tp - pad_left
+// < T and cp < C_in, else 0; rows of cpad = n_chunks * 32 channels, T_img rows
+// per sample.  A lane moves one 8 (channels) x 8 (positions) block: eight
+// 16-byte loads along t, a register transpose, eight 16-byte stores along the
+// channels.  Lane l of a wave takes channel group l % 8 and position group
+// l / 8 of a 64 x 64 tile, so both the loads (8 lanes per channel row) and the
+// stores (8 lanes per image row) come in 128-byte runs.  The tile's input
+// positions start at a multiple of 8 (t0 = 64 * bx - A, A = pad_left rounded
+// up to 8), so in-range blocks load with aligned 16-byte loads when T % 8 == 0.
+__global__ __launch_bounds__(256) void conv_bf16_pack_x_kernel(const u16* __restrict__ x,
+                                                              u16* __restrict__ ximg,
+                                                              int64_t C_in, int64_t T,
+                                                              int64_t cpad, int64_t T_img,
+                                                              int pad_left, int64_t A,
+                                                              int fast) {
+  const int64_t n = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t ci0 = (int64_t)blockIdx.y * 256 + 64 * wave + 8 * (lane & 7);
+  const int64_t tb = (int64_t)blockIdx.x * 64 - A + 8 * (lane >> 3);
+  if (ci0 >= cpad) return;
+  u32x4 in[8], out[8];
+  const bool vec = fast && tb >= 0 && tb + 8 <= T;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int64_t ci = ci0 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ci < C_in) {
+      const u16* src = x + (n * C_in + ci) * T;
+      if (vec) {
+        v = *(const u32x4*)(src + tb);
+      } else {
+        u16 e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = (tb + e >= 0 && tb + e < T) ? src[tb + e] : (u16)0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (uint32_t)e8[2 * k] | ((uint32_t)e8[2 * k + 1] << 16);
+      }
+    }
+    in[r] = v;
+  }
+  transpose8x8(in, out);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t tp = tb + e + pad_left;
+    if (tp >= 0 && tp < T_img) *(u32x4*)(ximg + (n * T_img + tp) * cpad + ci0) = out[e];
+  }
+}
+
+template <int WM, int KT, int XR>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
-  const bool fast = (a.T % 8 == 0) && ((((uintptr_t)a.x) & 15) == 0);
-  if (fast)
-    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, true, XC>), grid, dim3(NTHR), 0, st, a, epi);
-  else
-    hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, false, XC>), grid, dim3(NTHR), 0, st, a, epi);
+  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR>), grid, dim3(NTHR), 0, st, a, epi);
   return hipGetLastError();
 }
 
@@ -295,10 +366,12 @@ hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st) {
   }
 }
 
-// window (incl. the 8-position alignment shift) a TM-position tile needs
+// input rows a TM-position tile needs
 int64_t window(int tm, int stride, int K, int dilation) {
-  return (int64_t)(tm - 1) * stride + (int64_t)(K - 1) * dilation + 1 + 7;
+  return (int64_t)(tm - 1) * stride + (int64_t)(K - 1) * dilation + 1;
 }
+
+int xcap_of(int tm, int K) { return (tm == 128 && K > 5) ? XCAP_TAPS : XCAP_WIDE; }
 
 }  // namespace
 
@@ -307,6 +380,19 @@ int conv_bf16_tile_m(int stride, int K, int dilation) {
   if (K <= 5 && window(512, stride, K, dilation) <= XCAP_WIDE) return 512;
   if (window(128, stride, K, dilation) <= (K <= 5 ? XCAP_WIDE : XCAP_TAPS)) return 128;
   return 0;
+}
+
+int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation) {
+  const int tm = conv_bf16_tile_m(stride, K, dilation);
+  if (tm == 0) return 0;
+  const int64_t n_tt = (T_out + tm - 1) / tm;
+  // the last tile copies XR rows from its first input row
+  return (n_tt - 1) * tm * stride + xcap_of(tm, K);
+}
+
+size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img) {
+  const int64_t cpad = (C_in + CK - 1) / CK * CK;
+  return (size_t)(N * T_img * cpad) * sizeof(u16);
 }
 
 size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K) {
@@ -321,6 +407,19 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(conv_bf16_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, wp, C_in,
                      C_out, K, n_chunks, total);
+  return hipGetLastError();
+}
+
+hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_t C_in,
+                            int64_t T, int pad_left, int64_t T_img, hipStream_t s) {
+  const int64_t cpad = (C_in + CK - 1) / CK * CK;
+  const int64_t A = (pad_left + 7) / 8 * 8;  // first input position of tile 0: -A
+  const int fast = (T % 8 == 0) && ((((uintptr_t)x) & 15) == 0);
+  // tiles of 64 positions cover input positions -A .. T_img - 1 - pad_left
+  dim3 grid((unsigned)((T_img - pad_left + A + 63) / 64), (unsigned)((cpad + 255) / 256),
+            (unsigned)N);
+  hipLaunchKernelGGL(conv_bf16_pack_x_kernel, grid, dim3(256), 0, s, x, ximg, C_in, T, cpad,
+                     T_img, pad_left, A, fast);
   return hipGetLastError();
 }
 

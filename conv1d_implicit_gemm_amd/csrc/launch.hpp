@@ -20,6 +20,8 @@ enum ConvEpi : int {
 struct ConvArgs {
   const void* x;       // [N, C_in, T] fp32 or bf16
   const void* wp;      // packed weights (layout owned by the kernel file)
+  const void* ximg;    // bf16: channels-last input image (conv_bf16_pack_x)
+  int64_t T_img;       // bf16: rows per sample of the input image
   const float* bias;   // [C_out] or nullptr
   void* y;             // [N, C_out, T_out], fp32 or (y_bf16) bf16
   float* part;         // partial statistics (EPI_GN_PART / EPI_LN_PART), from fp32 values
@@ -44,12 +46,17 @@ hipError_t conv_f32_pack(const float* w, float* wp, int64_t C_in, int64_t C_out,
 hipError_t conv_f32_launch(const ConvArgs& a, int epi, hipStream_t s);
 
 // ---- bf16 split-path convolution (k_conv_bf16.hip)
-// Tile: TM (256 or 64, chosen from stride/K/dilation) positions x TN channels,
-// CK input channels per chunk; taps K <= 5.
+// Tile: TM (512 or 128, chosen from stride/K/dilation) positions x TN
+// channels, CK input channels per chunk; taps K <= 8.
 struct ConvBf16Cfg {
   static constexpr int TN = 128, CK = 32;
 };
 int conv_bf16_tile_m(int stride, int K, int dilation);  // 0 if unsupported
+// channels-last input image: rows per sample, bytes, and the repack of x
+int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation);
+size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img);
+hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_t C_in,
+                            int64_t T, int pad_left, int64_t T_img, hipStream_t s);
 size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K);
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
                           hipStream_t s);

@@ -122,12 +122,16 @@ def test_unsupported_sizes():
     # bf16 convolution: up to 8 taps (6..8 on 128-position tiles), not 9
     assert c1g.check(_desc(K=8, pad_left=3, pad_right=4, dtype=c1g.C1G_BF16)) == 0
     assert c1g.check(_desc(K=9, pad_left=4, pad_right=4, dtype=c1g.C1G_BF16)) == 2
-    # bf16, 8 taps: the window of a 128-position tile, 127 + 7*dilation + 1 rows
-    # plus up to 7 of alignment, must fit 224 rows
-    assert c1g.check(_desc(K=8, dilation=12, pad_left=0, pad_right=0, T=4096,
-                           dtype=c1g.C1G_BF16)) == 0
+    # bf16, 8 taps: the window of a 128-position tile, 127 + 7*dilation + 1
+    # input rows, must fit 224 rows
     assert c1g.check(_desc(K=8, dilation=13, pad_left=0, pad_right=0, T=4096,
+                           dtype=c1g.C1G_BF16)) == 0
+    assert c1g.check(_desc(K=8, dilation=14, pad_left=0, pad_right=0, T=4096,
                            dtype=c1g.C1G_BF16)) == 2
+    # bf16, 5 taps on a 512-position tile: 511 + 4*dilation + 1 <= 544 rows,
+    # else the 128-position tile
+    assert c1g.check(_desc(K=5, dilation=8, T=8192, dtype=c1g.C1G_BF16)) == 0
+    assert c1g.check(_desc(K=5, dilation=9, T=8192, dtype=c1g.C1G_BF16)) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -40,6 +40,12 @@ CONV_CASES = [
       pad_left=12, G=8, **BF),
     W("bf16_conv_ln_k6", N=1, C_in=64, C_out=130, T=200, K=6, pad_left=2, pad_right=3,
       norm="layer_channels", **BF),
+    # the widest windows: 8 taps at dilation 13 (219 of 224 rows on a
+    # 128-position tile); 5 taps at dilation 9 (too wide for 512 positions)
+    W("bf16_conv_gn_k8d13_widest", N=1, C_in=40, C_out=64, T=300, K=8, dilation=13,
+      pad_left=45, pad_right=46, G=4, **BF),
+    W("bf16_conv_gn_k5d9_small_tile", N=1, C_in=32, C_out=128, T=700, K=5, dilation=9,
+      pad_left=18, pad_right=18, G=8, **BF),
 ]
 
 
