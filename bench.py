@@ -196,21 +196,10 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
     # the dominant kernel's duration: on the single-pass route one step is one
-    # launch, timed per launch with events on the same stream
-    kern_ms = None
-    if op.route == "fused_single_pass":
-        n = min(args.steps, 100)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        torch.cuda.synchronize()
-        for a, b in evs:
-            a.record(stream)
-            op()
-            b.record(stream)
-        torch.cuda.synchronize()
-        kern_ms = sum(a.elapsed_time(b) for a, b in evs) / n
-    else:
-        kern_ms = ms_per_step
+    # launch, so the events around the K back-to-back steps on the launch
+    # stream time that kernel (kernel time plus the launch-to-launch gap); on
+    # the multi-kernel routes the same figure is the whole step
+    kern_ms = ms_per_step
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     bound, peak, unit = PEAKS[wl.dtype]

@@ -235,19 +235,28 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
   const float* xn = a.x + n * a.C_in * T;
   constexpr int K = KT;
 
-  // zero the padding slots of both window stages and, for a partial channel
-  // block, the weight entries of channels past C_out; loads never touch them
-  for (int e = tid; e < 2 * CK * Gm::XQ; e += NTHR) {
-    const int b = e / (CK * Gm::XQ), rq = e - b * (CK * Gm::XQ);
-    const int r = rq / Gm::XQ, q = rq - r * Gm::XQ;
-    const int64_t t = tal + 4 * q;
-    if (!(t >= 0 && t + 3 < T))
-      *(f32x4*)((b ? Xs1 : Xs0) + r * Gm::XS + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-  for (int e = tid; e < 2 * K * CK * CB; e += NTHR) {
-    const int b = e / (K * CK * CB), p = e - b * (K * CK * CB);
-    if (cbase + (p & (CB - 1)) >= a.C_out) (b ? Ws1 : Ws0)[p] = 0.f;
-  }
+  // Zero the padding slots of both window stages (slots q < qlo and q >= qhi
+  // of every row hold positions outside [0, T)) and, for a partial channel
+  // block, the weight entries of channels past C_out.  The copies never touch
+  // these slots, so the zero fill runs while the first chunk's copies land.
+  auto zero_fill = [&]() {
+    const int64_t qlo64 = (-tal + 3) / 4;  // first slot with t >= 0 (tal <= 0)
+    const int qlo = (int)(qlo64 < Gm::XQ ? qlo64 : Gm::XQ);
+    const int64_t qhi64 = (T - tal) / 4;   // first slot with t + 3 >= T
+    const int qhi = (int)(qhi64 < qlo ? qlo : (qhi64 < Gm::XQ ? qhi64 : Gm::XQ));
+    const int npad = qlo + (Gm::XQ - qhi);  // padding slots per row
+    for (int e = tid; e < 2 * CK * npad; e += NTHR) {
+      const int row = e / npad, k = e - row * npad;  // row: stage * CK + channel
+      const int q = k < qlo ? k : qhi + (k - qlo);
+      float* xs = row < CK ? Xs0 : Xs1;
+      *(f32x4*)(xs + (row % CK) * Gm::XS + 4 * q) = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    if (cbase + CB > a.C_out)
+      for (int e = tid; e < 2 * K * CK * CB; e += NTHR) {
+        const int b = e / (K * CK * CB), p = e - b * (K * CK * CB);
+        if (cbase + (p & (CB - 1)) >= a.C_out) (b ? Ws1 : Ws0)[p] = 0.f;
+      }
+  };
 
   // issue the direct loads of one chunk into a stage (window rows wave,
   // wave + NW, ...; weight instructions wave, wave + NW, ...)
@@ -287,8 +296,8 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
   const int abase = kq * Gm::XS + shift + wave * MQ * 16 + lr;  // stride 1
   const int bbase = kq * CB + lr;
 
-  __syncthreads();  // zero fill done before the first loads land
   stage(0, Xs0, Ws0);
+  zero_fill();
   __syncthreads();
   for (int c = 0; c < n_chunks; c += 2) {
     if (c + 1 < n_chunks) stage(c + 1, Xs1, Ws1);
