@@ -14,7 +14,11 @@ using namespace c1g;
 
 namespace {
 
-enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT, R_GEMM };
+enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT, R_GEMM, R_PERSIST };
+
+// Workgroups of the bf16 conv that one full MI355X keeps resident at once
+// (one per compute unit); the persistent route needs a sample's tiles to fit.
+constexpr int64_t kResidentTiles = 256;
 
 struct Plan {
   int status = C1G_OK;
@@ -27,6 +31,7 @@ struct Plan {
   bool gemm_fused = false;  // R_GEMM: GroupNorm + row-min inside the GEMM epilogue
   size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, off_y = 0, total = 0;
   size_t off_ximg = 0;  // bf16 conv: channels-last input image
+  size_t off_sync = 0;  // persistent route: per-round arrival counters
   int64_t T_img = 0;
 };
 
@@ -143,6 +148,14 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   if (n_tt > (1ll << 31) - 1 || n_ct > 65535) { p.status = C1G_ERR_UNSUPPORTED; return p; }
   p.n_ttiles = (int)n_tt;
   p.n_ctiles = (int)n_ct;
+  // bf16 GroupNorm (groups that tile the 128-channel tiles) or channel
+  // LayerNorm without the row-min: normalise inside the persistent conv
+  if (p.bf16 && (want_gn || want_ln) && p.epi == C1G_EPI_NONE &&
+      !(nd->flags & C1G_FLAG_NO_PERSISTENT) && n_tt * n_ct <= kResidentTiles) {
+    const int64_t tn = ConvBf16Cfg::TN;
+    const int64_t cpg = want_gn ? d->C_out / nd->G : tn;
+    if (tn % cpg == 0 || cpg % tn == 0) p.route = R_PERSIST;
+  }
 
   size_t off = 0;
   p.off_pack = off;
@@ -164,6 +177,8 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   off = align_up(off + stat_elems * sizeof(float));
   p.off_rstd = off;
   off = align_up(off + stat_elems * sizeof(float));
+  p.off_sync = off;  // rounds * samples-per-round counters + 1 fault word (<= 2N + 1)
+  if (p.route == R_PERSIST) off = align_up(off + (size_t)(2 * d->N + 2) * sizeof(unsigned));
   p.total = (p.route == R_CONV_ONLY) ? conv_bytes : off;
   return p;
 }
@@ -172,10 +187,9 @@ bool aligned(const void* p, size_t a) { return (((uintptr_t)p) % a) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? C1G_OK : C1G_ERR_HIP; }
 
-// Convolution into y (with the requested statistics epilogue); packs weights first.
-int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w,
-             const float* bias, void* y, char* ws, int epi, hipStream_t s) {
-  ConvArgs a;
+ConvArgs conv_args(const Plan& p, const c1g_conv_desc* d, const void* x, const float* bias,
+                   void* y, char* ws) {
+  ConvArgs a = {};
   a.x = x;
   a.wp = ws + p.off_pack;
   a.ximg = ws + p.off_ximg;
@@ -196,6 +210,17 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
   a.n_ttiles = p.n_ttiles;
   a.n_ctiles = p.n_ctiles;
   a.y_bf16 = p.out_bf16;
+  return a;
+}
+
+// Convolution into y (with the requested statistics epilogue); packs weights
+// (and, for bf16, the input image) first.  norm: the persistent route's
+// normalisation (epi EPI_GN_FUSED / EPI_LN_FUSED), else nullptr.
+int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w,
+             const float* bias, void* y, char* ws, int epi, hipStream_t s,
+             const c1g_norm_desc* nd = nullptr, const float* gamma = nullptr,
+             const float* beta = nullptr, float* mean_out = nullptr, float* rstd_out = nullptr) {
+  ConvArgs a = conv_args(p, d, x, bias, y, ws);
   hipError_t e;
   if (p.bf16) {
     e = conv_bf16_pack((const uint16_t*)w, (uint16_t*)(ws + p.off_pack), d->C_in, d->C_out,
@@ -204,6 +229,16 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
     e = conv_bf16_pack_x((const uint16_t*)x, (uint16_t*)(ws + p.off_ximg), d->N, d->C_in, d->T,
                          d->pad_left, p.T_img, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
+    if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
+      a.gamma = gamma;
+      a.beta = beta;
+      a.mean_out = mean_out;
+      a.rstd_out = rstd_out;
+      a.eps = nd->eps;
+      a.G = nd->G;
+      a.sync = (unsigned*)(ws + p.off_sync);
+      return hip_status(conv_bf16_fused_launch(a, epi, s));
+    }
     return hip_status(conv_bf16_launch(a, epi, s));
   }
   e = conv_f32_pack((const float*)w, (float*)(ws + p.off_pack), d->C_in, d->C_out, d->K, s);
@@ -282,6 +317,7 @@ const char* route_name(int r) {
     case R_FUSED: return "fused_single_pass";
     case R_SPLIT: return "split";
     case R_GEMM: return "gemm_rows";
+    case R_PERSIST: return "fused_persistent";
     default: return "invalid";
   }
 }
@@ -425,6 +461,15 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
     return run_gemm(p, d, nd, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, wsb, s);
   if (p.route == R_CONV_ONLY)
     return run_conv(p, d, x, w, bias, out, wsb, EPI_STORE, s);
+
+  // persistent route: the conv kernel normalises in registers and writes out
+  // once; on a device that cannot keep a sample's tiles resident together
+  // (a partitioned GPU) the split route runs instead, in the same workspace
+  if (p.route == R_PERSIST &&
+      conv_bf16_fused_capacity(d->stride, d->K, d->dilation) >= p.n_ttiles * p.n_ctiles)
+    return run_conv(p, d, x, w, bias, out, wsb,
+                    p.norm == C1G_NORM_GROUP ? EPI_GN_FUSED : EPI_LN_FUSED, s, nd, gamma, beta,
+                    mean_out, rstd_out);
 
   // split route: conv (+ partial statistics from the fp32 accumulators) into
   // out in out's type, merge, then in-place passes

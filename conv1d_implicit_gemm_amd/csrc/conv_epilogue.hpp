@@ -19,12 +19,32 @@
 //
 // Waves with active == false (extra waves of a workgroup whose results were
 // already folded into the active ones) store nothing but reach every barrier.
+// With store_y == false only the bias is added and the partials written (the
+// persistent kernel normalises the registers afterwards).
 #pragma once
 
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace c1g {
+
+// A partial (mean, M2) pair.  coherent: written as one device-scope atomic
+// 64-bit store, which goes to the point of coherence of all XCDs (the
+// persistent kernel's workgroups on other XCDs read it right after a barrier,
+// with no cache-wide flush in between).
+__device__ __forceinline__ void store_partial(float* p, float mean, float m2, bool coherent) {
+  if (coherent) {
+    const uint64_t bits = (uint64_t)__float_as_uint(mean) | ((uint64_t)__float_as_uint(m2) << 32);
+    __hip_atomic_store((uint64_t*)p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *(f32x2*)p = f32x2{mean, m2};
+  }
+}
+__device__ __forceinline__ f32x2 load_partial_coherent(const float* p) {
+  const uint64_t bits = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2{__uint_as_float((uint32_t)bits), __uint_as_float((uint32_t)(bits >> 32))};
+}
 
 // y = acc (bias already added) in the output type TO (float, or bf16 bits);
 // four consecutive positions of one channel per lane and tile.
@@ -59,7 +79,9 @@ template <int WM, int WN, int WGM, int WGN>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
                                               f32x4 (&acc)[WM][WN], int64_t n, int64_t t0,
                                               int c0, int ttile, int ctile, int wm, int wn,
-                                              Stats* red, bool active = true) {
+                                              Stats* red, bool active = true,
+                                              bool store_y = true) {
+  const bool coherent = !store_y;  // the persistent kernel's partials
   constexpr int TM = WGM * WM * 16, TN = WGN * WN * 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,7 +99,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
   for (int jn = 0; jn < WN; ++jn)
 #pragma unroll
     for (int i = 0; i < WM; ++i) acc[i][jn] += bias[jn];
-  if (active) {
+  if (active && store_y) {
     if (a.y_bf16)
       conv_store<uint16_t, WM, WN, WGM, WGN>(a, acc, n, t0, c0, wm, wn);
     else
@@ -119,8 +141,8 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
         Stats st = red[cl];
 #pragma unroll
         for (int w = 1; w < WGM; ++w) st = stats_merge(st, red[w * TN + cl]);
-        f32x2 v = {st.mean, st.m2};
-        *(f32x2*)(a.part + ((n * a.C_out + c) * a.n_ttiles + ttile) * 2) = v;
+        store_partial(a.part + ((n * a.C_out + c) * a.n_ttiles + ttile) * 2, st.mean, st.m2,
+                      coherent);
       }
     }
   } else {  // EPI_LN_PART
@@ -154,8 +176,8 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
         Stats st = red[tl];
 #pragma unroll
         for (int w = 1; w < WGN; ++w) st = stats_merge(st, red[w * TM + tl]);
-        f32x2 v = {st.mean, st.m2};
-        *(f32x2*)(a.part + ((n * a.n_ctiles + ctile) * T_out + t) * 2) = v;
+        store_partial(a.part + ((n * a.n_ctiles + ctile) * T_out + t) * 2, st.mean, st.m2,
+                      coherent);
       }
     }
   }

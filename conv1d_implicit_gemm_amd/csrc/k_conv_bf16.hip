@@ -79,8 +79,180 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // 16-byte column swizzle of LDS row `row`
 __host__ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 2; }
 
-template <int WM, int KT, int XR>
-__global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
+// Wait until every workgroup of the sample has published its partial
+// statistics.  The partials are device-scope atomic stores and are read back
+// with device-scope atomic loads, so they need no cache-wide flush: the
+// barrier waits until every wave's stores have completed, thread 0 then
+// counts the workgroup in (device-scope atomic add) and polls the counter.
+// The wait gives up after a bound no legitimate wait approaches (the launch
+// is cooperative, so every workgroup of the round is resident), records that
+// in *fault and returns false (the caller then poisons its statistics), so no
+// path can hang.
+__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault) {
+  __shared__ int complete;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned spins = 0;
+    int ok = 1;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
+      if (++spins > (1u << 22)) {  // ~0.1 s of polling
+        __hip_atomic_store(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    complete = ok;
+  }
+  __syncthreads();
+  return complete != 0;
+}
+
+// The kernel's arguments, read afresh from the argument segment: the pointer
+// is made opaque, so the fields are loaded inside each round of the
+// persistent loop instead of being hoisted out of it and held in scalar
+// registers (spilled) across every round.  ConvArgs is the first argument.
+__device__ __forceinline__ const ConvArgs& round_args() {
+  typedef const __attribute__((address_space(4))) char* kptr;
+  kptr p = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const ConvArgs*)p;
+}
+
+// Persistent-kernel epilogue: bias and partial statistics (as the split
+// path), the sample barrier, the fixed-order merge of the sample's partials
+// for this tile's groups (GroupNorm) or positions (LayerNorm over channels),
+// then normalise + affine in registers and write the output once.  Every
+// workgroup that needs a group's statistics merges the same partials in the
+// same order.
+template <int WM, int EPI>
+__device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
+                                                    f32x4 (&acc)[WM][WN], int64_t n,
+                                                    int64_t t0, int c0, int ttile, int ctile,
+                                                    int wm, int wn, int round, int slot,
+                                                    int tps, Stats* red, float* lds) {
+  constexpr int TM = WGM * WM * 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int64_t T_out = a.T_out;
+  constexpr bool gn = EPI == EPI_GN_FUSED;
+  conv_epilogue<WM, WN, WGM, WGN>(a, gn ? EPI_GN_PART : EPI_LN_PART, acc, n, t0, c0, ttile,
+                                  ctile, wm, wn, red, true, false);
+  // an incomplete set of partials (a wait that gave up) yields NaN statistics,
+  // hence a NaN output, never a plausible wrong one
+  const float poison =
+      sample_barrier(a.sync + (int64_t)round * a.spr + slot, (unsigned)tps, a.fault)
+          ? 0.f : __builtin_nanf("");
+
+  float* mean_s = lds;        // merged statistics of this tile
+  float* rstd_s = lds + 512;
+  Stats* tree = (Stats*)(lds + 1024);
+  if constexpr (gn) {
+    // groups of cpg channels, cpg dividing TN: ng groups per tile, S threads each
+    // (cpg divides TN, or TN divides cpg: then the whole tile is one group)
+    const int cpg = (int)(a.C_out / a.G);
+    const int ng = cpg >= TN ? 1 : TN / cpg, S = NTHR / ng;
+    const int k = tid / S, u = tid - k * S;
+    const int64_t g = (int64_t)(c0 / cpg) + k;
+    Stats st = {0.f, 0.f, 0.f};
+    if (g < a.G) {
+      const int64_t P = (int64_t)cpg * a.n_ttiles;
+      const float* base = a.part + ((n * a.C_out + g * cpg) * a.n_ttiles) * 2;
+      for (int64_t p = u; p < P; p += S) {
+        const int tt = (int)(p % a.n_ttiles);
+        const int64_t cntl = T_out - (int64_t)tt * TM;
+        const float cnt = (float)(cntl < TM ? cntl : TM);
+        const f32x2 v = load_partial_coherent(base + 2 * p);
+        st = stats_merge(st, Stats{cnt, v[0], v[1]});
+      }
+    }
+    tree[tid] = st;
+    __syncthreads();
+    for (int h = S / 2; h > 0; h >>= 1) {
+      if (u < h) tree[tid] = stats_merge(tree[tid], tree[tid + h]);
+      __syncthreads();
+    }
+    if (u == 0) {
+      const Stats r = tree[tid];
+      const float mu = r.mean + poison, rs = 1.0f / sqrtf(r.m2 / r.n + a.eps) + poison;
+      mean_s[k] = mu;
+      rstd_s[k] = rs;
+      if (ttile == 0 && g < a.G) {
+        if (a.mean_out) a.mean_out[n * a.G + g] = mu;
+        if (a.rstd_out) a.rstd_out[n * a.G + g] = rs;
+      }
+    }
+  } else {
+    // one position per thread: the channel tiles' partials at (n, t)
+    for (int tl = tid; tl < TM; tl += NTHR) {
+      const int64_t t = t0 + tl;
+      float mu = 0.f, rs = 0.f;
+      if (t < T_out) {
+        Stats st = {0.f, 0.f, 0.f};
+        for (int ct = 0; ct < a.n_ctiles; ++ct) {
+          const int64_t rem = a.C_out - (int64_t)ct * TN;
+          const float cnt = (float)(rem < TN ? rem : TN);
+          const f32x2 v = load_partial_coherent(a.part + ((n * a.n_ctiles + ct) * T_out + t) * 2);
+          st = stats_merge(st, Stats{cnt, v[0], v[1]});
+        }
+        mu = st.mean + poison;
+        rs = 1.0f / sqrtf(st.m2 / st.n + a.eps) + poison;
+        if (ctile == 0) {
+          if (a.mean_out) a.mean_out[n * T_out + t] = mu;
+          if (a.rstd_out) a.rstd_out[n * T_out + t] = rs;
+        }
+      }
+      mean_s[tl] = mu;
+      rstd_s[tl] = rs;
+    }
+  }
+  __syncthreads();
+
+  // normalise + affine in registers (channel c, position t of each lane)
+  float ga[WN], be[WN];
+#pragma unroll
+  for (int jn = 0; jn < WN; ++jn) {
+    const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+    ga[jn] = (a.gamma != nullptr && c < a.C_out) ? a.gamma[c] : 1.f;
+    be[jn] = (a.beta != nullptr && c < a.C_out) ? a.beta[c] : 0.f;
+  }
+  if constexpr (gn) {
+    const int cpg = (int)(a.C_out / a.G);
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      const int k = (wn * WN * 16 + jn * 16 + lr) / cpg;
+      const float mu = mean_s[k], sc = rstd_s[k] * ga[jn], b = be[jn];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][jn][r] = (acc[i][jn][r] - mu) * sc + b;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = wm * WM * 16 + i * 16 + 4 * kq + r;
+        const float mu = mean_s[tl], rs = rstd_s[tl];
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn)
+          acc[i][jn][r] = (acc[i][jn][r] - mu) * (rs * ga[jn]) + be[jn];
+      }
+  }
+  if (a.y_bf16)
+    conv_store<uint16_t, WM, WN, WGM, WGN>(a, acc, n, t0, c0, wm, wn);
+  else
+    conv_store<float, WM, WN, WGM, WGN>(a, acc, n, t0, c0, wm, wn);
+}
+
+// FUSE: 0 (one tile per workgroup, epilogue epi), or EPI_GN_FUSED /
+// EPI_LN_FUSED (persistent rounds of whole samples, normalised output)
+template <int WM, int KT, int XR, int FUSE>
+__global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
+  const ConvArgs& a = a_;
   // the weight stage also holds the epilogue's cross-wave merge (<= 12 KB)
   constexpr int WSK = KT < 2 ? 2 : KT;
   constexpr int TM = WGM * WM * 16;
@@ -93,21 +265,35 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   __shared__ __attribute__((aligned(16))) u16 Ws1[WSK * TN * RW];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: in a scalar register, everything derived from
+  // it (copy slots, wave-tile origin) stays scalar too
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WGM, wn = wave / WGM;
   const int lr = lane & 15, kq = lane >> 4;
+  const int s = a.stride, d = a.dilation;
   // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
   // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
   // c-tile fastest, so the channel tiles of one input window share an L2.
-  const int total = a.n_ttiles * a.n_ctiles * (int)a.N;
+  // The persistent kernel (FUSE) runs rounds of spr whole samples.
+  const int tps = a.n_ttiles * a.n_ctiles;  // tiles per sample
+  const int total = FUSE != 0 ? (int)gridDim.x : tps * (int)a.N;
   int lin = blockIdx.x;
   if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
   const int ctile = lin % a.n_ctiles;
   const int ttile = (lin / a.n_ctiles) % a.n_ttiles;
-  const int64_t n = lin / (a.n_ctiles * a.n_ttiles);
-  const int64_t t0 = (int64_t)ttile * TM;
-  const int c0 = ctile * TN;
-  const int s = a.stride, d = a.dilation;
+  const int slot = lin / tps;  // FUSE: sample slot within a round
+  const int64_t t0_ = (int64_t)ttile * TM;
+  const int c0_ = ctile * TN;
+  const int rounds = FUSE != 0 ? a.rounds : 1;
+  for (int round = 0; round < rounds; ++round) {
+  const ConvArgs& a = FUSE != 0 ? round_args() : a_;
+  const int64_t n = FUSE != 0 ? (int64_t)round * a.spr + slot : (int64_t)slot;
+  // the tile origin, opaque per round: nothing derived from it (masks,
+  // offsets of the epilogue) is hoisted out of the round loop
+  int64_t t0 = t0_;
+  int c0 = c0_;
+  if constexpr (FUSE != 0) asm volatile("" : "+s"(t0), "+s"(c0));
+  if (n >= a.N) break;  // whole workgroup: the samples of later rounds are none
 
   // ---- copies of one chunk: pieces 0..XP-1 are 16-row runs of the window,
   // XP.. the weight image (KT*8 runs of 16 rows); piece = wave + NWAVE * p.
@@ -211,9 +397,12 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   // the MFMAs of taps 0..KT-2 of the chunk in (xs, ws) (tap 0's fragments
   // already loaded), reading taps 1..KT-1 behind them; a runtime loop keeps
   // one copy of the body
+  int kt = KT;  // with two taps, opaque: the one-trip loop stays a loop (its
+                // unrolled form spills in the persistent kernel)
+  if constexpr (KT == 2) asm volatile("" : "+s"(kt));
   auto taps = [&](const u16* xs, const u16* ws) __attribute__((always_inline)) {
 #pragma nounroll
-    for (int j = 1; j < KT; ++j) mfma_reload(xs, ws, j);
+    for (int j = 1; j < kt; ++j) mfma_reload(xs, ws, j);
   };
 
   // Pairs of chunks per iteration.  Copies run unconditionally on chunk
@@ -250,7 +439,14 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a, int epi) {
   wait_all_mem();  // surplus copies land before the epilogue reuses the LDS
   __syncthreads();
 
-  conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
+  if constexpr (FUSE == 0) {
+    conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
+  } else {
+    fused_norm_epilogue<WM, FUSE>(a, acc, n, t0, c0, ttile, ctile, wm, wn, round, slot, tps,
+                                  (Stats*)Ws0, (float*)Ws1);
+    __syncthreads();  // the LDS is reused by the next round
+  }
+  }  // rounds
 }
 
 // Weight image: one block of K*TN*RW bf16 per (ctile, chunk), laid out
@@ -342,8 +538,19 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_kernel(const u16* __rest
 
 template <int WM, int KT, int XR>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
+  if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
+    // one round: spr whole samples, every workgroup resident at once
+    ConvArgs ac = a;
+    int ep = epi;
+    void* args[] = {(void*)&ac, (void*)&ep};
+    const void* k = epi == EPI_GN_FUSED
+                        ? (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>
+                        : (const void*)conv_bf16_kernel<WM, KT, XR, EPI_LN_FUSED>;
+    return hipLaunchCooperativeKernel(k, dim3((unsigned)(a.spr * a.n_ttiles * a.n_ctiles)),
+                                      dim3(NTHR), args, 0, st);
+  }
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
-  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR>), grid, dim3(NTHR), 0, st, a, epi);
+  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR, 0>), grid, dim3(NTHR), 0, st, a, epi);
   return hipGetLastError();
 }
 
@@ -428,6 +635,69 @@ hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
   if (tm == 512) return launch_w<8>(a, epi, s);  // wave tiles 128 x 64
   if (tm == 128) return launch_w<2>(a, epi, s);  // wave tiles 32 x 64
   return hipErrorInvalidValue;
+}
+
+namespace {
+template <int WM, int KT, int XR>
+int capacity_wk() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>, NTHR, 0) !=
+      hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+template <int WM>
+int capacity_w(int K) {
+  switch (K) {
+    case 1: return capacity_wk<WM, 1, XCAP_WIDE>();
+    case 2: return capacity_wk<WM, 2, XCAP_WIDE>();
+    case 3: return capacity_wk<WM, 3, XCAP_WIDE>();
+    case 4: return capacity_wk<WM, 4, XCAP_WIDE>();
+    case 5: return capacity_wk<WM, 5, XCAP_WIDE>();
+    default: break;
+  }
+  if (WM != 2) return 0;
+  switch (K) {
+    case 6: return capacity_wk<2, 6, XCAP_TAPS>();
+    case 7: return capacity_wk<2, 7, XCAP_TAPS>();
+    case 8: return capacity_wk<2, 8, XCAP_TAPS>();
+    default: return 0;
+  }
+}
+__global__ void zero_u32_kernel(unsigned* p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0u;
+}
+}  // namespace
+
+int conv_bf16_fused_capacity(int stride, int K, int dilation) {
+  const int tm = conv_bf16_tile_m(stride, K, dilation);
+  if (tm == 512) return capacity_w<8>(K);
+  if (tm == 128) return capacity_w<2>(K);
+  return 0;
+}
+
+hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s) {
+  const int tps = a.n_ttiles * a.n_ctiles;
+  const int cap = conv_bf16_fused_capacity(a.stride, a.K, a.dilation);
+  if (tps < 1 || cap < tps) return hipErrorInvalidValue;
+  int64_t spr = cap / tps;
+  if (spr > a.N) spr = a.N;
+  a.spr = (int32_t)spr;
+  a.rounds = (int32_t)((a.N + spr - 1) / spr);
+  // counters (and the fault word just after them) start at zero
+  const int64_t words = (int64_t)a.spr * a.rounds + 1;
+  a.fault = a.sync + (words - 1);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
+                     a.sync, words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
+  return tm == 512 ? launch_w<8>(a, epi, s) : launch_w<2>(a, epi, s);
 }
 
 }  // namespace c1g

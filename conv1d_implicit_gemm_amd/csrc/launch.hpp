@@ -14,6 +14,10 @@ enum ConvEpi : int {
   EPI_STORE = 0,      // y = acc + bias
   EPI_GN_PART = 1,    // y, plus per-(n, channel, t-tile) (mean, M2) partials
   EPI_LN_PART = 2,    // y, plus per-(n, c-tile, t) (mean, M2) partials
+  // bf16 persistent kernel: partials, a barrier among the workgroups of each
+  // sample, the merge, and the normalised output written once (no y)
+  EPI_GN_FUSED = 3,
+  EPI_LN_FUSED = 4,
 };
 
 // Geometry + pointers of one implicit-GEMM convolution launch.
@@ -31,6 +35,17 @@ struct ConvArgs {
   int32_t n_ttiles;    // ceil(T_out / TM)
   int32_t n_ctiles;    // ceil(C_out / TN)
   int32_t y_bf16;      // y is stored as bf16 (rounded to nearest even)
+  // EPI_GN_FUSED / EPI_LN_FUSED (y is then the normalised output)
+  const float* gamma;  // [C_out] or nullptr
+  const float* beta;
+  float* mean_out;     // [N, G] (GroupNorm) or [N, T_out] (LayerNorm), or nullptr
+  float* rstd_out;
+  float eps;
+  int32_t G;
+  unsigned* sync;      // [rounds * spr] arrival counters, zero at launch
+  int32_t spr;         // samples per round (spr * tiles per sample workgroups)
+  int32_t rounds;      // ceil(N / spr)
+  unsigned* fault;     // set when a barrier wait gives up (never on a full GPU)
 };
 
 // ---- fp32 split-path convolution (k_conv_f32.hip)
@@ -61,6 +76,12 @@ size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K);
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
                           hipStream_t s);
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s);
+// Persistent conv + normalisation (EPI_GN_FUSED / EPI_LN_FUSED): workgroups
+// that can be resident at once on the current device for this geometry (0 if
+// unknown); the launch zeroes the counters, fills spr/rounds and launches
+// cooperatively.
+int conv_bf16_fused_capacity(int stride, int K, int dilation);
+hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s);
 
 // ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
 enum GemmEpi : int { GEMM_STORE = 0, GEMM_GN_ROWMIN = 1 };

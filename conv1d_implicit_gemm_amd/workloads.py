@@ -47,6 +47,7 @@ class Workload:
     bias: bool = True             # conv bias present
     affine: bool = True           # gamma/beta present
     rowmin_bias: bool = False     # per-row min over channels + bias2 broadcast
+    persistent: bool = True       # allow the persistent conv + normalisation route
     w_bound: Optional[float] = None
 
     @property

@@ -103,7 +103,14 @@ typedef struct c1g_norm_desc {
   int32_t G;                   /* groups for C1G_NORM_GROUP (C_out % G == 0); else 0   */
   float eps;                   /* added to the variance inside the square root (> 0)   */
   int32_t epilogue;            /* enum c1g_epilogue                                    */
+  int32_t flags;               /* C1G_FLAG_* bits; 0 = defaults                        */
 } c1g_norm_desc;
+
+/* c1g_norm_desc.flags */
+enum c1g_flags {
+  C1G_FLAG_NO_PERSISTENT = 1   /* never take the "fused_persistent" route (it needs the
+                                  whole device: every workgroup of a round resident) */
+};
 
 /* T_out of the geometry, or -1 if the geometry is invalid or has no output.
  * Pure host function; touches no device. */
@@ -192,6 +199,17 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
  *                        layer): an MFMA GEMM whose epilogue applies GroupNorm
  *                        and the row-min when C_out/G == 16; needs x and w
  *                        16-byte aligned (C1G_ERR_MISALIGNED otherwise)
+ *   "fused_persistent"   bf16, GroupNorm whose groups tile the 128-channel tiles
+ *                        (C_out/G divides 128 or 128 divides it) or LayerNorm
+ *                        over channels, no epilogue, at most 256 tiles per
+ *                        sample, flags without C1G_FLAG_NO_PERSISTENT: one
+ *                        cooperative launch in rounds of whole samples; each
+ *                        workgroup publishes partial statistics, waits for
+ *                        the other workgroups of its sample, merges them in a
+ *                        fixed order, normalises its tile in registers and
+ *                        writes out once (y never reaches memory).  On a
+ *                        device that cannot keep a sample's tiles resident
+ *                        together, the call runs the split route instead.
  *   "split"              everything else: conv with a partial-statistics
  *                        epilogue, a fixed-order merge, then the apply pass */
 const char* c1g_route(const c1g_conv_desc* d, const c1g_norm_desc* norm);

@@ -97,8 +97,22 @@ def test_routes():
     assert c1g.route(lin) == "gemm_rows"
     conv = _desc(N=64, C_in=512, C_out=1024, T=4096, K=5, dilation=2, pad_left=2,
                  pad_right=2, dtype=bf)
-    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0)) == "split"
-    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == "split"
+    # bf16: the persistent conv normalises in registers (64 tiles per sample)
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0)) == "fused_persistent"
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == \
+        "fused_persistent"
+    no_p = c1g.FLAG_NO_PERSISTENT
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0, no_p)) == "split"
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0, no_p)) == "split"
+    # groups that straddle the 128-channel tiles (C_out/G = 48), the row-min
+    # epilogue, or more than 256 tiles per sample: split
+    assert c1g.route(_desc(C_in=64, C_out=192, T=512, dtype=bf),
+                     c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0)) == "split"
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 1)) == "split"
+    assert c1g.route(_desc(C_in=64, C_out=1024, T=140000, dtype=bf),
+                     c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == "split"
+    # groups spanning whole tiles (C_out/G = 256) stay persistent
+    assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0)) == "fused_persistent"
     assert c1g.route(conv) == "conv_only"
 
 
@@ -200,6 +214,7 @@ def test_bf16_output_workspace():
     for dt in (c1g.C1G_F32, c1g.C1G_BF16):
         a, b = _desc(dtype=dt, **conv), _desc(dtype=dt, out_dtype=c1g.C1G_BF16, **conv)
         for nd in (c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0),     # 32 channels per group
+                   c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0, c1g.FLAG_NO_PERSISTENT),
                    c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 1)):
-            assert c1g.route(a, nd) == c1g.route(b, nd) == "split"
+            assert c1g.route(a, nd) == c1g.route(b, nd) != "gemm_rows"
             assert c1g.conv1d_gn_workspace_size(a, nd) == c1g.conv1d_gn_workspace_size(b, nd)

@@ -118,3 +118,62 @@ def test_bf16_determinism():
     g = GEMM_CASES[0]
     inp = make_inputs(g, 4)
     assert torch.equal(run_library(g, inp), run_library(g, inp))
+
+
+# The persistent route: one cooperative launch in rounds of whole samples
+# (256 resident workgroups / tiles per sample = samples per round), partial
+# statistics published, merged after a barrier among the sample's workgroups,
+# the output written once.
+PERSIST_CASES = [
+    # 5 x 4 tiles per sample -> 12 samples per round: two rounds, the second partial
+    W("persist_gn_2rounds", N=14, C_in=64, C_out=512, T=2200, K=3, pad_left=1, pad_right=1,
+      G=32, **BF),
+    W("persist_ln_2rounds", N=14, C_in=64, C_out=512, T=2200, K=3, pad_left=1, pad_right=1,
+      norm="layer_channels", **BF),
+    # one group spans two channel tiles (C_out/G = 256)
+    W("persist_gn_group_spans_tiles", N=3, C_in=40, C_out=512, T=700, K=5, dilation=2,
+      pad_left=4, pad_right=4, G=2, **BF),
+    # one channel per group, ragged channel tile (200 = 128 + 72)
+    W("persist_gn_cpg1_ragged", N=5, C_in=33, C_out=200, T=300, K=3, pad_left=1, pad_right=1,
+      G=200, **BF),
+    # 8 taps: 128-position tiles
+    W("persist_ln_k8", N=4, C_in=48, C_out=144, T=300, K=8, pad_left=3, pad_right=4,
+      norm="layer_channels", **BF),
+    W("persist_gn_bf16_out", N=6, C_in=64, C_out=256, T=1100, K=5, dilation=2, pad_left=4,
+      pad_right=4, G=16, out_dtype="bf16", **BF),
+]
+
+
+@pytest.mark.parametrize("wl", PERSIST_CASES, ids=lambda w: w.name)
+def test_persistent_route_parity(wl):
+    from tests.gpu_util import library_route
+    assert library_route(wl) == "fused_persistent"
+    check_parity(wl)
+
+
+def test_persistent_and_split_agree_with_oracle():
+    """The same inputs through the persistent route and, with the persistent
+    route switched off, the split route: both within tolerance of the oracle,
+    statistics included."""
+    wl = PERSIST_CASES[0]
+    announce("persistent vs split", wl.name)
+    inp = make_inputs(wl, 2)
+    ref = run_oracle(wl, inp)
+    x, w = (inp[k].to("cuda:0") for k in ("x", "w"))
+    b, ga, be = (inp[k].to("cuda:0") for k in ("bias", "gamma", "beta"))
+    for persistent in (True, False):
+        out, mean, rstd = c1g.conv1d_gn_forward(x, w, b, pad_left=1, pad_right=1, norm="group",
+                                                groups=wl.G, gamma=ga, beta=be,
+                                                return_stats=True, persistent=persistent)
+        torch.cuda.synchronize()
+        assert max_abs_err(out, ref["out"]) <= TOL_BF16, persistent
+        assert max_abs_err(mean, ref["mean"]) <= 1e-4, persistent
+        r = rstd.cpu().double().numpy()
+        assert float(np.max(np.abs(r / ref["rstd"] - 1))) <= 1e-4, persistent
+
+
+def test_persistent_determinism():
+    wl = PERSIST_CASES[1]
+    announce("persistent determinism", wl.name)
+    inp = make_inputs(wl, 5)
+    assert torch.equal(run_library(wl, inp), run_library(wl, inp))

@@ -22,9 +22,13 @@ CASES = [
     (W("bf16o_conv_gn_k5d2", N=2, C_in=72, C_out=160, T=1300, K=5, dilation=2, pad_left=2,
        pad_right=2, G=8, dtype="bf16", **BO), "split"),
     (W("bf16o_conv_gn_odd_T", N=2, C_in=40, C_out=64, T=203, K=3, pad_left=1, pad_right=1,
-       G=4, dtype="bf16", **BO), "split"),
+       G=4, dtype="bf16", **BO), "fused_persistent"),
+    (W("bf16o_conv_gn_odd_T_split", N=2, C_in=40, C_out=64, T=203, K=3, pad_left=1,
+       pad_right=1, G=4, dtype="bf16", persistent=False, **BO), "split"),
     (W("bf16o_conv_ln", N=1, C_in=40, C_out=272, T=1300, K=5, dilation=2, pad_left=2,
-       pad_right=2, norm="layer_channels", dtype="bf16", **BO), "split"),
+       pad_right=2, norm="layer_channels", dtype="bf16", **BO), "fused_persistent"),
+    (W("bf16o_conv_ln_split", N=1, C_in=40, C_out=272, T=1300, K=5, dilation=2, pad_left=2,
+       pad_right=2, norm="layer_channels", dtype="bf16", persistent=False, **BO), "split"),
     (W("bf16o_conv_gn_rowmin", N=2, C_in=32, C_out=64, T=96, K=3, pad_left=1, pad_right=1,
        G=4, rowmin_bias=True, dtype="bf16", **BO), "split"),
     (W("bf16o_conv_ln_rowmin", N=2, C_in=32, C_out=48, T=70, K=3, pad_left=1, pad_right=1,
@@ -32,7 +36,7 @@ CASES = [
     (W("bf16o_conv_only", N=3, C_in=48, C_out=130, T=256, K=2, norm=None, dtype="bf16", **BO),
      "conv_only"),
     (W("bf16o_conv_gn_k8", N=2, C_in=48, C_out=144, T=300, K=8, pad_left=3, pad_right=4, G=9,
-       dtype="bf16", **BO), "split"),
+       dtype="bf16", **BO), "fused_persistent"),
     # fp32 inputs
     (W("f32in_bf16o_fused_gn", N=2, C_in=64, C_out=128, T=512, K=3, pad_left=1, pad_right=1,
        G=16, **BO), "fused_single_pass"),
@@ -63,10 +67,13 @@ def test_bf16_out_parity(wl, route):
 
 
 def test_bf16_out_matches_rounded_fp32_out():
-    """Where only the final value is rounded (fused and GEMM routes), the bf16
-    output is the fp32 output rounded to nearest even, bit for bit (same
-    kernels, same fp32 arithmetic)."""
-    for wl in (CASES[7][0], CASES[11][0], CASES[14][0]):
+    """Where only the final value is rounded (fused, persistent and GEMM
+    routes), the bf16 output is the fp32 output rounded to nearest even, bit
+    for bit (same kernels, same fp32 arithmetic)."""
+    by_name = {wl.name: wl for wl, _ in CASES}
+    for name in ("f32in_bf16o_fused_gn", "gemm_bf16o_gn_rowmin_fused", "gemm_bf16o_only",
+                 "bf16o_conv_gn_odd_T", "bf16o_conv_ln"):
+        wl = by_name[name]
         announce("bf16 out == rne(fp32 out)", wl.name)
         inp = make_inputs(wl, 1)
         got = run_library(wl, inp)
