@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--no-persistent", action="store_true",
                     help="bf16 conv + GroupNorm/LayerNorm: time the multi-kernel split route "
                          "instead of the persistent single-kernel one")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="Linear + GroupNorm + row-min: one cooperative launch instead of the "
+                         "GEMM and a broadcast kernel")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -179,7 +182,8 @@ def main():
                               pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
                               gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"],
                               out_dtype=torch.bfloat16 if wl.out_dtype == "bf16"
-                              else torch.float32, persistent=not args.no_persistent)
+                              else torch.float32, persistent=not args.no_persistent,
+                              one_launch=args.one_launch)
     T_out = op.T_out
     flops = 2 * wl.N * T_out * wl.C_out * wl.C_in * wl.K
     stream = torch.cuda.current_stream(dev)

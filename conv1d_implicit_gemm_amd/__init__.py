@@ -32,6 +32,7 @@ C1G_F32, C1G_BF16 = 0, 1
 NORM_NONE, NORM_GROUP, NORM_LAYER_CHANNELS = 0, 1, 2
 EPI_NONE, EPI_ROWMIN_BIAS = 0, 1
 FLAG_NO_PERSISTENT = 1
+FLAG_ROWMIN_ONE_LAUNCH = 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "misaligned pointer",
           5: "HIP runtime error at launch"}
@@ -136,14 +137,18 @@ def _out_dtype(out, out_dtype):
     return dt
 
 
-def make_norm(norm=None, groups=0, eps=1e-5, rowmin=False, persistent=True) -> NormDesc:
-    """persistent=False forbids the "fused_persistent" route (it needs the
-    whole device for one cooperative launch)."""
+def make_norm(norm=None, groups=0, eps=1e-5, rowmin=False, persistent=True,
+              one_launch=False) -> NormDesc:
+    """persistent=False forbids cooperative launches (no "fused_persistent"
+    route; they need every workgroup of a round resident at once).
+    one_launch=True asks for the "gemm_rows" GroupNorm + row-min as one
+    cooperative launch instead of a GEMM plus a broadcast kernel."""
     code = {None: NORM_NONE, "none": NORM_NONE, "group": NORM_GROUP,
             "layer_channels": NORM_LAYER_CHANNELS}[norm]
     return NormDesc(code, groups if code == NORM_GROUP else 0, eps,
                     EPI_ROWMIN_BIAS if rowmin else EPI_NONE,
-                    0 if persistent else FLAG_NO_PERSISTENT)
+                    (0 if persistent else FLAG_NO_PERSISTENT) |
+                    (FLAG_ROWMIN_ONE_LAUNCH if one_launch else 0))
 
 
 def out_len(desc: ConvDesc) -> int:
@@ -249,7 +254,8 @@ def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_r
 def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                       causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                       beta=None, rowmin_bias=None, return_stats=False, out=None,
-                      out_dtype=torch.float32, persistent=True, workspace=None):
+                      out_dtype=torch.float32, persistent=True, one_launch=False,
+                      workspace=None):
     """conv -> GroupNorm / LayerNorm over channels / none -> optional row-min + bias.
 
     Returns out [N, C_out, T_out] (fp32, or bf16 with out_dtype=torch.bfloat16
@@ -258,7 +264,7 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
     lib = load_library()
     odt = _out_dtype(out, out_dtype)
     desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt)
-    nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent)
+    nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent, one_launch)
     for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
         _need(t, nm, torch.float32, x.device)
     T_out = lib.c1g_out_len(ctypes.byref(desc))
@@ -337,12 +343,13 @@ class PreparedConv1dGN:
     def __init__(self, x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                  causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                  beta=None, rowmin_bias=None, out=None, out_dtype=torch.float32, mean=None,
-                 rstd=None, persistent=True):
+                 rstd=None, persistent=True, one_launch=False):
         lib = load_library()
         odt = _out_dtype(out, out_dtype)
         self.desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
                                 odt)
-        self.norm = make_norm(norm, groups, eps, rowmin_bias is not None, persistent)
+        self.norm = make_norm(norm, groups, eps, rowmin_bias is not None, persistent,
+                              one_launch)
         for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"),
                       (rowmin_bias, "rowmin_bias"), (mean, "mean"), (rstd, "rstd")):
             _need(t, nm, torch.float32, x.device)

@@ -114,6 +114,10 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
     // statistics and the affine read unrounded values
     p.off_y = off;
     if (p.out_bf16 && !p.gemm_fused) off = align_up(off + (size_t)d->N * d->C_out * sizeof(float));
+    // the one-launch form of the fused epilogue: an arrival counter per row
+    // block and a fault word
+    p.off_sync = off;
+    if (p.gemm_fused) off = align_up(off + (size_t)(p.n_ttiles + 1) * sizeof(unsigned));
     p.total = conv_only ? 0 : off;
     return p;
   }
@@ -254,7 +258,7 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
   if (!aligned(x, 16) || !aligned(w, 16)) return C1G_ERR_MISALIGNED;
   const bool conv_only = !nd || (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE);
   const int out_dt = p.out_bf16 ? C1G_BF16 : C1G_F32;
-  GemmArgs g;
+  GemmArgs g{};
   g.x = x;
   g.w = w;
   g.bias = bias;
@@ -276,6 +280,16 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
   g.n_ntiles = p.n_ttiles;
   g.eps = nd ? nd->eps : 0.f;
   if (p.gemm_fused) {
+    // one cooperative launch on request when every tile can be resident at
+    // once, else the GEMM and a broadcast kernel
+    if ((nd->flags & C1G_FLAG_ROWMIN_ONE_LAUNCH) && !(nd->flags & C1G_FLAG_NO_PERSISTENT) &&
+        (int64_t)p.n_ctiles * p.n_ttiles <= gemm_bf16_rowmin_capacity()) {
+      g.bias2 = bias2;
+      g.out = out;
+      g.out_bf16 = p.out_bf16;
+      g.sync = (unsigned*)(ws + p.off_sync);
+      return hip_status(gemm_bf16_rowmin_one_launch(g, s));
+    }
     hipError_t e = gemm_bf16_launch(g, GEMM_GN_ROWMIN, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     return hip_status(

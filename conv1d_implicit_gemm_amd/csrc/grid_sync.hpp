@@ -1,0 +1,51 @@
+// Waits between the workgroups of one cooperative launch.
+//
+// A group of workgroups (the tiles of one sample, or of one row block) meets
+// on a 32-bit arrival counter in the caller's workspace, zeroed before the
+// launch by zero_u32_kernel (a fill kernel rather than a memset, so the call
+// may be captured in a graph).  What the workgroups exchange is written with
+// device-scope atomic stores and read with device-scope atomic loads: those
+// reach the point of coherence of all XCDs, so no cache-wide flush is needed.
+#pragma once
+
+#include "common.hpp"
+
+namespace c1g {
+namespace {
+
+// Every thread of the workgroup returns once `expect` workgroups have arrived
+// on *ctr (this one included).  Waits for this wave's outstanding memory
+// operations first, so every store the workgroup issued before the call is
+// visible to the others once they see its arrival.  The wait gives up after
+// a bound no legitimate wait approaches (in a cooperative launch every
+// workgroup is resident), records that in *fault and returns false, so no
+// path can hang; the caller then poisons what depended on the others.
+__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault) {
+  __shared__ int complete;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned spins = 0;
+    int ok = 1;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
+      if (++spins > (1u << 22)) {  // ~0.1 s of polling
+        __hip_atomic_store(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    complete = ok;
+  }
+  __syncthreads();
+  return complete != 0;
+}
+
+__global__ void zero_u32_kernel(unsigned* p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0u;
+}
+
+}  // namespace
+}  // namespace c1g

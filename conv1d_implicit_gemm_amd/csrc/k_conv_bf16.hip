@@ -36,6 +36,7 @@
 // LayerNorm partial statistics).
 #include "common.hpp"
 #include "conv_epilogue.hpp"
+#include "grid_sync.hpp"
 #include "launch.hpp"
 
 namespace c1g {
@@ -78,37 +79,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 
 // 16-byte column swizzle of LDS row `row`
 __host__ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 2; }
-
-// Wait until every workgroup of the sample has published its partial
-// statistics.  The partials are device-scope atomic stores and are read back
-// with device-scope atomic loads, so they need no cache-wide flush: the
-// barrier waits until every wave's stores have completed, thread 0 then
-// counts the workgroup in (device-scope atomic add) and polls the counter.
-// The wait gives up after a bound no legitimate wait approaches (the launch
-// is cooperative, so every workgroup of the round is resident), records that
-// in *fault and returns false (the caller then poisons its statistics), so no
-// path can hang.
-__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault) {
-  __shared__ int complete;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are done
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned spins = 0;
-    int ok = 1;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
-      if (++spins > (1u << 22)) {  // ~0.1 s of polling
-        __hip_atomic_store(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    complete = ok;
-  }
-  __syncthreads();
-  return complete != 0;
-}
 
 // The kernel's arguments, read afresh from the argument segment: the pointer
 // is made opaque, so the fields are loaded inside each round of the
@@ -667,10 +637,6 @@ int capacity_w(int K) {
     case 8: return capacity_wk<2, 8, XCAP_TAPS>();
     default: return 0;
   }
-}
-__global__ void zero_u32_kernel(unsigned* p, int64_t count) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0u;
 }
 }  // namespace
 

@@ -38,8 +38,13 @@
 // tile's channels into
 // one partial per (n, c-tile) (fixed slots, no atomics); optional mean/rstd
 // outputs.  rowmin_bcast then folds the partials in a fixed order and writes
-// out[n][c] = min + bias2[c].
+// out[n][c] = min + bias2[c].  GEMM_GN_ROWMIN_ONE does that last step inside
+// the same launch: the grid is launched cooperatively (every tile resident),
+// each workgroup publishes its partials, waits until the other c-tiles of its
+// rows have published theirs, folds them (min is exact, so any order gives the
+// same bits) and writes its own 256 x 128 block of the broadcast output.
 #include "common.hpp"
+#include "grid_sync.hpp"
 #include "launch.hpp"
 
 namespace c1g {
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       const int64_t c = cg + 4 * kq;
       gam[i] = (f32x4){1.f, 1.f, 1.f, 1.f};
       bet[i] = bis[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (EPI == GEMM_GN_ROWMIN) {
+      if (EPI != GEMM_STORE) {
         // whole groups of 16: a group either lies inside C_out or past it
         const int64_t cc = cg < a.C_out ? c : 4 * kq;
         if (vec) {
@@ -422,7 +427,64 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       float m = red[tid];
 #pragma unroll
       for (int w = 1; w < KSPLIT * WGC; ++w) m = fminf(m, red[w * BN + tid]);
-      if (nn < a.N) a.part[nn * a.n_ctiles + ctile] = m;
+      if (nn < a.N) {
+        float* p = a.part + nn * a.n_ctiles + ctile;
+        if (EPI == GEMM_GN_ROWMIN_ONE)  // read by the other c-tiles' workgroups
+          __hip_atomic_store((unsigned*)p, __float_as_uint(m), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *p = m;
+      }
+    }
+    if constexpr (EPI == GEMM_GN_ROWMIN_ONE) {
+      const bool ok = sample_barrier(a.sync + ntile, (unsigned)a.n_ctiles, a.fault);
+      // the rows' minima over all c-tiles (NaN if a wait gave up)
+      float* rowm = red + KSPLIT * WGC * BN;
+      if (tid < BN) {
+        const int64_t nn = n0 + tid;
+        float m = __builtin_inff();
+        if (nn < a.N)
+          for (int t = 0; t < a.n_ctiles; ++t)
+            m = fminf(m, __uint_as_float(__hip_atomic_load(
+                             (const unsigned*)(a.part + nn * a.n_ctiles + t), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT)));
+        rowm[tid] = ok ? m : __builtin_nanf("");
+      }
+      __syncthreads();
+      // this tile's block of out[n][c] = min[n] + bias2[c]: a wave writes whole
+      // 256-channel row segments, four channels per lane
+      const int64_t c = c0 + 4 * lane;
+      f32x4 b = {0.f, 0.f, 0.f, 0.f};
+      const bool vec = (a.C_out % 4 == 0) &&
+                       ((((uintptr_t)a.out) & (a.out_bf16 ? 7 : 15)) == 0) &&
+                       ((((uintptr_t)a.bias2) & 15) == 0);
+      if (a.bias2) {
+        if (vec && c + 3 < a.C_out) {
+          b = *(const f32x4*)(a.bias2 + c);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) b[r] = c + r < a.C_out ? a.bias2[c + r] : 0.f;
+        }
+      }
+      auto bcast = [&](auto* out) __attribute__((always_inline)) {
+        for (int r = wave; r < BN; r += NWAVE) {
+          const int64_t nn = n0 + r;
+          if (nn >= a.N) break;
+          const f32x4 v = b + rowm[r];
+          auto* dst = out + nn * a.C_out + c;
+          if (vec && c + 3 < a.C_out) {
+            store_elem4(dst, v);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (c + q < a.C_out) store_elem(dst + q, v[q]);
+          }
+        }
+      };
+      if (a.out_bf16)
+        bcast((uint16_t*)a.out);
+      else
+        bcast((float*)a.out);
     }
   }
 }
@@ -469,6 +531,32 @@ hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const
     hipLaunchKernelGGL(rowmin_bcast_kernel<float>, dim3((unsigned)N), dim3(NTHR), 0, s, part,
                        n_ctiles, bias2, (float*)out, C);
   return hipGetLastError();
+}
+
+int gemm_bf16_rowmin_capacity() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, (const void*)gemm_bf16_kernel<GEMM_GN_ROWMIN_ONE>, NTHR, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
+hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, hipStream_t s) {
+  const int64_t tiles = (int64_t)a.n_ctiles * a.n_ntiles;
+  if (tiles < 1 || tiles > gemm_bf16_rowmin_capacity()) return hipErrorInvalidValue;
+  // one arrival counter per row block, then the fault word
+  const int64_t words = (int64_t)a.n_ntiles + 1;
+  a.fault = a.sync + a.n_ntiles;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
+                     a.sync, words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void* args[] = {(void*)&a};
+  return hipLaunchCooperativeKernel((const void*)gemm_bf16_kernel<GEMM_GN_ROWMIN_ONE>,
+                                    dim3((unsigned)tiles), dim3(NTHR), args, 0, s);
 }
 
 int gemm_bf16_tile_c() { return BM; }

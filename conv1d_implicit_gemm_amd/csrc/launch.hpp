@@ -84,7 +84,10 @@ int conv_bf16_fused_capacity(int stride, int K, int dilation);
 hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s);
 
 // ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
-enum GemmEpi : int { GEMM_STORE = 0, GEMM_GN_ROWMIN = 1 };
+// GEMM_GN_ROWMIN writes per-tile row minima for rowmin_bcast;
+// GEMM_GN_ROWMIN_ONE (cooperative launch, every tile resident) also waits for
+// the other c-tiles of its rows and writes its block of the broadcast output
+enum GemmEpi : int { GEMM_STORE = 0, GEMM_GN_ROWMIN = 1, GEMM_GN_ROWMIN_ONE = 2 };
 struct GemmArgs {
   const void* x;       // [N, C_in] bf16, 16-byte aligned, C_in % 8 == 0
   const void* w;       // [C_out, C_in] bf16, 16-byte aligned
@@ -95,14 +98,24 @@ struct GemmArgs {
   float* part;         // GN_ROWMIN: [N, n_ctiles] per-tile row minima
   float* mean_out;     // GN_ROWMIN: [N, G] or nullptr
   float* rstd_out;
+  const float* bias2;  // GN_ROWMIN_ONE: [C_out] or nullptr
+  void* out;           // GN_ROWMIN_ONE: [N, C_out], fp32 or (out_bf16) bf16
+  unsigned* sync;      // GN_ROWMIN_ONE: n_ntiles arrival counters, zeroed by the launcher
+  unsigned* fault;     // set when a barrier wait gives up (never on a full GPU)
   int64_t N, C_in, C_out;
   int32_t G, n_ctiles, n_ntiles;
   float eps;
-  int32_t y_bf16;
+  int32_t y_bf16, out_bf16;
 };
 int gemm_bf16_tile_c();
 int gemm_bf16_tile_n();
 hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s);
+// GEMM + GroupNorm + row-min + bias2 in one cooperative launch: workgroups the
+// device keeps resident at once with the GN_ROWMIN_ONE kernel (0 on error);
+// the launch needs n_ctiles * n_ntiles of them and n_ntiles + 1 zeroed
+// words at a.sync (zeroed here)
+int gemm_bf16_rowmin_capacity();
+hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, hipStream_t s);
 // out[n][c] = min_t part[n][t] + bias2[c]; out fp32 or (out_bf16) bf16
 hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const float* bias2,
                                void* out, bool out_bf16, int64_t C, hipStream_t s);

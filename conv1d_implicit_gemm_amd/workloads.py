@@ -48,6 +48,7 @@ class Workload:
     affine: bool = True           # gamma/beta present
     rowmin_bias: bool = False     # per-row min over channels + bias2 broadcast
     persistent: bool = True       # allow the persistent conv + normalisation route
+    one_launch: bool = False      # Linear + GroupNorm + row-min as one cooperative launch
     w_bound: Optional[float] = None
 
     @property

@@ -108,8 +108,15 @@ typedef struct c1g_norm_desc {
 
 /* c1g_norm_desc.flags */
 enum c1g_flags {
-  C1G_FLAG_NO_PERSISTENT = 1   /* never take the "fused_persistent" route (it needs the
-                                  whole device: every workgroup of a round resident) */
+  C1G_FLAG_NO_PERSISTENT = 1,  /* no cooperative launches: never take the
+                                  "fused_persistent" route, and ignore
+                                  C1G_FLAG_ROWMIN_ONE_LAUNCH (the cooperative forms
+                                  need every workgroup of a round resident at once) */
+  C1G_FLAG_ROWMIN_ONE_LAUNCH = 2  /* "gemm_rows" with GroupNorm + row-min: one
+                                  cooperative launch instead of a GEMM and a broadcast
+                                  kernel (same result, bit for bit; on MI355X the
+                                  cooperative launch's queue synchronisation costs more
+                                  than the second launch, so it is not the default) */
 };
 
 /* T_out of the geometry, or -1 if the geometry is invalid or has no output.
@@ -198,7 +205,14 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
  *   "gemm_rows"          bf16, K = 1, T = 1, no padding, C_in % 8 == 0 (a Linear
  *                        layer): an MFMA GEMM whose epilogue applies GroupNorm
  *                        and the row-min when C_out/G == 16; needs x and w
- *                        16-byte aligned (C1G_ERR_MISALIGNED otherwise)
+ *                        16-byte aligned (C1G_ERR_MISALIGNED otherwise).  The
+ *                        row-min epilogue runs as the GEMM plus a broadcast
+ *                        kernel, or with C1G_FLAG_ROWMIN_ONE_LAUNCH (and the
+ *                        device able to keep every GEMM tile resident at once)
+ *                        as one cooperative launch: each workgroup publishes
+ *                        its rows' partial minima, waits for the other channel
+ *                        tiles of those rows and writes its block of the
+ *                        broadcast output (same result, bit for bit)
  *   "fused_persistent"   bf16, GroupNorm whose groups tile the 128-channel tiles
  *                        (C_out/G divides 128 or 128 divides it) or LayerNorm
  *                        over channels, no epilogue, at most 256 tiles per

@@ -47,7 +47,7 @@ def run_library(wl: Workload, inp: dict, *, return_stats=False, poison=True):
                                     pad_left=wl.pad_left, pad_right=wl.pad_right,
                                     norm=wl.norm, groups=wl.G, eps=wl.eps, gamma=ga, beta=be,
                                     rowmin_bias=b2, return_stats=True, out=out,
-                                    persistent=wl.persistent)
+                                    persistent=wl.persistent, one_launch=wl.one_launch)
     torch.cuda.synchronize()
     return res if return_stats else res[0]
 
@@ -80,7 +80,8 @@ def library_route(wl: Workload):
                          dilation=wl.dilation, pad_left=wl.pad_left, pad_right=wl.pad_right,
                          dtype=c1g.C1G_BF16 if wl.dtype == "bf16" else c1g.C1G_F32,
                          out_dtype=c1g.C1G_BF16 if wl.out_dtype == "bf16" else c1g.C1G_F32)
-    return c1g.route(desc, c1g.make_norm(wl.norm, wl.G, wl.eps, wl.rowmin_bias, wl.persistent))
+    return c1g.route(desc, c1g.make_norm(wl.norm, wl.G, wl.eps, wl.rowmin_bias, wl.persistent,
+                                         wl.one_launch))
 
 
 def bf16_out_bound(wl: Workload, inp: dict, ref: dict):

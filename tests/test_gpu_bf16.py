@@ -69,6 +69,13 @@ GEMM_CASES = [
     W("gemm_tail_only", N=17, C_in=40, C_out=64, T=1, K=1, G=4, rowmin_bias=True, **BF),
     # odd number of whole chunks plus a tail
     W("gemm_odd_chunks_tail", N=90, C_in=200, C_out=128, T=1, K=1, G=8, **BF),
+    # GroupNorm + row-min in one cooperative launch over 3 row blocks x 5
+    # channel tiles, both ragged (1040 = 4 * 256 + 16 channels, 300 = 2 * 128 + 44
+    # rows), and the same as a GEMM plus a broadcast kernel
+    W("gemm_gn_rowmin_one_launch_ragged", N=300, C_in=200, C_out=1040, T=1, K=1, G=65,
+      rowmin_bias=True, one_launch=True, **BF),
+    W("gemm_gn_rowmin_two_launch_ragged", N=300, C_in=200, C_out=1040, T=1, K=1, G=65,
+      rowmin_bias=True, **BF),
 ]
 
 
@@ -80,6 +87,21 @@ def test_bf16_gemm_parity(wl):
 def test_gemm_route_is_taken():
     d = c1g.make_desc(1024, 8192, 8192, 1, 1, dtype=c1g.C1G_BF16)
     assert c1g.route(d, c1g.make_norm("group", 512, 1e-5, True)) == "gemm_rows"
+
+
+@pytest.mark.parametrize("name", ["gemm_gn_rowmin_one_launch_ragged",
+                                  "gemm_gn_rowmin_bf16_m1024_n8192_k8192"])
+def test_gemm_rowmin_one_and_two_launches_identical(name):
+    """GroupNorm + row-min + bias2 as one cooperative launch and as a GEMM plus
+    a broadcast kernel: the same arithmetic in the same order, and a minimum is
+    exact, so the outputs and statistics agree bit for bit."""
+    wl = WORKLOADS.get(name) or next(w for w in GEMM_CASES if w.name == name)
+    announce("gemm one vs two launches", wl.name)
+    inp = make_inputs(wl, 3)
+    one = run_library(wl.replace(one_launch=True), inp, return_stats=True)
+    two = run_library(wl.replace(one_launch=False), inp, return_stats=True)
+    for a, b in zip(one, two):
+        assert torch.equal(a, b)
 
 
 def test_linear_gn_rowmin_full_size_sampled():

@@ -57,6 +57,8 @@ CASES = [
      "gemm_rows"),
     (W("gemm_bf16o_gn_rowmin_unfused", N=20, C_in=64, C_out=96, T=1, K=1, G=3,
        rowmin_bias=True, dtype="bf16", **BO), "gemm_rows"),
+    (W("gemm_bf16o_gn_rowmin_one_launch", N=200, C_in=128, C_out=528, T=1, K=1, G=33,
+       rowmin_bias=True, dtype="bf16", one_launch=True, **BO), "gemm_rows"),
 ]
 
 
@@ -72,7 +74,7 @@ def test_bf16_out_matches_rounded_fp32_out():
     for bit (same kernels, same fp32 arithmetic)."""
     by_name = {wl.name: wl for wl, _ in CASES}
     for name in ("f32in_bf16o_fused_gn", "gemm_bf16o_gn_rowmin_fused", "gemm_bf16o_only",
-                 "bf16o_conv_gn_odd_T", "bf16o_conv_ln"):
+                 "gemm_bf16o_gn_rowmin_one_launch", "bf16o_conv_gn_odd_T", "bf16o_conv_ln"):
         wl = by_name[name]
         announce("bf16 out == rne(fp32 out)", wl.name)
         inp = make_inputs(wl, 1)
