@@ -75,6 +75,44 @@ __device__ __forceinline__ void conv_store(const ConvArgs& a, const f32x4 (&acc)
   }
 }
 
+// GroupNorm statistics of this wave's positions, per channel: lane (lr, kq == 0)
+// of wave (wm, wn) writes red[wm * TN + channel-in-tile] = (count, mean, M2)
+// over the wave's valid positions (two passes over the registers, cross-lane
+// sums).  The caller synchronises before reading red.
+template <int WM, int WN, int WGM, int WGN>
+__device__ __forceinline__ void gn_wave_channel_stats(const ConvArgs& a,
+                                                      const f32x4 (&acc)[WM][WN], int64_t t0,
+                                                      int wm, int wn, Stats* red, bool active) {
+  constexpr int TN = WGN * WN * 16;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int64_t T_out = a.T_out;
+#pragma unroll
+  for (int jn = 0; jn < WN; ++jn) {
+    float sum = 0.f, cnt = 0.f;
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
+        if (t < T_out) { sum += acc[i][jn][r]; cnt += 1.f; }
+      }
+    sum = lane_sum<48>(sum);
+    cnt = lane_sum<48>(cnt);
+    const float mean = cnt > 0.f ? sum / cnt : 0.f;
+    float m2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
+        if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
+      }
+    m2 = lane_sum<48>(m2);
+    if (active && kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
+  }
+}
+
 template <int WM, int WN, int WGM, int WGN>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
                                               f32x4 (&acc)[WM][WN], int64_t n, int64_t t0,
@@ -110,30 +148,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
   __syncthreads();  // the staging LDS is free again: reuse it for the cross-wave merge
 
   if (epi == EPI_GN_PART) {
-#pragma unroll
-    for (int jn = 0; jn < WN; ++jn) {
-      float sum = 0.f, cnt = 0.f;
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-          if (t < T_out) { sum += acc[i][jn][r]; cnt += 1.f; }
-        }
-      sum = lane_sum<48>(sum);
-      cnt = lane_sum<48>(cnt);
-      const float mean = cnt > 0.f ? sum / cnt : 0.f;
-      float m2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-          if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
-        }
-      m2 = lane_sum<48>(m2);
-      if (active && kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
-    }
+    gn_wave_channel_stats<WM, WN, WGM, WGN>(a, acc, t0, wm, wn, red, active);
     __syncthreads();
     for (int cl = tid; cl < TN; cl += blockDim.x) {
       const int c = c0 + cl;

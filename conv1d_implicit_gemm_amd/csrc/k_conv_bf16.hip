@@ -91,12 +91,32 @@ __device__ __forceinline__ const ConvArgs& round_args() {
   return *(const ConvArgs*)p;
 }
 
-// Persistent-kernel epilogue: bias and partial statistics (as the split
-// path), the sample barrier, the fixed-order merge of the sample's partials
-// for this tile's groups (GroupNorm) or positions (LayerNorm over channels),
-// then normalise + affine in registers and write the output once.  Every
-// workgroup that needs a group's statistics merges the same partials in the
-// same order.
+// Sum over aligned groups of w lanes (w a power of two up to 64, uniform)
+__device__ __forceinline__ float group_lane_sum(float v, int w) {
+  switch (w) {
+    case 2: return lane_sum<1>(v);
+    case 4: return lane_sum<3>(v);
+    case 8: return lane_sum<7>(v);
+    case 16: return lane_sum<15>(v);
+    case 32: return lane_sum<31>(v);
+    case 64: return lane_sum<63>(v);
+    default: return v;
+  }
+}
+
+// Persistent-kernel epilogue: bias and partial statistics, the sample
+// barrier, the fixed-order merge of the sample's partials for this tile's
+// groups (GroupNorm) or positions (LayerNorm over channels), then normalise +
+// affine in registers and write the output once.  Every workgroup that needs
+// a group's statistics merges the same partials in the same order.
+//
+// GroupNorm partials: one (mean, M2) per chunk of pg = min(C_out/G, 64)
+// channels of a group per position tile, at part[((n * C_out/pg + chunk) *
+// n_ttiles + ttile) * 2], so a group's partials are one contiguous run.  Every
+// channel of a tile has the same count (the tile's valid positions), so the
+// chunk's mean is the mean of its channel means and its M2 the sum of the
+// channel M2s plus count * (channel mean - chunk mean)^2 (exact).
+// LayerNorm partials: as on the split path, per position and channel tile.
 template <int WM, int EPI>
 __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
                                                     f32x4 (&acc)[WM][WN], int64_t n,
@@ -109,8 +129,37 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t T_out = a.T_out;
   constexpr bool gn = EPI == EPI_GN_FUSED;
-  conv_epilogue<WM, WN, WGM, WGN>(a, gn ? EPI_GN_PART : EPI_LN_PART, acc, n, t0, c0, ttile,
-                                  ctile, wm, wn, red, true, false);
+  const int cpg = gn ? (int)(a.C_out / a.G) : 0;
+  const int pg = cpg < 64 ? cpg : 64;  // channels per GroupNorm partial
+  if constexpr (gn) {
+    float bias[WN];
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn) {
+      const int c = c0 + wn * WN * 16 + jn * 16 + lr;
+      bias[jn] = (a.bias != nullptr && c < a.C_out) ? a.bias[c] : 0.f;
+    }
+#pragma unroll
+    for (int jn = 0; jn < WN; ++jn)
+#pragma unroll
+      for (int i = 0; i < WM; ++i) acc[i][jn] += bias[jn];
+    gn_wave_channel_stats<WM, WN, WGM, WGN>(a, acc, t0, wm, wn, red, true);
+    __syncthreads();
+    if (tid < TN) {  // two whole waves: every lane takes part in the lane sums
+      const int c = c0 + tid;
+      Stats st = red[tid];
+#pragma unroll
+      for (int w = 1; w < WGM; ++w) st = stats_merge(st, red[w * TN + tid]);
+      const float mg = group_lane_sum(st.mean, pg) / (float)pg;
+      const float dv = st.mean - mg;
+      const float q = group_lane_sum(st.m2 + st.n * dv * dv, pg);
+      if ((tid % pg) == 0 && c < a.C_out)
+        store_partial(a.part + ((n * (a.C_out / pg) + c / pg) * a.n_ttiles + ttile) * 2, mg, q,
+                      true);
+    }
+  } else {
+    conv_epilogue<WM, WN, WGM, WGN>(a, EPI_LN_PART, acc, n, t0, c0, ttile, ctile, wm, wn, red,
+                                    true, false);
+  }
   // an incomplete set of partials (a wait that gave up) yields NaN statistics,
   // hence a NaN output, never a plausible wrong one
   const float poison =
@@ -119,34 +168,34 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
 
   float* mean_s = lds;        // merged statistics of this tile
   float* rstd_s = lds + 512;
-  Stats* tree = (Stats*)(lds + 1024);
   if constexpr (gn) {
-    // groups of cpg channels, cpg dividing TN: ng groups per tile, S threads each
-    // (cpg divides TN, or TN divides cpg: then the whole tile is one group)
-    const int cpg = (int)(a.C_out / a.G);
-    const int ng = cpg >= TN ? 1 : TN / cpg, S = NTHR / ng;
+    // ng groups in this tile (cpg divides TN, or TN divides cpg: then the
+    // whole tile is one group), P partials per group, S lanes of one wave per
+    // group (a power of two): lane u folds partials u, u + S, ... in order,
+    // then a fixed tree over the S lanes (lane u takes lane u + h)
+    const int ng = cpg >= TN ? 1 : TN / cpg;
+    const int P = (cpg / pg) * a.n_ttiles;
+    int S = 1;
+    while (S < P && S < 64 && 2 * S * ng <= NTHR) S *= 2;
     const int k = tid / S, u = tid - k * S;
     const int64_t g = (int64_t)(c0 / cpg) + k;
     Stats st = {0.f, 0.f, 0.f};
-    if (g < a.G) {
-      const int64_t P = (int64_t)cpg * a.n_ttiles;
-      const float* base = a.part + ((n * a.C_out + g * cpg) * a.n_ttiles) * 2;
-      for (int64_t p = u; p < P; p += S) {
-        const int tt = (int)(p % a.n_ttiles);
+    if (k < ng && g < a.G) {
+      const float* base = a.part + ((n * (a.C_out / pg) + g * (cpg / pg)) * a.n_ttiles) * 2;
+      for (int p = u; p < P; p += S) {
+        const int tt = p % a.n_ttiles;
         const int64_t cntl = T_out - (int64_t)tt * TM;
-        const float cnt = (float)(cntl < TM ? cntl : TM);
+        const float cnt = (float)pg * (float)(cntl < TM ? cntl : TM);
         const f32x2 v = load_partial_coherent(base + 2 * p);
         st = stats_merge(st, Stats{cnt, v[0], v[1]});
       }
     }
-    tree[tid] = st;
-    __syncthreads();
     for (int h = S / 2; h > 0; h >>= 1) {
-      if (u < h) tree[tid] = stats_merge(tree[tid], tree[tid + h]);
-      __syncthreads();
+      const Stats o = {__shfl_xor(st.n, h), __shfl_xor(st.mean, h), __shfl_xor(st.m2, h)};
+      if (u < h) st = stats_merge(st, o);
     }
-    if (u == 0) {
-      const Stats r = tree[tid];
+    if (u == 0 && k < ng) {
+      const Stats r = st;
       const float mu = r.mean + poison, rs = 1.0f / sqrtf(r.m2 / r.n + a.eps) + poison;
       mean_s[k] = mu;
       rstd_s[k] = rs;
