@@ -29,6 +29,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libconv1d_gn.so")
 
 C1G_F32, C1G_BF16 = 0, 1
+LAYOUT_NCL, LAYOUT_NLC = 0, 1
 NORM_NONE, NORM_GROUP, NORM_LAYER_CHANNELS = 0, 1, 2
 EPI_NONE, EPI_ROWMIN_BIAS = 0, 1
 FLAG_NO_PERSISTENT = 1
@@ -49,7 +50,7 @@ class ConvDesc(ctypes.Structure):
                 ("T", ctypes.c_int64), ("K", ctypes.c_int32), ("stride", ctypes.c_int32),
                 ("dilation", ctypes.c_int32), ("pad_left", ctypes.c_int32),
                 ("pad_right", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("x_layout", ctypes.c_int32)]
 
 
 class NormDesc(ctypes.Structure):
@@ -121,9 +122,10 @@ def _pads(K, dilation, padding, pad_left, pad_right, causal):
 
 
 def make_desc(N, C_in, C_out, T, K, *, stride=1, dilation=1, padding=0, pad_left=None,
-              pad_right=None, causal=False, dtype=C1G_F32, out_dtype=C1G_F32) -> ConvDesc:
+              pad_right=None, causal=False, dtype=C1G_F32, out_dtype=C1G_F32,
+              x_layout=LAYOUT_NCL) -> ConvDesc:
     pl, pr = _pads(K, dilation, padding, pad_left, pad_right, causal)
-    return ConvDesc(N, C_in, C_out, T, K, stride, dilation, pl, pr, dtype, out_dtype)
+    return ConvDesc(N, C_in, C_out, T, K, stride, dilation, pl, pr, dtype, out_dtype, x_layout)
 
 
 _DT_CODE = {torch.float32: C1G_F32, torch.bfloat16: C1G_BF16}
@@ -203,9 +205,10 @@ def _raise(status, where):
 
 
 def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
-                out_dtype=torch.float32):
+                out_dtype=torch.float32, channels_last=False):
     if x.dim() != 3 or w.dim() != 3:
-        raise ValueError("x must be [N, C_in, T] and w [C_out, C_in, K]")
+        raise ValueError("x must be [N, C_in, T] ([N, T, C_in] with channels_last) and w "
+                         "[C_out, C_in, K]")
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
     if x.dtype == torch.float32:
@@ -216,24 +219,30 @@ def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
         raise TypeError("x must be float32 or bfloat16")
     _need(x, "x", None, x.device)
     _need(w, "w", x.dtype, x.device)
-    N, C_in, T = x.shape
+    if channels_last:
+        N, T, C_in = x.shape
+    else:
+        N, C_in, T = x.shape
     C_out, C_in_w, K = w.shape
     if C_in_w != C_in:
         raise ValueError("x and w disagree on C_in")
     desc = make_desc(N, C_in, C_out, T, K, stride=stride, dilation=dilation, padding=padding,
                      pad_left=pad_left, pad_right=pad_right, causal=causal, dtype=dt,
-                     out_dtype=_DT_CODE[out_dtype])
+                     out_dtype=_DT_CODE[out_dtype],
+                     x_layout=LAYOUT_NLC if channels_last else LAYOUT_NCL)
     return desc
 
 
 # ----------------------------------------------------------------- entry points
 def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                    causal=False, dilation=1, out=None, out_dtype=torch.float32,
-                   workspace=None):
-    """y = conv1d(x, w) + bias, output [N, C_out, T_out] (fp32 or bf16)."""
+                   channels_last=False, workspace=None):
+    """y = conv1d(x, w) + bias, output [N, C_out, T_out] (fp32 or bf16); x is
+    [N, C_in, T], or [N, T, C_in] with channels_last=True."""
     lib = load_library()
     odt = _out_dtype(out, out_dtype)
-    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt)
+    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt,
+                       channels_last)
     _need(bias, "bias", torch.float32, x.device)
     T_out = lib.c1g_out_len(ctypes.byref(desc))
     if T_out < 1:
@@ -255,15 +264,17 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
                       causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                       beta=None, rowmin_bias=None, return_stats=False, out=None,
                       out_dtype=torch.float32, persistent=True, one_launch=False,
-                      workspace=None):
+                      channels_last=False, workspace=None):
     """conv -> GroupNorm / LayerNorm over channels / none -> optional row-min + bias.
 
-    Returns out [N, C_out, T_out] (fp32, or bf16 with out_dtype=torch.bfloat16
-    or a bf16 ``out``), or (out, mean, rstd) with return_stats=True (fp32
-    mean/rstd [N, G] for GroupNorm, [N, T_out] for the channel LayerNorm)."""
+    x is [N, C_in, T], or [N, T, C_in] with channels_last=True.  Returns out
+    [N, C_out, T_out] (fp32, or bf16 with out_dtype=torch.bfloat16 or a bf16
+    ``out``), or (out, mean, rstd) with return_stats=True (fp32 mean/rstd
+    [N, G] for GroupNorm, [N, T_out] for the channel LayerNorm)."""
     lib = load_library()
     odt = _out_dtype(out, out_dtype)
-    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt)
+    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt,
+                       channels_last)
     nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent, one_launch)
     for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
         _need(t, nm, torch.float32, x.device)
@@ -343,11 +354,11 @@ class PreparedConv1dGN:
     def __init__(self, x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                  causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                  beta=None, rowmin_bias=None, out=None, out_dtype=torch.float32, mean=None,
-                 rstd=None, persistent=True, one_launch=False):
+                 rstd=None, persistent=True, one_launch=False, channels_last=False):
         lib = load_library()
         odt = _out_dtype(out, out_dtype)
         self.desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
-                                odt)
+                                odt, channels_last)
         self.norm = make_norm(norm, groups, eps, rowmin_bias is not None, persistent,
                               one_launch)
         for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"),

@@ -32,6 +32,8 @@ struct Plan {
   size_t off_pack = 0, off_part = 0, off_mean = 0, off_rstd = 0, off_y = 0, total = 0;
   size_t off_ximg = 0;  // bf16 conv: channels-last input image
   size_t off_sync = 0;  // persistent route: per-round arrival counters
+  bool x_nlc = false;   // channels-last x with T > 1 (T == 1: the same bytes as [N, C_in, 1])
+  size_t off_xt = 0;    // fp32 and x_nlc: x transposed to [N, C_in, T] (at offset 0)
   int64_t T_img = 0;
 };
 
@@ -61,6 +63,16 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
     return p;
   }
   p.out_bf16 = d->out_dtype == C1G_BF16;
+  if (d->x_layout != C1G_LAYOUT_NCL && d->x_layout != C1G_LAYOUT_NLC) {
+    p.status = C1G_ERR_INVALID_ARG;
+    return p;
+  }
+  p.x_nlc = d->x_layout == C1G_LAYOUT_NLC && d->T > 1;
+  // fp32 kernels read x position-contiguous: a channels-last x is transposed
+  // into the front of the workspace first
+  const size_t xt_bytes =
+      (p.x_nlc && !p.bf16) ? align_up((size_t)d->N * d->C_in * d->T * sizeof(float)) : 0;
+  if (xt_bytes && (d->C_in + 63) / 64 > 65535) { p.status = C1G_ERR_UNSUPPORTED; return p; }
   if (nd) {
     p.norm = nd->norm;
     p.epi = nd->epilogue;
@@ -91,7 +103,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   if (!p.bf16 && want_gn && p.epi == C1G_EPI_NONE &&
       fused_gn_supported(d->C_in, d->C_out, nd->G, p.T_out, d->stride, d->K, d->dilation)) {
     p.route = R_FUSED;
-    p.total = 0;
+    p.total = xt_bytes;
     return p;
   }
   // K = 1, T = 1 (a Linear layer) in bf16: plain GEMM over rows n
@@ -161,7 +173,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
     if (tn % cpg == 0 || cpg % tn == 0) p.route = R_PERSIST;
   }
 
-  size_t off = 0;
+  size_t off = xt_bytes;
   p.off_pack = off;
   off = align_up(off + pack_bytes);
   p.off_ximg = off;
@@ -224,14 +236,19 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
              const float* bias, void* y, char* ws, int epi, hipStream_t s,
              const c1g_norm_desc* nd = nullptr, const float* gamma = nullptr,
              const float* beta = nullptr, float* mean_out = nullptr, float* rstd_out = nullptr) {
-  ConvArgs a = conv_args(p, d, x, bias, y, ws);
   hipError_t e;
+  if (p.x_nlc && !p.bf16) {
+    e = transpose_nlc_f32((const float*)x, (float*)(ws + p.off_xt), d->N, d->T, d->C_in, s);
+    if (e != hipSuccess) return C1G_ERR_HIP;
+    x = ws + p.off_xt;
+  }
+  ConvArgs a = conv_args(p, d, x, bias, y, ws);
   if (p.bf16) {
     e = conv_bf16_pack((const uint16_t*)w, (uint16_t*)(ws + p.off_pack), d->C_in, d->C_out,
                        d->K, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     e = conv_bf16_pack_x((const uint16_t*)x, (uint16_t*)(ws + p.off_ximg), d->N, d->C_in, d->T,
-                         d->pad_left, p.T_img, s);
+                         d->pad_left, p.T_img, p.x_nlc, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
       a.gamma = gamma;
@@ -448,6 +465,12 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
   char* wsb = (char*)ws;
 
   if (p.route == R_FUSED) {
+    if (p.x_nlc) {
+      if (transpose_nlc_f32((const float*)x, (float*)(wsb + p.off_xt), d->N, d->T, d->C_in, s) !=
+          hipSuccess)
+        return C1G_ERR_HIP;
+      x = wsb + p.off_xt;
+    }
     FusedArgs a;
     a.x = (const float*)x;
     a.w = (const float*)w;

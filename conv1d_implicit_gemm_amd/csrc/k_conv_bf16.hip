@@ -555,6 +555,40 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_kernel(const u16* __rest
   }
 }
 
+// The same image from a channels-last x [N, T, C_in]: every in-range image
+// row is one input row padded with zeros to cpad channels, the others are
+// zero.  A thread writes 8 channels (16 bytes) of a row, so consecutive lanes
+// read and write consecutive 16-byte pieces of the same rows.  vec: C_in % 8
+// == 0 and x 16-byte aligned (every piece is one aligned load).
+__global__ __launch_bounds__(256) void conv_bf16_pack_x_nlc_kernel(const u16* __restrict__ x,
+                                                                  u16* __restrict__ ximg,
+                                                                  int64_t C_in, int64_t T,
+                                                                  int64_t cpad, int64_t T_img,
+                                                                  int pad_left, int64_t total,
+                                                                  int vec) {
+  const int64_t per_row = cpad / 8;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = idx / per_row;  // n * T_img + tp
+    const int64_t c = 8 * (idx - row * per_row);
+    const int64_t n = row / T_img, t = row - n * T_img - pad_left;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t >= 0 && t < T && c < C_in) {
+      const u16* src = x + (n * T + t) * C_in + c;
+      if (vec) {
+        v = *(const u32x4*)src;
+      } else {
+        u16 e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = c + e < C_in ? src[e] : (u16)0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = (uint32_t)e8[2 * k] | ((uint32_t)e8[2 * k + 1] << 16);
+      }
+    }
+    *(u32x4*)(ximg + row * cpad + c) = v;
+  }
+}
+
 template <int WM, int KT, int XR>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
   if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
@@ -637,8 +671,17 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
 }
 
 hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_t C_in,
-                            int64_t T, int pad_left, int64_t T_img, hipStream_t s) {
+                            int64_t T, int pad_left, int64_t T_img, bool nlc, hipStream_t s) {
   const int64_t cpad = (C_in + CK - 1) / CK * CK;
+  if (nlc) {
+    const int64_t total = N * T_img * (cpad / 8);
+    const int64_t blocks = (total + 255) / 256;
+    const int vec = (C_in % 8 == 0) && ((((uintptr_t)x) & 15) == 0);
+    hipLaunchKernelGGL(conv_bf16_pack_x_nlc_kernel,
+                       dim3((unsigned)(blocks < 1048576 ? blocks : 1048576)), dim3(256), 0, s, x,
+                       ximg, C_in, T, cpad, T_img, pad_left, total, vec);
+    return hipGetLastError();
+  }
   const int64_t A = (pad_left + 7) / 8 * 8;  // first input position of tile 0: -A
   const int fast = (T % 8 == 0) && ((((uintptr_t)x) & 15) == 0);
   // tiles of 64 positions cover input positions -A .. T_img - 1 - pad_left

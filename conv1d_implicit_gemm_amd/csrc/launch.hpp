@@ -70,8 +70,9 @@ int conv_bf16_tile_m(int stride, int K, int dilation);  // 0 if unsupported
 // channels-last input image: rows per sample, bytes, and the repack of x
 int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation);
 size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img);
+// x [N, C_in, T], or (nlc) channels-last x [N, T, C_in]
 hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_t C_in,
-                            int64_t T, int pad_left, int64_t T_img, hipStream_t s);
+                            int64_t T, int pad_left, int64_t T_img, bool nlc, hipStream_t s);
 size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K);
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
                           hipStream_t s);
@@ -110,6 +111,10 @@ struct GemmArgs {
 int gemm_bf16_tile_c();
 int gemm_bf16_tile_n();
 hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s);
+// channels-last fp32 x [N, T, C] -> xt [N, C, T] (k_layout.hip); needs
+// ceil(C / 64) <= 65535
+hipError_t transpose_nlc_f32(const float* x, float* xt, int64_t N, int64_t T, int64_t C,
+                             hipStream_t s);
 // GEMM + GroupNorm + row-min + bias2 in one cooperative launch: workgroups the
 // device keeps resident at once with the GN_ROWMIN_ONE kernel (0 on error);
 // the launch needs n_ctiles * n_ntiles of them and n_ntiles + 1 zeroed

@@ -49,6 +49,7 @@ class Workload:
     rowmin_bias: bool = False     # per-row min over channels + bias2 broadcast
     persistent: bool = True       # allow the persistent conv + normalisation route
     one_launch: bool = False      # Linear + GroupNorm + row-min as one cooperative launch
+    channels_last: bool = False   # hand x to the library as [N, T, C_in]
     w_bound: Optional[float] = None
 
     @property

@@ -57,6 +57,12 @@ extern "C" {
 /* element type of x and w, and of y / out */
 enum c1g_dtype { C1G_F32 = 0, C1G_BF16 = 1 };
 
+/* memory layout of x */
+enum c1g_layout {
+  C1G_LAYOUT_NCL = 0,          /* x [N, C_in, T]: positions contiguous (default)      */
+  C1G_LAYOUT_NLC = 1           /* x [N, T, C_in]: channels contiguous (channels-last)  */
+};
+
 /* normalisation applied to the convolution output y */
 enum c1g_norm {
   C1G_NORM_NONE = 0,           /* out = y                                            */
@@ -81,7 +87,8 @@ enum c1g_status {
 };
 
 /* Geometry of the convolution.
- *   x [N, C_in, T], w [C_out, C_in, K], y/out [N, C_out, T_out] with
+ *   x [N, C_in, T] (or [N, T, C_in] with x_layout = C1G_LAYOUT_NLC),
+ *   w [C_out, C_in, K], y/out [N, C_out, T_out] with
  *   T_out = floor((T + pad_left + pad_right - dilation*(K-1) - 1) / stride) + 1
  *   ("Kimi-K2.6 l2_p35", output-length formula; symmetric padding p is
  *   pad_left = pad_right = p; causal per "Kimi-K2.6 l1_p5" is
@@ -95,6 +102,12 @@ typedef struct c1g_conv_desc {
   int32_t dtype;               /* enum c1g_dtype of x and w */
   int32_t out_dtype;           /* enum c1g_dtype of y (conv1d_forward) and out
                                   (conv1d_gn_forward); 0 = fp32 */
+  int32_t x_layout;            /* enum c1g_layout of x; 0 = [N, C_in, T].  The
+                                  result is the same, bit for bit, in either layout:
+                                  bf16 routes build their channels-last input image
+                                  from it directly, fp32 routes transpose it once
+                                  into the workspace (counted by the size queries);
+                                  with T = 1 the two layouts are the same bytes */
 } c1g_conv_desc;
 
 /* What follows the convolution in conv1d_gn_forward. */

@@ -31,6 +31,8 @@ def run_library(wl: Workload, inp: dict, *, return_stats=False, poison=True):
     """conv1d_gn_forward (or conv1d_forward when the workload has no norm
     and no epilogue) on device copies of the inputs."""
     x, w = to_dev(inp["x"]), to_dev(inp["w"])
+    if wl.channels_last:  # the same values, laid out [N, T, C_in]
+        x = x.transpose(1, 2).contiguous()
     b, ga, be, b2 = (to_dev(inp[k]) for k in ("bias", "gamma", "beta", "bias2"))
     T_out = c1g.out_len(c1g.make_desc(wl.N, wl.C_in, wl.C_out, wl.T, wl.K, stride=wl.stride,
                                       dilation=wl.dilation, pad_left=wl.pad_left,
@@ -40,14 +42,16 @@ def run_library(wl: Workload, inp: dict, *, return_stats=False, poison=True):
                      dtype=odt)
     if wl.norm is None and not wl.rowmin_bias:
         c1g.conv1d_forward(x, w, b, stride=wl.stride, dilation=wl.dilation,
-                           pad_left=wl.pad_left, pad_right=wl.pad_right, out=out)
+                           pad_left=wl.pad_left, pad_right=wl.pad_right, out=out,
+                           channels_last=wl.channels_last)
         res = (out, None, None)
     else:
         res = c1g.conv1d_gn_forward(x, w, b, stride=wl.stride, dilation=wl.dilation,
                                     pad_left=wl.pad_left, pad_right=wl.pad_right,
                                     norm=wl.norm, groups=wl.G, eps=wl.eps, gamma=ga, beta=be,
                                     rowmin_bias=b2, return_stats=True, out=out,
-                                    persistent=wl.persistent, one_launch=wl.one_launch)
+                                    persistent=wl.persistent, one_launch=wl.one_launch,
+                                    channels_last=wl.channels_last)
     torch.cuda.synchronize()
     return res if return_stats else res[0]
 
@@ -79,7 +83,8 @@ def library_route(wl: Workload):
     desc = c1g.make_desc(wl.N, wl.C_in, wl.C_out, wl.T, wl.K, stride=wl.stride,
                          dilation=wl.dilation, pad_left=wl.pad_left, pad_right=wl.pad_right,
                          dtype=c1g.C1G_BF16 if wl.dtype == "bf16" else c1g.C1G_F32,
-                         out_dtype=c1g.C1G_BF16 if wl.out_dtype == "bf16" else c1g.C1G_F32)
+                         out_dtype=c1g.C1G_BF16 if wl.out_dtype == "bf16" else c1g.C1G_F32,
+                         x_layout=c1g.LAYOUT_NLC if wl.channels_last else c1g.LAYOUT_NCL)
     return c1g.route(desc, c1g.make_norm(wl.norm, wl.G, wl.eps, wl.rowmin_bias, wl.persistent,
                                          wl.one_launch))
 

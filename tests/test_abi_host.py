@@ -49,11 +49,11 @@ def test_out_len_matches_oracle(T, K, s, d, pl, pr):
 
 def _desc(**kw):
     base = dict(N=2, C_in=16, C_out=32, T=256, K=3, stride=1, dilation=1, pad_left=1,
-                pad_right=1, dtype=c1g.C1G_F32, out_dtype=c1g.C1G_F32)
+                pad_right=1, dtype=c1g.C1G_F32, out_dtype=c1g.C1G_F32, x_layout=0)
     base.update(kw)
     return c1g.ConvDesc(base["N"], base["C_in"], base["C_out"], base["T"], base["K"],
                         base["stride"], base["dilation"], base["pad_left"], base["pad_right"],
-                        base["dtype"], base["out_dtype"])
+                        base["dtype"], base["out_dtype"], base["x_layout"])
 
 
 @pytest.mark.parametrize("kw", [dict(N=0), dict(C_in=0), dict(C_out=0), dict(T=0), dict(K=0),
@@ -218,3 +218,42 @@ def test_bf16_output_workspace():
                    c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 1)):
             assert c1g.route(a, nd) == c1g.route(b, nd) != "gemm_rows"
             assert c1g.conv1d_gn_workspace_size(a, nd) == c1g.conv1d_gn_workspace_size(b, nd)
+
+
+def test_conv_desc_abi_size():
+    """c1g_conv_desc: four int64 fields then eight int32 fields, 64 bytes."""
+    assert ctypes.sizeof(c1g.ConvDesc) == 64
+    assert c1g.ConvDesc.x_layout.offset == 60
+
+
+def test_channels_last_planning():
+    """A channels-last x: an invalid layout code is an argument error; fp32
+    routes add x transposed ([N, C_in, T] fp32, 256-byte aligned) to the front
+    of the workspace, including the otherwise workspace-free fused route;
+    bf16 routes build their input image from either layout at no extra size;
+    with T = 1 the layouts are the same bytes and nothing changes."""
+    assert c1g.check(_desc(x_layout=2)) == 1
+    assert c1g.check(_desc(x_layout=-1)) == 1
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    cases = [dict(), dict(C_out=24), dict(N=3, C_in=40, C_out=64, T=513, K=4, pad_left=3,
+                                           pad_right=0)]
+    for kw in cases:
+        a, b = _desc(**kw), _desc(x_layout=c1g.LAYOUT_NLC, **kw)
+        xt = -(-(a.N * a.C_in * a.T * 4) // 256) * 256
+        for nd in (gn, None):
+            if nd is None:
+                wa, wb = c1g.conv1d_workspace_size(a), c1g.conv1d_workspace_size(b)
+            else:
+                assert c1g.route(a, nd) == c1g.route(b, nd)
+                wa, wb = c1g.conv1d_gn_workspace_size(a, nd), c1g.conv1d_gn_workspace_size(b, nd)
+            assert wb == wa + xt, (kw, nd)
+    for kw in (dict(dtype=c1g.C1G_BF16), dict(dtype=c1g.C1G_BF16, C_out=256, T=2000)):
+        a, b = _desc(**kw), _desc(x_layout=c1g.LAYOUT_NLC, **kw)
+        assert c1g.route(a, gn) == c1g.route(b, gn)
+        assert c1g.conv1d_gn_workspace_size(a, gn) == c1g.conv1d_gn_workspace_size(b, gn)
+        assert c1g.conv1d_workspace_size(a) == c1g.conv1d_workspace_size(b)
+    lin = dict(N=64, C_in=256, C_out=512, T=1, K=1, pad_left=0, pad_right=0)
+    for dt in (c1g.C1G_F32, c1g.C1G_BF16):
+        a, b = _desc(dtype=dt, **lin), _desc(dtype=dt, x_layout=c1g.LAYOUT_NLC, **lin)
+        assert c1g.route(a, gn) == c1g.route(b, gn)
+        assert c1g.conv1d_gn_workspace_size(a, gn) == c1g.conv1d_gn_workspace_size(b, gn)

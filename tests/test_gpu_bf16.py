@@ -199,3 +199,39 @@ def test_persistent_determinism():
     announce("persistent determinism", wl.name)
     inp = make_inputs(wl, 5)
     assert torch.equal(run_library(wl, inp), run_library(wl, inp))
+
+
+# Generality at scale: stride > 1, 8 taps at dilation 2, groups wider than 32
+# channels (one group spanning channel tiles; a width that does not tile the
+# 128-channel tiles, hence the split route), channels-last input; the oracle
+# checks the first and the last sample of each.
+SCALE_CASES = [
+    (W("scale_bf16_stride2_gn", N=12, C_in=512, C_out=1024, T=8192, K=5, stride=2, pad_left=2,
+       pad_right=2, G=32, **BF), "fused_persistent"),
+    (W("scale_bf16_k8d2_gn", N=8, C_in=256, C_out=512, T=4096, K=8, dilation=2, pad_left=7,
+       pad_right=7, G=16, **BF), "fused_persistent"),
+    (W("scale_bf16_cpg256_gn", N=8, C_in=512, C_out=1024, T=4096, K=5, dilation=2, pad_left=4,
+       pad_right=4, G=4, **BF), "fused_persistent"),
+    (W("scale_bf16_cpg48_gn_split", N=6, C_in=256, C_out=1536, T=4096, K=3, pad_left=1,
+       pad_right=1, G=32, **BF), "split"),
+    (W("scale_bf16_stride3_ln_nlc", N=6, C_in=384, C_out=768, T=6000, K=4, stride=3,
+       pad_left=3, norm="layer_channels", channels_last=True, **BF), "fused_persistent"),
+    (W("scale_f32_stride2_gn", N=6, C_in=256, C_out=256, T=8192, K=4, stride=2, pad_left=3,
+       G=32), "split"),
+]
+
+
+@pytest.mark.parametrize("wl,route", SCALE_CASES, ids=lambda c: getattr(c, "name", c))
+def test_generality_at_scale_sampled(wl, route):
+    from tests.gpu_util import library_route, tol_for
+    assert library_route(wl) == route
+    announce("scale", wl.name)
+    inp = make_inputs(wl, 0)
+    got, mean, rstd = run_library(wl, inp, return_stats=True)
+    for n in (0, wl.N - 1):
+        ref = run_oracle(wl, inp, n_slice=slice(n, n + 1))
+        err = max_abs_err(got[n:n + 1], ref["out"])
+        assert err <= tol_for(wl), (n, err)
+        assert max_abs_err(mean[n:n + 1], ref["mean"]) <= 1e-4
+        r = rstd[n:n + 1].cpu().double().numpy()
+        assert float(np.max(np.abs(r / ref["rstd"] - 1))) <= 1e-4
