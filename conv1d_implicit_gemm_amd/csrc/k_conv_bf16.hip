@@ -514,8 +514,10 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 // channels.  Lane l of a wave takes channel group l % 8 and position group
 // l / 8 of a 64 x 64 tile, so both the loads (8 lanes per channel row) and the
 // stores (8 lanes per image row) come in 128-byte runs.  The tile's input
-// positions start at a multiple of 8 (t0 = 64 * bx - A, A = pad_left rounded
-// up to 8), so in-range blocks load with aligned 16-byte loads when T % 8 == 0.
+// positions start at a multiple of 64 (t0 = 64 * bx - A, A = pad_left rounded
+// up to 64), so in-range blocks load with aligned 16-byte loads when T % 8 == 0
+// and, when T % 64 == 0, each 128-byte run is one whole 128-byte line (a run
+// straddling two lines would fetch both: twice the bytes of x).
 __global__ __launch_bounds__(256) void conv_bf16_pack_x_kernel(const u16* __restrict__ x,
                                                               u16* __restrict__ ximg,
                                                               int64_t C_in, int64_t T,
@@ -682,7 +684,9 @@ hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_
                        ximg, C_in, T, cpad, T_img, pad_left, total, vec);
     return hipGetLastError();
   }
-  const int64_t A = (pad_left + 7) / 8 * 8;  // first input position of tile 0: -A
+  // first input position of tile 0: -A, a multiple of 64 positions, so each
+  // lane group's 128-byte run of a channel row is one whole 128-byte line
+  const int64_t A = (pad_left + 63) / 64 * 64;
   const int fast = (T % 8 == 0) && ((((uintptr_t)x) & 15) == 0);
   // tiles of 64 positions cover input positions -A .. T_img - 1 - pad_left
   dim3 grid((unsigned)((T_img - pad_left + A + 63) / 64), (unsigned)((cpad + 255) / 256),
