@@ -49,6 +49,17 @@ GN_CASES = [
     W("fused_no_affine_no_bias", N=1, C_in=4, C_out=8, T=64, K=3, G=2, bias=False,
       affine=False),
     W("fused_t1", N=4, C_in=40, C_out=32, T=1, K=1, G=4),
+    # more of the fused route: a partial last 16-channel chunk, a single chunk,
+    # 8 taps at dilation 2 (causal), dilation 3 with 13 chunks, many chunks,
+    # and a halo of 18 positions
+    W("fused_cin20_t512", N=2, C_in=20, C_out=32, T=512, K=3, pad_left=1, pad_right=1, G=8),
+    W("fused_one_chunk_k5", N=2, C_in=5, C_out=16, T=64, K=5, pad_left=2, pad_right=2, G=4),
+    W("fused_k8d2_causal", N=1, C_in=16, C_out=16, T=256, K=8, dilation=2, pad_left=14, G=2),
+    W("fused_k5d3_cin100", N=2, C_in=100, C_out=32, T=1024, K=5, dilation=3, pad_left=6,
+      pad_right=6, G=4),
+    W("fused_cin256", N=2, C_in=256, C_out=32, T=1024, K=3, pad_left=1, pad_right=1, G=4),
+    W("fused_k4d6_halo18", N=1, C_in=16, C_out=16, T=1024, K=4, dilation=6, pad_left=9,
+      pad_right=9, G=2),
     # split route: C_out/G not a divisor of 16, or T_out beyond the on-chip slab
     W("split_cpg3", N=2, C_in=20, C_out=24, T=300, K=3, pad_left=1, pad_right=1, G=8),
     W("split_long", N=2, C_in=16, C_out=32, T=1500, K=3, pad_left=1, pad_right=1, G=8),
