@@ -8,10 +8,26 @@
 // reach the point of coherence of all XCDs, so no cache-wide flush is needed.
 #pragma once
 
+#include <cstdlib>
+
 #include "common.hpp"
 
 namespace c1g {
 namespace {
+
+// Polls before a barrier wait gives up: ~0.1 s, far beyond any legitimate
+// wait.  The environment variable C1G_BARRIER_SPINS overrides it (read at each
+// launch), which lets a test force the give-up path with every kernel still
+// ending normally.
+inline unsigned barrier_poll_limit() {
+  const char* e = std::getenv("C1G_BARRIER_SPINS");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    if (end && *end == '\0' && v <= (1ul << 22)) return (unsigned)v;
+  }
+  return 1u << 22;
+}
 
 // Every thread of the workgroup returns once `expect` workgroups have arrived
 // on *ctr (this one included).  Waits for this wave's outstanding memory
@@ -20,7 +36,8 @@ namespace {
 // a bound no legitimate wait approaches (in a cooperative launch every
 // workgroup is resident), records that in *fault and returns false, so no
 // path can hang; the caller then poisons what depended on the others.
-__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault) {
+__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault,
+                                               unsigned max_polls) {
   __shared__ int complete;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are done
   __syncthreads();
@@ -29,7 +46,7 @@ __device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, u
     unsigned spins = 0;
     int ok = 1;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
-      if (++spins > (1u << 22)) {  // ~0.1 s of polling
+      if (++spins > max_polls) {
         __hip_atomic_store(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = 0;
         break;

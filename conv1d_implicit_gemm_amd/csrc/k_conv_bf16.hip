@@ -163,7 +163,7 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
   // an incomplete set of partials (a wait that gave up) yields NaN statistics,
   // hence a NaN output, never a plausible wrong one
   const float poison =
-      sample_barrier(a.sync + (int64_t)round * a.spr + slot, (unsigned)tps, a.fault)
+      sample_barrier(a.sync + (int64_t)round * a.spr + slot, (unsigned)tps, a.fault, a.polls)
           ? 0.f : __builtin_nanf("");
 
   float* mean_s = lds;        // merged statistics of this tile
@@ -754,6 +754,7 @@ hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s) {
   // counters (and the fault word just after them) start at zero
   const int64_t words = (int64_t)a.spr * a.rounds + 1;
   a.fault = a.sync + (words - 1);
+  a.polls = barrier_poll_limit();
   hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
                      a.sync, words);
   hipError_t e = hipGetLastError();

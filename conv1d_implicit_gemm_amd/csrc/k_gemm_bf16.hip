@@ -437,7 +437,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       }
     }
     if constexpr (EPI == GEMM_GN_ROWMIN_ONE) {
-      const bool ok = sample_barrier(a.sync + ntile, (unsigned)a.n_ctiles, a.fault);
+      const bool ok = sample_barrier(a.sync + ntile, (unsigned)a.n_ctiles, a.fault, a.polls);
       // the rows' minima over all c-tiles (NaN if a wait gave up)
       float* rowm = red + KSPLIT * WGC * BN;
       if (tid < BN) {
@@ -550,6 +550,7 @@ hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, hipStream_t s) {
   // one arrival counter per row block, then the fault word
   const int64_t words = (int64_t)a.n_ntiles + 1;
   a.fault = a.sync + a.n_ntiles;
+  a.polls = barrier_poll_limit();
   hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
                      a.sync, words);
   hipError_t e = hipGetLastError();

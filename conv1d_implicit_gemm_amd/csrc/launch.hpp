@@ -46,6 +46,7 @@ struct ConvArgs {
   int32_t spr;         // samples per round (spr * tiles per sample workgroups)
   int32_t rounds;      // ceil(N / spr)
   unsigned* fault;     // set when a barrier wait gives up (never on a full GPU)
+  uint32_t polls;      // polls before a barrier wait gives up (set by the launcher)
 };
 
 // ---- fp32 split-path convolution (k_conv_f32.hip)
@@ -103,6 +104,7 @@ struct GemmArgs {
   void* out;           // GN_ROWMIN_ONE: [N, C_out], fp32 or (out_bf16) bf16
   unsigned* sync;      // GN_ROWMIN_ONE: n_ntiles arrival counters, zeroed by the launcher
   unsigned* fault;     // set when a barrier wait gives up (never on a full GPU)
+  uint32_t polls;      // polls before a barrier wait gives up (set by the launcher)
   int64_t N, C_in, C_out;
   int32_t G, n_ctiles, n_ntiles;
   float eps;

@@ -237,6 +237,9 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
  *                        writes out once (y never reaches memory).  On a
  *                        device that cannot keep a sample's tiles resident
  *                        together, the call runs the split route instead.
+ *                        The waits are bounded (environment variable
+ *                        C1G_BARRIER_SPINS, default 4194304 polls); a wait
+ *                        that gives up makes that workgroup's output NaN.
  *   "split"              everything else: conv with a partial-statistics
  *                        epilogue, a fixed-order merge, then the apply pass */
 const char* c1g_route(const c1g_conv_desc* d, const c1g_norm_desc* norm);

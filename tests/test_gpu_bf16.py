@@ -235,3 +235,28 @@ def test_generality_at_scale_sampled(wl, route):
         assert max_abs_err(mean[n:n + 1], ref["mean"]) <= 1e-4
         r = rstd[n:n + 1].cpu().double().numpy()
         assert float(np.max(np.abs(r / ref["rstd"] - 1))) <= 1e-4
+
+
+@pytest.mark.parametrize("which", ["persistent_conv", "gemm_one_launch"])
+def test_barrier_give_up_poisons_output(which, monkeypatch):
+    """A grid-barrier wait that gives up (forced from the host with
+    C1G_BARRIER_SPINS=0: a workgroup that does not find its group complete at
+    the first poll stops waiting) never hangs and never yields a plausible
+    wrong value: the statistics of such a workgroup are NaN, so its output is
+    NaN, while every finite output equals the normal result bit for bit.  The
+    next call with the default limit is exact again."""
+    if which == "persistent_conv":
+        wl = PERSIST_CASES[0]
+    else:
+        wl = next(w for w in GEMM_CASES if w.name == "gemm_gn_rowmin_one_launch_ragged")
+    announce("barrier give-up", wl.name)
+    inp = make_inputs(wl, 7)
+    ref = run_library(wl, inp, poison=False)
+    monkeypatch.setenv("C1G_BARRIER_SPINS", "0")
+    forced = run_library(wl, inp, poison=False)
+    monkeypatch.delenv("C1G_BARRIER_SPINS")
+    again = run_library(wl, inp, poison=False)
+    assert torch.isfinite(ref).all() and torch.equal(again, ref)
+    nan = torch.isnan(forced)
+    assert nan.any(), "no workgroup gave up (the wait should fail at the first poll)"
+    assert torch.equal(forced[~nan], ref[~nan])
