@@ -62,8 +62,19 @@ static_assert(TN == 128, "weight rows keep bit 2 of c across taps");
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef uint16_t u16;
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+// Direct global -> LDS copy of 16 bytes per lane: lane i reads base +
+// lane_off and writes M0 + 16 i.  Issued as inline assembly so that the
+// wave-uniform part of the address stays in scalar registers (one VGPR per
+// copy however many are in flight) and the compiler adds no waits of its own
+// before LDS reads: every read of a copied stage is ordered by the kernel's
+// explicit wait_all_mem before the workgroup barrier.  The memory clobber
+// keeps all memory accesses on their side of the copy.
+__device__ __forceinline__ void dma16(const void* base, uint32_t lane_off, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"(base), "s"(m0)
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0) lgkmcnt(0) as a compiler builtin (gfx9 encoding, expcnt
@@ -322,32 +333,38 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const char* const xwin = (const char*)a.ximg + (n * a.T_img + t0 * s) * row_bytes;
   const char* const wimg =
       (const char*)a.wp + (int64_t)ctile * a.n_chunks * (KT * TN * RW * 2);
-  uint32_t soff[PPW];  // byte offset of this lane's 16 bytes within chunk 0
-  int dst[PPW];        // byte offset of the copy within its stage buffer
-  bool isx[PPW];       // window (else weight) copy; uniform over the wave
-#pragma unroll
-  for (int p = 0; p < PPW; ++p) {
+  // A copy's source offset is a wave-uniform part (its piece) plus one of two
+  // lane offsets: window row 16 * piece + lane / 4 at logical column
+  // (lane % 4) ^ swz(row) (the column landing at slot lane % 4; swz of the
+  // row depends only on the lane), or weight bytes 16 * lane.
+  const uint32_t lane_x =
+      (uint32_t)((lane >> 2) * row_bytes + 16 * ((lane & 3) ^ swz(lane >> 2)));
+  const uint32_t lane_w = (uint32_t)(16 * lane);
+  auto copy = [&](int p, int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
     int piece = wave + NWAVE * p;
     if (piece >= NPIECE) piece = NPIECE - 1;
-    isx[p] = piece < XP;
-    if (isx[p]) {
-      const int row = 16 * piece + (lane >> 2);
-      const int q = (lane & 3) ^ swz(row);  // logical column landing at slot lane % 4
-      soff[p] = (uint32_t)(row * row_bytes + 16 * q);
-      dst[p] = piece * 1024;
-    } else {
-      soff[p] = (uint32_t)((piece - XP) * 1024 + lane * 16);
-      dst[p] = (piece - XP) * 1024;
-    }
-  }
+    if (piece < XP)
+      dma16(xwin + (int64_t)chunk * (CK * 2) + (int64_t)16 * piece * row_bytes, lane_x,
+            (char*)xs + piece * 1024);
+    else
+      dma16(wimg + (int64_t)chunk * (KT * TN * RW * 2) + (piece - XP) * 1024, lane_w,
+            (char*)ws + (piece - XP) * 1024);
+  };
   auto stage = [&](int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-      if (isx[p])
-        dma16(xwin + (int64_t)chunk * (CK * 2) + soff[p], (char*)xs + dst[p]);
-      else
-        dma16(wimg + (int64_t)chunk * (KT * TN * RW * 2) + soff[p], (char*)ws + dst[p]);
-    }
+    for (int p = 0; p < PPW; ++p) copy(p, chunk, xs, ws);
+  };
+  // The copies of the next chunk are issued in NG groups, one after each of
+  // the first NG tap steps of the current chunk, not all at once after the
+  // barrier: the copy path takes ~64 bytes per clock per CU, so a wave that
+  // issues all its copies at once stalls for ~1.2 K cycles, and with both
+  // waves of a SIMD doing so right after the barrier the MFMA pipe idles.
+  // The last tap step issues none, leaving it for the copies to land.
+  constexpr int NG = KT > 2 ? KT - 1 : 1;
+  auto stage_group = [&](int chunk, u16* xs, u16* ws, int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PPW; ++p)
+      if ((p * NG) / PPW == g) copy(p, chunk, xs, ws);
   };
 
   f32x4 acc[WM][WN];
@@ -419,9 +436,15 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   int kt = KT;  // with two taps, opaque: the one-trip loop stays a loop (its
                 // unrolled form spills in the persistent kernel)
   if constexpr (KT == 2) asm volatile("" : "+s"(kt));
-  auto taps = [&](const u16* xs, const u16* ws) __attribute__((always_inline)) {
+  // ... and issue copy groups 1 .. NG-1 of chunk cc into (cxs, cws) behind
+  // the first tap steps
+  auto taps = [&](const u16* xs, const u16* ws, int cc, u16* cxs, u16* cws)
+      __attribute__((always_inline)) {
 #pragma nounroll
-    for (int j = 1; j < kt; ++j) mfma_reload(xs, ws, j);
+    for (int j = 1; j < kt; ++j) {
+      mfma_reload(xs, ws, j);
+      if (j < NG) stage_group(cc, cxs, cws, j);
+    }
   };
 
   // Pairs of chunks per iteration.  Copies run unconditionally on chunk
@@ -434,25 +457,25 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   stage(0, Xs0, Ws0);
   wait_all_mem();
   lds_barrier();
-  stage(cl(1), Xs1, Ws1);
   read_tap(Xs0, Ws0, 0);
+  stage_group(cl(1), Xs1, Ws1, 0);
   int c = 0;
   for (; c + 1 < n_chunks; c += 2) {
     // stage 0 holds chunk c, its tap 0 in the fragments; stage 1 is loading c+1
-    taps(Xs0, Ws0);
+    taps(Xs0, Ws0, cl(c + 1), Xs1, Ws1);
     wait_all_mem();
     lds_barrier();
-    stage(cl(c + 2), Xs0, Ws0);
     mfma_reload(Xs1, Ws1, 0);  // chunk c's last tap; chunk c+1's tap 0
+    stage_group(cl(c + 2), Xs0, Ws0, 0);
     // stage 1 holds chunk c+1; stage 0 is loading c+2
-    taps(Xs1, Ws1);
+    taps(Xs1, Ws1, cl(c + 2), Xs0, Ws0);
     wait_all_mem();
     lds_barrier();
-    stage(cl(c + 3), Xs1, Ws1);
     mfma_reload(Xs0, Ws0, 0);
+    stage_group(cl(c + 3), Xs1, Ws1, 0);
   }
   if (c < n_chunks) {  // odd count: the last chunk is in stage 0
-    taps(Xs0, Ws0);
+    taps(Xs0, Ws0, cl(c + 1), Xs1, Ws1);
     mfma_only();
   }
   wait_all_mem();  // surplus copies land before the epilogue reuses the LDS
