@@ -1,4 +1,7 @@
-// bf16 implicit-GEMM 1-D convolution for gfx950 (split path), fp32 accumulate.
+// bf16 implicit-GEMM 1-D convolution for gfx950, fp32 accumulate: the
+// convolution of the split route (y plus partial statistics) and, as a
+// persistent cooperative kernel, the whole conv + GroupNorm / channel
+// LayerNorm of the fused_persistent route.
 //
 // GEMM view ("Kimi-K2.6 l1_p5", the implicit-GEMM shape M = N*T_out,
 // N = C_out, K = C_in*K): row m = (n, t), column = output channel c; the
@@ -28,12 +31,14 @@
 // eight waves form a 4 x 2 grid of wave tiles of WM x 4 MFMA tiles (128 x 64
 // for TM = 512), each running every tap, so a wave reads 12 KB of operands per
 // 32 MFMAs.  Two LDS stages, one barrier per chunk: the next chunk's copies
-// run while the current chunk is consumed.  Within a chunk a wave reads each
+// run while the current chunk is consumed, issued in groups behind its first
+// tap steps.  Within a chunk a wave reads each
 // tap's fragments while the previous tap's MFMAs run (a fragment register is
 // reloaded as soon as its last MFMA has issued), and across chunks the last
 // tap's MFMAs run after the barrier while the next chunk's first tap is read.
 // Epilogue: shared with the fp32 kernel (store y, GroupNorm or channel-
-// LayerNorm partial statistics).
+// LayerNorm partial statistics), or in the persistent kernel the sample-wide
+// statistics and the normalised output (fused_norm_epilogue).
 #include "common.hpp"
 #include "conv_epilogue.hpp"
 #include "grid_sync.hpp"
