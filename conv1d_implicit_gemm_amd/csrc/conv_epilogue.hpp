@@ -87,18 +87,20 @@ __device__ __forceinline__ void gn_wave_channel_stats(const ConvArgs& a,
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t T_out = a.T_out;
+  // the wave's valid positions: the same count for every channel
+  const int64_t vt = T_out - (t0 + wm * WM * 16);
+  const float cnt = (float)(vt < 0 ? 0 : (vt < WM * 16 ? vt : WM * 16));
 #pragma unroll
   for (int jn = 0; jn < WN; ++jn) {
-    float sum = 0.f, cnt = 0.f;
+    float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-        if (t < T_out) { sum += acc[i][jn][r]; cnt += 1.f; }
+        if (t < T_out) sum += acc[i][jn][r];
       }
     sum = lane_sum<48>(sum);
-    cnt = lane_sum<48>(cnt);
     const float mean = cnt > 0.f ? sum / cnt : 0.f;
     float m2 = 0.f;
 #pragma unroll
@@ -161,19 +163,22 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
       }
     }
   } else {  // EPI_LN_PART
+    // the wave's valid channels: the same count for every position
+    const int vc = a.C_out - (c0 + wn * WN * 16);
+    const float cnt = (float)(vc < 0 ? 0 : (vc < WN * 16 ? vc : WN * 16));
+    const float inv = cnt > 0.f ? 1.0f / cnt : 0.f;
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float sum = 0.f, cnt = 0.f;
+        float sum = 0.f;
 #pragma unroll
         for (int jn = 0; jn < WN; ++jn) {
           const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-          if (c < a.C_out) { sum += acc[i][jn][r]; cnt += 1.f; }
+          if (c < a.C_out) sum += acc[i][jn][r];
         }
         sum = lane_sum<15>(sum);
-        cnt = lane_sum<15>(cnt);
-        const float mean = cnt > 0.f ? sum / cnt : 0.f;
+        const float mean = sum * inv;
         float m2 = 0.f;
 #pragma unroll
         for (int jn = 0; jn < WN; ++jn) {
