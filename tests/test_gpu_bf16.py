@@ -155,6 +155,9 @@ PERSIST_CASES = [
     # one group spans two channel tiles (C_out/G = 256)
     W("persist_gn_group_spans_tiles", N=3, C_in=40, C_out=512, T=700, K=5, dilation=2,
       pad_left=4, pad_right=4, G=2, **BF),
+    # a single group over all 256 channels (two channel tiles)
+    W("persist_gn_g1", N=3, C_in=40, C_out=256, T=600, K=3, pad_left=1, pad_right=1, G=1,
+      **BF),
     # one channel per group, ragged channel tile (200 = 128 + 72)
     W("persist_gn_cpg1_ragged", N=5, C_in=33, C_out=200, T=300, K=3, pad_left=1, pad_right=1,
       G=200, **BF),

@@ -66,6 +66,8 @@ GN_CASES = [
     W("split_stride2", N=2, C_in=9, C_out=40, T=500, K=4, stride=2, G=5),
     W("split_cpg24_ctile_straddle", N=2, C_in=17, C_out=240, T=130, K=3, pad_left=1,
       pad_right=1, G=10),
+    # a single group over every channel
+    W("split_g1", N=2, C_in=12, C_out=48, T=300, K=3, pad_left=1, pad_right=1, G=1),
 ]
 
 
@@ -181,3 +183,20 @@ def test_error_status_no_launch():
     assert ei.value.status == 1
     torch.cuda.synchronize()
     assert torch.equal(out, torch.full_like(out, 7.0))
+
+
+@pytest.mark.parametrize("wl", [GN_CASES[1], GN_CASES[-1]], ids=lambda w: w.name)
+def test_groupnorm_invariant_on_device(wl):
+    """With unit affine, every (n, group) of the output has mean 0 and variance
+    var / (var + eps), where var = 1 / rstd^2 - eps is the group's variance the
+    library itself reports: a property of the device result alone."""
+    announce("GN invariant", wl.name)
+    inp = make_inputs(wl.replace(affine=False), 3)
+    out, mean, rstd = run_library(wl.replace(affine=False), inp, return_stats=True)
+    z = out.double().cpu().numpy()
+    N, C, T = z.shape
+    zg = z.reshape(N, wl.G, (C // wl.G) * T)
+    r = rstd.double().cpu().numpy()
+    assert float(np.abs(zg.mean(axis=2)).max()) <= 1e-5
+    want = 1.0 - wl.eps * r * r
+    assert float(np.abs(zg.var(axis=2) / want - 1).max()) <= 1e-4
