@@ -117,5 +117,13 @@ __device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = f32_to_b
 // four consecutive elements; p aligned to 4 elements
 __device__ __forceinline__ void store_elem4(float* p, f32x4 v) { *(f32x4*)p = v; }
 __device__ __forceinline__ void store_elem4(uint16_t* p, f32x4 v) { *(u32x2*)p = f32x4_to_bf16(v); }
+// the same as non-temporal (streaming) stores, for final outputs that no
+// later kernel of the call reads back
+__device__ __forceinline__ void store_elem4_nt(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, (f32x4*)p);
+}
+__device__ __forceinline__ void store_elem4_nt(uint16_t* p, f32x4 v) {
+  __builtin_nontemporal_store(f32x4_to_bf16(v), (u32x2*)p);
+}
 
 }  // namespace c1g

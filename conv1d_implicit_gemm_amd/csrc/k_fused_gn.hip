@@ -186,7 +186,7 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
 #pragma unroll
         for (int r = 0; r < 4; ++r) z[r] = (acc[m][r] - mean) * sc + be;
         if (vec_ok && t + 3 < T_out) {
-          store_elem4(dst + t, z);
+          store_elem4_nt(dst + t, z);  // the final output: streaming stores
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
