@@ -114,9 +114,16 @@ __device__ __forceinline__ void compute_chunk(const float* xs, const float* ws,
 }
 
 // Statistics, normalisation and the single write of the output slab.
+// Statistics, normalisation and the single write of the output slab.  lo /
+// hi: LDS no longer in use (waves 0-7 / 8-15, 16 x (P + 4) floats each) in
+// which a wave re-lays its normalised fp32 tile so that each streaming store
+// writes whole channel-row runs (16 lanes x 16 bytes) instead of the 64-byte
+// halves of lines the MFMA layout gives (which the streaming path does not
+// merge: 1.5x the output's bytes reached HBM); nullptr: direct stores.
 template <int MQ>
 __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
-                                         f32x4 (&acc)[MQ], float* red) {
+                                         f32x4 (&acc)[MQ], float* red, float* lo = nullptr,
+                                         float* hi = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
@@ -169,6 +176,40 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
       }
   const float var = block_total(ss) / cnt;
   const float rstd = 1.0f / sqrtf(var + a.eps);
+
+  // fp32 out, whole wave tile inside [0, T_out), aligned: through LDS
+  constexpr int P = MQ * 16, RS = P + 4;  // positions per wave; LDS row stride
+  constexpr int LPC = P / 4, CPI = 64 / LPC;  // lanes per channel row; rows per store
+  if (lo != nullptr && !a.out_bf16 && (T_out & 3) == 0 &&
+      (((uintptr_t)a.out) & 15) == 0 && (int64_t)(wave + 1) * P <= T_out) {
+    const float ga = (a.gamma != nullptr && cvalid) ? a.gamma[c] : 1.f;
+    const float be = (a.beta != nullptr && cvalid) ? a.beta[c] : 0.f;
+    const float sc = rstd * ga;
+    float* tile = (wave < NW / 2 ? lo : hi) + (wave % (NW / 2)) * (CB * RS);
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      f32x4 z;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[r] = (acc[m][r] - mean) * sc + be;
+      *(f32x4*)(tile + lr * RS + m * 16 + 4 * kq) = z;
+    }
+    float* outp = (float*)a.out;
+#pragma unroll
+    for (int k = 0; k < CB / CPI; ++k) {
+      const int ch = lane / LPC + CPI * k;
+      const f32x4 v = *(const f32x4*)(tile + ch * RS + 4 * (lane % LPC));
+      if (co.cbase + ch < a.C_out)
+        store_elem4_nt(outp + (n * a.C_out + co.cbase + ch) * T_out + (int64_t)wave * P +
+                           4 * (lane % LPC),
+                       v);
+    }
+    if (cvalid && wave == 0 && kq == 0 && (lr % cpg) == 0) {
+      const int64_t g = c / cpg;
+      if (a.mean_out) a.mean_out[n * a.G + g] = mean;
+      if (a.rstd_out) a.rstd_out[n * a.G + g] = rstd;
+    }
+    return;
+  }
 
   if (cvalid) {
     const float ga = a.gamma ? a.gamma[c] : 1.f;
@@ -308,7 +349,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
     compute_chunk<MQ, KT>(Xs1, Ws1, acc, abase, bbase, d);
     __syncthreads();
   }
-  epilogue<MQ>(a, co, acc, red);
+  epilogue<MQ>(a, co, acc, red, Xs0, Xs1);
 }
 
 // ------------------------------------------------------------ register-staged variant
