@@ -113,7 +113,6 @@ __device__ __forceinline__ void compute_chunk(const float* xs, const float* ws,
   }
 }
 
-// Statistics, normalisation and the single write of the output slab.
 // Statistics, normalisation and the single write of the output slab.  lo /
 // hi: LDS no longer in use (waves 0-7 / 8-15, 16 x (P + 4) floats each) in
 // which a wave re-lays its normalised fp32 tile so that each streaming store
