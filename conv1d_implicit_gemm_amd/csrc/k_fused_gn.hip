@@ -55,15 +55,33 @@ struct FusedGeom {
   static constexpr int DPR = (XQ + 63) / 64;         // direct-load instructions per row
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Direct global->LDS copies: lane i of the wave writes lds_wave_base + i*size.
+// Direct global->LDS copies: lane i of the wave writes lds_wave_base + i*size
+// (M0 holds the wave's LDS base).  Written as inline assembly: the compiler
+// treats its own LDS-DMA builtin like a flat access that may complete out of
+// order with the LDS reads, and then waits for every LDS read in flight
+// (lgkmcnt(0)) at each K-step of a chunk during which copies are pending,
+// instead of only for the reads that step consumes.  Here the compiler does
+// not know about the copies, so the kernel waits for them itself
+// (wait_all_mem) before each workgroup barrier that publishes a stage; the
+// memory clobber keeps every memory access on its side of a copy.
+__device__ __forceinline__ uint32_t lds_addr(const float* lds) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+}
 __device__ __forceinline__ void dma16(const float* src, float* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const float* src, float* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds_addr(lds_wave_base))
+               : "memory", "m0");
 }
+// s_waitcnt vmcnt(0) lgkmcnt(0) (gfx9 encoding, expcnt at its maximum)
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(7 << 4); }
 
 struct Coord {
   int64_t n;
@@ -338,14 +356,17 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
 
   stage(0, Xs0, Ws0);
   zero_fill();
+  wait_all_mem();
   __syncthreads();
   for (int c = 0; c < n_chunks; c += 2) {
     if (c + 1 < n_chunks) stage(c + 1, Xs1, Ws1);
     compute_chunk<MQ, KT>(Xs0, Ws0, acc, abase, bbase, d);
+    wait_all_mem();  // this wave's copies of the next stage have landed
     __syncthreads();
     if (c + 1 >= n_chunks) break;
     if (c + 2 < n_chunks) stage(c + 2, Xs0, Ws0);
     compute_chunk<MQ, KT>(Xs1, Ws1, acc, abase, bbase, d);
+    wait_all_mem();
     __syncthreads();
   }
   epilogue<MQ>(a, co, acc, red, Xs0, Xs1);
