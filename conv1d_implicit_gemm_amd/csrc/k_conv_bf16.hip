@@ -443,10 +443,22 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   if constexpr (KT == 2) asm volatile("" : "+s"(kt));
   // ... and issue copy groups 1 .. NG-1 of chunk cc into (cxs, cws) behind
   // the first tap steps
+  // The two waves of a SIMD (wave w and w + 4) take turns at the higher
+  // issue priority, one tap each, so that they progress together instead of
+  // oldest first (which leaves the younger wave running alone, its LDS
+  // latency uncovered, while the older one waits at the chunk barrier).
+  const int prio_par = (wave >> 2) & 1;
+  auto set_prio = [&](int j) __attribute__((always_inline)) {
+    if (((j + prio_par) & 1) != 0)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
   auto taps = [&](const u16* xs, const u16* ws, int cc, u16* cxs, u16* cws)
       __attribute__((always_inline)) {
 #pragma nounroll
     for (int j = 1; j < kt; ++j) {
+      set_prio(j);
       mfma_reload(xs, ws, j);
       if (j < NG) stage_group(cc, cxs, cws, j);
     }
@@ -470,12 +482,14 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
     taps(Xs0, Ws0, cl(c + 1), Xs1, Ws1);
     wait_all_mem();
     lds_barrier();
+    set_prio(0);
     mfma_reload(Xs1, Ws1, 0);  // chunk c's last tap; chunk c+1's tap 0
     stage_group(cl(c + 2), Xs0, Ws0, 0);
     // stage 1 holds chunk c+1; stage 0 is loading c+2
     taps(Xs1, Ws1, cl(c + 2), Xs0, Ws0);
     wait_all_mem();
     lds_barrier();
+    set_prio(0);
     mfma_reload(Xs0, Ws0, 0);
     stage_group(cl(c + 3), Xs1, Ws1, 0);
   }
@@ -483,6 +497,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
     taps(Xs0, Ws0, cl(c + 1), Xs1, Ws1);
     mfma_only();
   }
+  __builtin_amdgcn_s_setprio(0);
   wait_all_mem();  // surplus copies land before the epilogue reuses the LDS
   __syncthreads();
 
