@@ -358,13 +358,20 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
   zero_fill();
   wait_all_mem();
   __syncthreads();
+  // Each wave issues the next stage's copies at the highest issue priority,
+  // so that the younger waves' copies are not held behind the older waves'
+  // MFMAs (the SIMD otherwise serves its waves oldest first).
   for (int c = 0; c < n_chunks; c += 2) {
+    __builtin_amdgcn_s_setprio(3);
     if (c + 1 < n_chunks) stage(c + 1, Xs1, Ws1);
+    __builtin_amdgcn_s_setprio(0);
     compute_chunk<MQ, KT>(Xs0, Ws0, acc, abase, bbase, d);
     wait_all_mem();  // this wave's copies of the next stage have landed
     __syncthreads();
     if (c + 1 >= n_chunks) break;
+    __builtin_amdgcn_s_setprio(3);
     if (c + 2 < n_chunks) stage(c + 2, Xs0, Ws0);
+    __builtin_amdgcn_s_setprio(0);
     compute_chunk<MQ, KT>(Xs1, Ws1, acc, abase, bbase, d);
     wait_all_mem();
     __syncthreads();
