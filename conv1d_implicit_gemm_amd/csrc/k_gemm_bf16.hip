@@ -490,21 +490,26 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // out[n][c] = min over c-tiles of part[n][*] + bias2[c]; one workgroup per row;
-// TO is float, or bf16 bits (rounded to nearest even)
+// TO is float, or bf16 bits (rounded to nearest even).  Each wave takes the
+// row's minimum itself: one partial per lane, then a min across the lanes
+// (not a chain of dependent loads per thread).  Streaming stores.
 template <typename TO>
 __global__ __launch_bounds__(NTHR) void rowmin_bcast_kernel(const float* __restrict__ part,
                                                             int n_ctiles,
                                                             const float* __restrict__ bias2,
                                                             TO* out, int64_t C) {
   const int64_t n = blockIdx.x;
+  const int lane = threadIdx.x & 63;
   float m = __builtin_inff();
-  for (int t = 0; t < n_ctiles; ++t) m = fminf(m, part[n * n_ctiles + t]);
+  for (int t = lane; t < n_ctiles; t += 64) m = fminf(m, part[n * n_ctiles + t]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fminf(m, __shfl_xor(m, off));
   TO* row = out + n * C;
   if ((C % 4) == 0 && (((uintptr_t)out) & (4 * sizeof(TO) - 1)) == 0 &&
       (((uintptr_t)bias2) & 15) == 0) {
     for (int64_t q = threadIdx.x; q < C / 4; q += NTHR) {
       const f32x4 b = *(const f32x4*)(bias2 + 4 * q);
-      store_elem4(row + 4 * q, b + m);
+      store_elem4_nt(row + 4 * q, b + m);  // whole 1 KB runs, never read back here
     }
   } else {
     for (int64_t c = threadIdx.x; c < C; c += NTHR) store_elem(row + c, m + bias2[c]);
