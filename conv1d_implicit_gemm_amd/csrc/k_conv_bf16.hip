@@ -585,7 +585,9 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_kernel(const u16* __rest
     if (ci < C_in) {
       const u16* src = x + (n * C_in + ci) * T;
       if (vec) {
-        v = *(const u32x4*)(src + tb);
+        // x is read once here: streaming loads keep it from evicting the
+        // image (which the conv reads next) from the caches
+        v = __builtin_nontemporal_load((const u32x4*)(src + tb));
       } else {
         u16 e8[8];
 #pragma unroll
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_nlc_kernel(const u16* __
     if (t >= 0 && t < T && c < C_in) {
       const u16* src = x + (n * T + t) * C_in + c;
       if (vec) {
-        v = *(const u32x4*)src;
+        v = __builtin_nontemporal_load((const u32x4*)src);  // read once
       } else {
         u16 e8[8];
 #pragma unroll
