@@ -47,8 +47,16 @@ __global__ __launch_bounds__(NTHR) void conv_f32_kernel(ConvArgs a, int epi) {
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 15, kq = lane >> 4;
 
-  const int ttile = blockIdx.x, ctile = blockIdx.y;
-  const int64_t n = blockIdx.z;
+  // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
+  // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
+  // c-tile fastest, so the channel tiles of one input window share an L2
+  // (and x comes from HBM once)
+  const int total = (int)gridDim.x;
+  int lin = blockIdx.x;
+  if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int ctile = lin % a.n_ctiles;
+  const int ttile = (lin / a.n_ctiles) % a.n_ttiles;
+  const int64_t n = lin / (a.n_ctiles * a.n_ttiles);
   const int64_t t0 = (int64_t)ttile * TM;
   const int c0 = ctile * TN;
   const int K = a.K, s = a.stride, d = a.dilation;
@@ -175,7 +183,7 @@ __global__ void conv_f32_pack_kernel(const float* __restrict__ w, float* __restr
 template <int XCAP>
 hipError_t launch_xcap(const ConvArgs& a, int epi, hipStream_t s) {
   const size_t lds = (size_t)(CK * xs_stride(XCAP) + a.K * CK * TNS) * sizeof(float);
-  dim3 grid(a.n_ttiles, a.n_ctiles, (unsigned)a.N);
+  dim3 grid((unsigned)(a.N * a.n_ttiles * a.n_ctiles));
   hipLaunchKernelGGL(conv_f32_kernel<XCAP>, grid, dim3(NTHR), lds, s, a, epi);
   return hipGetLastError();
 }
