@@ -395,6 +395,7 @@ int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const f
   if (!aligned(x, es) || !aligned(w, es) || !aligned(y, os) || (bias && !aligned(bias, 4)))
     return C1G_ERR_MISALIGNED;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
+  if (p.total > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
   if (p.route == R_GEMM)
     return run_gemm(p, d, nullptr, x, w, bias, nullptr, nullptr, nullptr, y, nullptr, nullptr,
                     (char*)ws, (hipStream_t)stream);
@@ -461,6 +462,7 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
       (rstd_out && !aligned(rstd_out, 4)))
     return C1G_ERR_MISALIGNED;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
+  if (p.total > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
   hipStream_t s = (hipStream_t)stream;
   char* wsb = (char*)ws;
 

@@ -82,7 +82,8 @@ enum c1g_status {
   C1G_ERR_UNSUPPORTED = 2,     /* valid but not built (e.g. window wider than a tile)  */
   C1G_ERR_WORKSPACE = 3,       /* workspace NULL or smaller than the size query       */
   C1G_ERR_MISALIGNED = 4,      /* a tensor pointer not aligned to its element size,   */
-                               /* or x / w not 16-byte aligned on the gemm_rows route */
+                               /* x / w not 16-byte aligned on the gemm_rows route,   */
+                               /* or a workspace not 256-byte aligned                 */
   C1G_ERR_HIP = 5              /* the HIP runtime reported an error at launch         */
 };
 
@@ -150,8 +151,9 @@ size_t c1g_conv1d_workspace_size(const c1g_conv_desc* d);
  *   w    [C_out, C_in, K]    same type as x, device
  *   bias [C_out] fp32 or NULL (no bias)
  *   y    [N, C_out, T_out] of d->out_dtype, device, written completely
- *   ws   device scratch of ws_bytes >= c1g_conv1d_workspace_size(d)
- *        (may be NULL when that size is 0); contents are clobbered. */
+ *   ws   device scratch of ws_bytes >= c1g_conv1d_workspace_size(d), 256-byte
+ *        aligned (C1G_ERR_MISALIGNED otherwise; may be NULL when that size is
+ *        0); contents are clobbered. */
 int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
                    void* y, void* ws, size_t ws_bytes, void* stream);
 
@@ -195,7 +197,8 @@ size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc*
  *   out            [N, C_out, T_out] of d->out_dtype, device, written completely
  *   mean_out, rstd_out  optional fp32 device outputs ([N,G] for GroupNorm,
  *                  [N,T_out] for LayerNorm over channels), or NULL
- *   ws             device scratch of ws_bytes >= c1g_conv1d_gn_workspace_size
+ *   ws             device scratch of ws_bytes >= c1g_conv1d_gn_workspace_size,
+ *                  256-byte aligned (C1G_ERR_MISALIGNED otherwise)
  * A bf16 out: on the "split" route the conv stores y already rounded to bf16
  * (its statistics come from the fp32 accumulators) and the normalisation
  * runs in place on those values; the other routes round only the final

@@ -181,6 +181,15 @@ def test_error_status_no_launch():
     with pytest.raises(c1g.C1GError) as ei:
         c1g.conv1d_gn_forward(x, w, norm="group", groups=3, out=out)   # 8 % 3 != 0
     assert ei.value.status == 1
+    # a workspace that is not 256-byte aligned: C1G_ERR_MISALIGNED, nothing launched
+    xb, wb = x.to(torch.bfloat16), w.to(torch.bfloat16)
+    need = c1g.conv1d_gn_workspace_size(
+        c1g.make_desc(2, 4, 8, 50, 3, dtype=c1g.C1G_BF16), c1g.make_norm("group", 2))
+    assert need > 0
+    ws = torch.empty(need + 256, device=DEV, dtype=torch.uint8)[16:]
+    with pytest.raises(c1g.C1GError) as ei:
+        c1g.conv1d_gn_forward(xb, wb, norm="group", groups=2, out=out, workspace=ws)
+    assert ei.value.status == 4
     torch.cuda.synchronize()
     assert torch.equal(out, torch.full_like(out, 7.0))
 
