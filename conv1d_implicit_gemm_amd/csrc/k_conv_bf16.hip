@@ -520,31 +520,41 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
 // column q of row c stored at column q ^ swz(c):
 //   wp[(((ctile*n_chunks + chunk)*K + j)*TN + c)*RW + 8*(q ^ swz(c)) + e]
 //     = w[ctile*TN + c][chunk*32 + 8*q + e][j]      (0 outside the tensor)
-// A thread writes one 16-byte column piece (8 input channels of one (c, j)).
+// A thread reads the 8 * K contiguous weights of 8 input channels of one
+// output channel (every tap) once, and writes the K 16-byte pieces they form.
 __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict__ wp,
                                       int64_t C_in, int64_t C_out, int K, int n_chunks,
                                       int64_t total) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // piece index
-  if (idx >= total / 8) return;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total / (8 * K)) return;
   const int pq = (int)(idx % (RW / 8));
   int64_t rest = idx / (RW / 8);
   const int c = (int)(rest % TN);
   rest /= TN;
-  const int j = (int)(rest % K);
-  rest /= K;
   const int chunk = (int)(rest % n_chunks);
   const int64_t ctile = rest / n_chunks;
   const int q = pq ^ swz(c);
   const int64_t co = ctile * TN + c;
   const int64_t ci0 = (int64_t)chunk * CK + 8 * q;
-  u16 v[8];
+  u16 v[8 * KMAX];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    v[e] = (co < C_out && ci0 + e < C_in) ? w[(co * C_in + ci0 + e) * K + j] : (u16)0;
-  u32x4 o;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = (uint32_t)v[2 * k] | ((uint32_t)v[2 * k + 1] << 16);
-  *(u32x4*)(wp + 8 * idx) = o;
+    for (int j = 0; j < KMAX; ++j)
+      if (j < K)
+        v[e * KMAX + j] =
+            (co < C_out && ci0 + e < C_in) ? w[(co * C_in + ci0 + e) * K + j] : (u16)0;
+  u16* dst = wp + ((((ctile * n_chunks + chunk) * K) * TN + c) * RW + 8 * pq);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < K) {
+      u32x4 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = (uint32_t)v[2 * k * KMAX + j] | ((uint32_t)v[(2 * k + 1) * KMAX + j] << 16);
+      *(u32x4*)(dst + (int64_t)j * TN * RW) = o;
+    }
+  }
 }
 
 // 8x8 transpose of 16-bit values: in[r] holds row r (4 dwords, element 2k in
@@ -722,7 +732,7 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
                           hipStream_t s) {
   const int n_chunks = (int)((C_in + CK - 1) / CK);
   const int64_t total = (int64_t)(conv_bf16_packed_bytes(C_in, C_out, K) / sizeof(u16));
-  const int64_t blocks = (total / 8 + 255) / 256;
+  const int64_t blocks = (total / (8 * K) + 255) / 256;
   hipLaunchKernelGGL(conv_bf16_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, wp, C_in,
                      C_out, K, n_chunks, total);
   return hipGetLastError();
