@@ -34,6 +34,7 @@ NORM_NONE, NORM_GROUP, NORM_LAYER_CHANNELS = 0, 1, 2
 EPI_NONE, EPI_ROWMIN_BIAS = 0, 1
 FLAG_NO_PERSISTENT = 1
 FLAG_ROWMIN_ONE_LAUNCH = 2
+FLAG_COOPERATIVE = 4
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "misaligned pointer",
           5: "HIP runtime error at launch"}
@@ -140,17 +141,20 @@ def _out_dtype(out, out_dtype):
 
 
 def make_norm(norm=None, groups=0, eps=1e-5, rowmin=False, persistent=True,
-              one_launch=False) -> NormDesc:
-    """persistent=False forbids cooperative launches (no "fused_persistent"
-    route; they need every workgroup of a round resident at once).
-    one_launch=True asks for the "gemm_rows" GroupNorm + row-min as one
-    cooperative launch instead of a GEMM plus a broadcast kernel."""
+              one_launch=False, cooperative=False) -> NormDesc:
+    """persistent=False forbids kernels whose workgroups wait on each other
+    (no "fused_persistent" route; they need every workgroup of a round
+    resident at once).  one_launch=True asks for the "gemm_rows" GroupNorm +
+    row-min as one such launch instead of a GEMM plus a broadcast kernel.
+    cooperative=True launches those kernels through the runtime's cooperative
+    launch, for callers that run other work on the device concurrently."""
     code = {None: NORM_NONE, "none": NORM_NONE, "group": NORM_GROUP,
             "layer_channels": NORM_LAYER_CHANNELS}[norm]
     return NormDesc(code, groups if code == NORM_GROUP else 0, eps,
                     EPI_ROWMIN_BIAS if rowmin else EPI_NONE,
                     (0 if persistent else FLAG_NO_PERSISTENT) |
-                    (FLAG_ROWMIN_ONE_LAUNCH if one_launch else 0))
+                    (FLAG_ROWMIN_ONE_LAUNCH if one_launch else 0) |
+                    (FLAG_COOPERATIVE if cooperative else 0))
 
 
 def out_len(desc: ConvDesc) -> int:
@@ -199,26 +203,42 @@ def _need(t, name, dtype, device):
     return t
 
 
+def _shape(t, name, shape):
+    """Shape check of an optional tensor argument, done before anything else
+    is looked at (device, dtype), so a wrong size never reaches a kernel."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _per_channel(t, name, C):
+    """A per-channel parameter: exactly C values (shape [C])."""
+    _shape(t, name, (C,))
+
+
+def _stats_shape(desc, nd, T_out, G):
+    """Shape of exported mean/rstd: [N, G] (GroupNorm) or [N, T_out] (channel LayerNorm)."""
+    return (desc.N, G) if nd.norm == NORM_GROUP else (desc.N, T_out)
+
+
 def _raise(status, where):
     if status != 0:
         raise C1GError(status, where)
 
 
-def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
-                out_dtype=torch.float32, channels_last=False):
+def _conv_desc(x, w, stride, padding, pad_left, pad_right, causal, dilation,
+               out_dtype=torch.float32, channels_last=False, out=None):
+    """The conv descriptor from the shapes of x and w, and ``out`` checked
+    against [N, C_out, T_out]; no device or dtype check yet.  Returns
+    (desc, T_out)."""
+    if not isinstance(x, torch.Tensor) or not isinstance(w, torch.Tensor):
+        raise TypeError("x and w must be tensors")
     if x.dim() != 3 or w.dim() != 3:
         raise ValueError("x must be [N, C_in, T] ([N, T, C_in] with channels_last) and w "
                          "[C_out, C_in, K]")
-    if not x.is_cuda:
-        raise ValueError("x must be a device tensor")
-    if x.dtype == torch.float32:
-        dt = C1G_F32
-    elif x.dtype == torch.bfloat16:
-        dt = C1G_BF16
-    else:
-        raise TypeError("x must be float32 or bfloat16")
-    _need(x, "x", None, x.device)
-    _need(w, "w", x.dtype, x.device)
     if channels_last:
         N, T, C_in = x.shape
     else:
@@ -226,11 +246,26 @@ def _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
     C_out, C_in_w, K = w.shape
     if C_in_w != C_in:
         raise ValueError("x and w disagree on C_in")
+    dt = C1G_BF16 if x.dtype == torch.bfloat16 else C1G_F32
     desc = make_desc(N, C_in, C_out, T, K, stride=stride, dilation=dilation, padding=padding,
                      pad_left=pad_left, pad_right=pad_right, causal=causal, dtype=dt,
                      out_dtype=_DT_CODE[out_dtype],
                      x_layout=LAYOUT_NLC if channels_last else LAYOUT_NCL)
-    return desc
+    T_out = int(load_library().c1g_out_len(ctypes.byref(desc)))
+    if T_out < 1:
+        _raise(1, "conv1d (output length)")
+    _shape(out, "out", (N, C_out, T_out))
+    return desc, T_out
+
+
+def _conv_device(x, w):
+    """Device, dtype and contiguity of x and w (after every shape check)."""
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, "x", None, x.device)
+    _need(w, "w", x.dtype, x.device)
 
 
 # ----------------------------------------------------------------- entry points
@@ -241,12 +276,11 @@ def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_r
     [N, C_in, T], or [N, T, C_in] with channels_last=True."""
     lib = load_library()
     odt = _out_dtype(out, out_dtype)
-    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt,
-                       channels_last)
+    _per_channel(bias, "bias", w.shape[0] if isinstance(w, torch.Tensor) else -1)
+    desc, T_out = _conv_desc(x, w, stride, padding, pad_left, pad_right, causal, dilation,
+                             odt, channels_last, out)
+    _conv_device(x, w)
     _need(bias, "bias", torch.float32, x.device)
-    T_out = lib.c1g_out_len(ctypes.byref(desc))
-    if T_out < 1:
-        _raise(1, "conv1d_forward")
     if out is None:
         out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=odt)
     _need(out, "out", odt, x.device)
@@ -264,7 +298,7 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
                       causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                       beta=None, rowmin_bias=None, return_stats=False, out=None,
                       out_dtype=torch.float32, persistent=True, one_launch=False,
-                      channels_last=False, workspace=None):
+                      cooperative=False, channels_last=False, workspace=None):
     """conv -> GroupNorm / LayerNorm over channels / none -> optional row-min + bias.
 
     x is [N, C_in, T], or [N, T, C_in] with channels_last=True.  Returns out
@@ -273,20 +307,22 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
     [N, G] for GroupNorm, [N, T_out] for the channel LayerNorm)."""
     lib = load_library()
     odt = _out_dtype(out, out_dtype)
-    desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation, odt,
-                       channels_last)
-    nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent, one_launch)
+    C_out = w.shape[0] if isinstance(w, torch.Tensor) else -1
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
+        _per_channel(t, nm, C_out)
+    desc, T_out = _conv_desc(x, w, stride, padding, pad_left, pad_right, causal, dilation,
+                             odt, channels_last, out)
+    nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent, one_launch,
+                   cooperative)
+    _conv_device(x, w)
     for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
         _need(t, nm, torch.float32, x.device)
-    T_out = lib.c1g_out_len(ctypes.byref(desc))
-    if T_out < 1:
-        _raise(1, "conv1d_gn_forward")
     if out is None:
         out = torch.empty((desc.N, desc.C_out, T_out), device=x.device, dtype=odt)
     _need(out, "out", odt, x.device)
     mean = rstd = None
     if return_stats and nd.norm != NORM_NONE:
-        shp = (desc.N, groups) if nd.norm == NORM_GROUP else (desc.N, T_out)
+        shp = _stats_shape(desc, nd, T_out, groups)
         mean = torch.empty(shp, device=x.device, dtype=torch.float32)
         rstd = torch.empty(shp, device=x.device, dtype=torch.float32)
     ws_bytes = lib.c1g_conv1d_gn_workspace_size(ctypes.byref(desc), ctypes.byref(nd))
@@ -304,10 +340,14 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
 def gn_stats(y, groups, eps=1e-5):
     """GroupNorm statistics of y [N, C, L]: (mean[N,G], rstd[N,G])."""
     lib = load_library()
-    if y.dim() != 3 or not y.is_cuda:
-        raise ValueError("y must be a [N, C, L] device tensor")
-    _need(y, "y", torch.float32, y.device)
+    if not isinstance(y, torch.Tensor) or y.dim() != 3:
+        raise ValueError("y must be a [N, C, L] tensor")
     N, C, L = y.shape
+    if not isinstance(groups, int) or groups < 1 or C % groups:
+        raise ValueError("groups must be a positive divisor of C = %d" % C)
+    if not y.is_cuda:
+        raise ValueError("y must be a device tensor")
+    _need(y, "y", torch.float32, y.device)
     mean = torch.empty((N, groups), device=y.device, dtype=torch.float32)
     rstd = torch.empty_like(mean)
     ws_bytes = lib.c1g_gn_stats_workspace_size(N, C, L, groups)
@@ -323,13 +363,26 @@ def gn_apply(y, mean, rstd, gamma=None, beta=None, groups=None, out=None):
     y and out are both fp32 (gn_apply) or both bf16 (gn_apply_bf16).
     ``out=y`` normalises in place."""
     lib = load_library()
-    if y.dim() != 3 or not y.is_cuda:
-        raise ValueError("y must be a [N, C, L] device tensor")
+    if not isinstance(y, torch.Tensor) or y.dim() != 3:
+        raise ValueError("y must be a [N, C, L] tensor")
+    if not isinstance(mean, torch.Tensor) or not isinstance(rstd, torch.Tensor):
+        raise TypeError("mean and rstd must be tensors")
+    N, C, L = y.shape
+    if mean.dim() != 2:
+        raise ValueError("mean must be [N, G], got %s" % (tuple(mean.shape),))
+    G = groups if groups is not None else mean.shape[1]
+    if not isinstance(G, int) or G < 1 or C % G:
+        raise ValueError("groups must be a positive divisor of C = %d" % C)
+    _shape(mean, "mean", (N, G))
+    _shape(rstd, "rstd", (N, G))
+    _per_channel(gamma, "gamma", C)
+    _per_channel(beta, "beta", C)
+    _shape(out, "out", (N, C, L))
+    if not y.is_cuda:
+        raise ValueError("y must be a device tensor")
     if y.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("y must be float32 or bfloat16")
     _need(y, "y", y.dtype, y.device)
-    N, C, L = y.shape
-    G = groups if groups is not None else mean.shape[1]
     for t, nm in ((mean, "mean"), (rstd, "rstd"), (gamma, "gamma"), (beta, "beta")):
         _need(t, nm, torch.float32, y.device)
     if out is None:
@@ -354,19 +407,28 @@ class PreparedConv1dGN:
     def __init__(self, x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_right=None,
                  causal=False, dilation=1, norm="group", groups=1, eps=1e-5, gamma=None,
                  beta=None, rowmin_bias=None, out=None, out_dtype=torch.float32, mean=None,
-                 rstd=None, persistent=True, one_launch=False, channels_last=False):
+                 rstd=None, persistent=True, one_launch=False, cooperative=False,
+                 channels_last=False):
         lib = load_library()
         odt = _out_dtype(out, out_dtype)
-        self.desc = _conv_setup(x, w, stride, padding, pad_left, pad_right, causal, dilation,
-                                odt, channels_last)
+        C_out = w.shape[0] if isinstance(w, torch.Tensor) else -1
+        for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"),
+                      (rowmin_bias, "rowmin_bias")):
+            _per_channel(t, nm, C_out)
         self.norm = make_norm(norm, groups, eps, rowmin_bias is not None, persistent,
-                              one_launch)
+                              one_launch, cooperative)
+        self.desc, self.T_out = _conv_desc(x, w, stride, padding, pad_left, pad_right, causal,
+                                           dilation, odt, channels_last, out)
+        if mean is not None or rstd is not None:
+            if self.norm.norm == NORM_NONE:
+                raise ValueError("mean/rstd exports need a normalisation")
+            st_shape = _stats_shape(self.desc, self.norm, self.T_out, groups)
+            _shape(mean, "mean", st_shape)
+            _shape(rstd, "rstd", st_shape)
+        _conv_device(x, w)
         for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"),
                       (rowmin_bias, "rowmin_bias"), (mean, "mean"), (rstd, "rstd")):
             _need(t, nm, torch.float32, x.device)
-        self.T_out = lib.c1g_out_len(ctypes.byref(self.desc))
-        if self.T_out < 1:
-            _raise(1, "PreparedConv1dGN")
         if out is None:
             out = torch.empty((self.desc.N, self.desc.C_out, self.T_out), device=x.device,
                               dtype=odt)

@@ -258,7 +258,8 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
       a.eps = nd->eps;
       a.G = nd->G;
       a.sync = (unsigned*)(ws + p.off_sync);
-      return hip_status(conv_bf16_fused_launch(a, epi, s));
+      return hip_status(
+          conv_bf16_fused_launch(a, epi, (nd->flags & C1G_FLAG_COOPERATIVE) != 0, s));
     }
     return hip_status(conv_bf16_launch(a, epi, s));
   }
@@ -305,7 +306,8 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
       g.out = out;
       g.out_bf16 = p.out_bf16;
       g.sync = (unsigned*)(ws + p.off_sync);
-      return hip_status(gemm_bf16_rowmin_one_launch(g, s));
+      return hip_status(
+          gemm_bf16_rowmin_one_launch(g, (nd->flags & C1G_FLAG_COOPERATIVE) != 0, s));
     }
     hipError_t e = gemm_bf16_launch(g, GEMM_GN_ROWMIN, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
@@ -319,7 +321,7 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
   float* mean = mean_out ? mean_out : (float*)(ws + p.off_mean);
   float* rstd = rstd_out ? rstd_out : (float*)(ws + p.off_rstd);
   if (p.norm == C1G_NORM_GROUP) {
-    e = gn_stats_launch(y, d->N, d->C_out, 1, nd->G, nd->eps, mean, rstd, s);
+    e = gn_stats_launch(y, d->N, d->C_out, 1, nd->G, nd->eps, mean, rstd, nullptr, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     e = (p.epi == C1G_EPI_NONE)
             ? gn_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, out_dt, d->N, d->C_out,
@@ -328,7 +330,7 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
                                  d->C_out, 1, nd->G, 1, s);
   } else if (p.norm == C1G_NORM_LAYER_CHANNELS) {
     // LayerNorm over the channels of one position == GroupNorm with one group
-    e = gn_stats_launch(y, d->N, d->C_out, 1, 1, nd->eps, mean, rstd, s);
+    e = gn_stats_launch(y, d->N, d->C_out, 1, 1, nd->eps, mean, rstd, nullptr, s);
     if (e != hipSuccess) return C1G_ERR_HIP;
     e = (p.epi == C1G_EPI_NONE)
             ? ln_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, out_dt, d->N, d->C_out,
@@ -402,20 +404,36 @@ int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const f
   return run_conv(p, d, x, w, bias, y, (char*)ws, EPI_STORE, (hipStream_t)stream);
 }
 
+namespace {
+bool gn_stats_args_ok(int64_t N, int64_t C, int64_t L, int32_t G) {
+  return N >= 1 && C >= 1 && L >= 1 && G >= 1 && C % G == 0;
+}
+// grid of the first stage: one workgroup per slice of 32768 values of a group
+bool gn_stats_fits(int64_t N, int64_t C, int64_t L, int32_t G) {
+  const uint64_t len = (uint64_t)(C / G) * (uint64_t)L;
+  return (uint64_t)N * G * ((len + 32767) / 32768) <= 0x7fffffffull;
+}
+}  // namespace
+
 size_t c1g_gn_stats_workspace_size(int64_t N, int64_t C, int64_t L, int32_t G) {
-  (void)N; (void)C; (void)L; (void)G;
-  return 0;
+  if (!gn_stats_args_ok(N, C, L, G) || !gn_stats_fits(N, C, L, G)) return 0;
+  const size_t b = gn_stats_workspace_bytes(N, C, L, G);
+  return b ? align_up(b) : 0;
 }
 
 int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float* y, float* mean,
              float* rstd, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
-  if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0 || !(eps > 0.f && std::isfinite(eps)))
+  if (!gn_stats_args_ok(N, C, L, G) || !(eps > 0.f && std::isfinite(eps)))
     return C1G_ERR_INVALID_ARG;
   if (!y || !mean || !rstd) return C1G_ERR_INVALID_ARG;
-  if ((uint64_t)N * G > 0x7fffffffull) return C1G_ERR_UNSUPPORTED;
+  if (!gn_stats_fits(N, C, L, G)) return C1G_ERR_UNSUPPORTED;
   if (!aligned(y, 4) || !aligned(mean, 4) || !aligned(rstd, 4)) return C1G_ERR_MISALIGNED;
-  return hip_status(gn_stats_launch(y, N, C, L, G, eps, mean, rstd, (hipStream_t)stream));
+  // the size the query reports (rounded up to the workspace alignment)
+  const size_t need = c1g_gn_stats_workspace_size(N, C, L, G);
+  if (need > 0 && (!ws || ws_bytes < need)) return C1G_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
+  return hip_status(gn_stats_launch(y, N, C, L, G, eps, mean, rstd,
+                                    need > 0 ? (float*)ws : nullptr, (hipStream_t)stream));
 }
 
 int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const float* mean,

@@ -39,7 +39,15 @@ inline unsigned barrier_poll_limit() {
 __device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault,
                                                unsigned max_polls) {
   __shared__ int complete;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are done
+  // This wave's stores are done: the hardware wait, and (memory clobber) no
+  // store the compiler could otherwise sink past it.  Together with the
+  // workgroup barrier below, every store of the workgroup has been
+  // acknowledged before thread 0 publishes the arrival.  The stores other
+  // workgroups read are device-scope atomic stores, acknowledged only once
+  // they are at the point of coherence of all XCDs, and those workgroups read
+  // them with device-scope atomic loads issued after they observed the count,
+  // so no cache flush or invalidation is needed on either side.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

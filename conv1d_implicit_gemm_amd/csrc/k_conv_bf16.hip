@@ -658,7 +658,7 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_nlc_kernel(const u16* __
 }
 
 template <int WM, int KT, int XR>
-hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
+hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = false) {
   if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
     // one round: spr whole samples, every workgroup resident at once
     ConvArgs ac = a;
@@ -667,8 +667,8 @@ hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
     const void* k = epi == EPI_GN_FUSED
                         ? (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>
                         : (const void*)conv_bf16_kernel<WM, KT, XR, EPI_LN_FUSED>;
-    return hipLaunchCooperativeKernel(k, dim3((unsigned)(a.spr * a.n_ttiles * a.n_ctiles)),
-                                      dim3(NTHR), args, 0, st);
+    return launch_coresident(k, (unsigned)(a.spr * a.n_ttiles * a.n_ctiles), NTHR, args, coop,
+                             st);
   }
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
   hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR, 0>), grid, dim3(NTHR), 0, st, a, epi);
@@ -676,20 +676,20 @@ hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st) {
 }
 
 template <int WM>
-hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st) {
+hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = false) {
   switch (a.K) {
-    case 1: return launch_wk<WM, 1, XCAP_WIDE>(a, epi, st);
-    case 2: return launch_wk<WM, 2, XCAP_WIDE>(a, epi, st);
-    case 3: return launch_wk<WM, 3, XCAP_WIDE>(a, epi, st);
-    case 4: return launch_wk<WM, 4, XCAP_WIDE>(a, epi, st);
-    case 5: return launch_wk<WM, 5, XCAP_WIDE>(a, epi, st);
+    case 1: return launch_wk<WM, 1, XCAP_WIDE>(a, epi, st, coop);
+    case 2: return launch_wk<WM, 2, XCAP_WIDE>(a, epi, st, coop);
+    case 3: return launch_wk<WM, 3, XCAP_WIDE>(a, epi, st, coop);
+    case 4: return launch_wk<WM, 4, XCAP_WIDE>(a, epi, st, coop);
+    case 5: return launch_wk<WM, 5, XCAP_WIDE>(a, epi, st, coop);
     default: break;
   }
   if (WM != 2) return hipErrorInvalidValue;
   switch (a.K) {
-    case 6: return launch_wk<2, 6, XCAP_TAPS>(a, epi, st);
-    case 7: return launch_wk<2, 7, XCAP_TAPS>(a, epi, st);
-    case 8: return launch_wk<2, 8, XCAP_TAPS>(a, epi, st);
+    case 6: return launch_wk<2, 6, XCAP_TAPS>(a, epi, st, coop);
+    case 7: return launch_wk<2, 7, XCAP_TAPS>(a, epi, st, coop);
+    case 8: return launch_wk<2, 8, XCAP_TAPS>(a, epi, st, coop);
     default: return hipErrorInvalidValue;
   }
 }
@@ -770,17 +770,11 @@ hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
 }
 
 namespace {
+// the GroupNorm and LayerNorm instances share their resources (same LDS,
+// launch bounds), so either stands for both
 template <int WM, int KT, int XR>
 int capacity_wk() {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>, NTHR, 0) !=
-      hipSuccess)
-    return 0;
-  return cus * per_cu;
+  return resident_capacity((const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>, NTHR);
 }
 template <int WM>
 int capacity_w(int K) {
@@ -809,7 +803,7 @@ int conv_bf16_fused_capacity(int stride, int K, int dilation) {
   return 0;
 }
 
-hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s) {
+hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStream_t s) {
   const int tps = a.n_ttiles * a.n_ctiles;
   const int cap = conv_bf16_fused_capacity(a.stride, a.K, a.dilation);
   if (tps < 1 || cap < tps) return hipErrorInvalidValue;
@@ -826,7 +820,7 @@ hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
-  return tm == 512 ? launch_w<8>(a, epi, s) : launch_w<2>(a, epi, s);
+  return tm == 512 ? launch_w<8>(a, epi, s, cooperative) : launch_w<2>(a, epi, s, cooperative);
 }
 
 }  // namespace c1g

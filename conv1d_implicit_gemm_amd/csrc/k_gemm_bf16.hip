@@ -539,17 +539,10 @@ hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const
 }
 
 int gemm_bf16_rowmin_capacity() {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, (const void*)gemm_bf16_kernel<GEMM_GN_ROWMIN_ONE>, NTHR, 0) != hipSuccess)
-    return 0;
-  return cus * per_cu;
+  return resident_capacity((const void*)gemm_bf16_kernel<GEMM_GN_ROWMIN_ONE>, NTHR);
 }
 
-hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, hipStream_t s) {
+hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, bool cooperative, hipStream_t s) {
   const int64_t tiles = (int64_t)a.n_ctiles * a.n_ntiles;
   if (tiles < 1 || tiles > gemm_bf16_rowmin_capacity()) return hipErrorInvalidValue;
   // one arrival counter per row block, then the fault word
@@ -561,8 +554,8 @@ hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   void* args[] = {(void*)&a};
-  return hipLaunchCooperativeKernel((const void*)gemm_bf16_kernel<GEMM_GN_ROWMIN_ONE>,
-                                    dim3((unsigned)tiles), dim3(NTHR), args, 0, s);
+  return launch_coresident((const void*)gemm_bf16_kernel<GEMM_GN_ROWMIN_ONE>, (unsigned)tiles,
+                           NTHR, args, cooperative, s);
 }
 
 int gemm_bf16_tile_c() { return BM; }

@@ -1,6 +1,7 @@
 // Normalisation kernels of the split path (all HBM- or latency-bound):
 //   gn_merge   per-(n, c, t-tile) partials -> GroupNorm mean/rstd per (n, g)
-//   gn_stats   GroupNorm mean/rstd straight from an fp32 y (one pass)
+//   gn_stats   GroupNorm mean/rstd straight from an fp32 y (slices of each
+//              group in parallel, then a fixed-order merge)
 //   gn_apply   out = (y - mean) * rstd * gamma + beta, per (n, g) statistics
 //              (y and out fp32 or bf16; arithmetic in fp32)
 //   ln_merge   per-(n, c-tile, t) partials -> LayerNorm-over-channels mean/rstd
@@ -94,40 +95,103 @@ __device__ __forceinline__ Stats batch16(const f32x4 v[4]) {
   return Stats{16.f, mu, m2};
 }
 
-__global__ __launch_bounds__(NT) void gn_stats_kernel(const float* __restrict__ y, int64_t C,
-                                                      int64_t L, int32_t G, float eps,
-                                                      float* mean, float* rstd) {
-  __shared__ Stats sh[NT];
-  const int64_t ng = blockIdx.x;
-  const int64_t n = ng / G, g = ng - n * G;
-  const int64_t cpg = C / G;
-  const int64_t len = cpg * L;
-  const float* p = y + (n * C + g * cpg) * L;  // a group's values are contiguous
-  int64_t head = (int64_t)(((16 - (((uintptr_t)p) & 15)) & 15) >> 2);
-  if (head > len) head = len;
+// Fold the statistics of all 64 lanes of a wave into lane 0 (a fixed xor
+// tree: every run merges the same pairs in the same order).
+__device__ __forceinline__ Stats wave_merge(Stats st) {
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const Stats o = {__shfl_xor(st.n, h), __shfl_xor(st.mean, h), __shfl_xor(st.m2, h)};
+    st = stats_merge(st, o);
+  }
+  return st;
+}
+
+// GroupNorm statistics straight from an fp32 y, in two stages, so that any
+// number of (n, g) groups fills the GPU.  The values of group (n, g) are one
+// contiguous run of len = (C/G) * L elements ("Kimi-K2.6 l2_p35": statistics
+// over the C/G channels x L positions of a group), cut into S slices of
+// kStatSlice elements (the last one shorter).
+// Stage 1 (gn_stats_slice_kernel): one workgroup per (n, g, slice) reduces
+// its slice to (mean, M2) at part[((n*G + g)*S + s)*2] (the count follows from
+// the geometry); with S == 1 it writes mean/rstd itself.
+// Stage 2 (gn_stats_merge_kernel): one wave per (n, g) folds the S partials
+// in a fixed order.  Every reduction order is fixed, so results are bit
+// identical from run to run.
+constexpr int64_t kStatSlice = 32768;  // elements per stage-1 workgroup (128 KB)
+
+int64_t stat_slices(int64_t len, bool two_stage) {
+  return two_stage ? (len + kStatSlice - 1) / kStatSlice : 1;
+}
+
+// VEC: y 16-byte aligned and len % 4 == 0 (every slice starts aligned)
+template <bool VEC>
+__global__ __launch_bounds__(NT) void gn_stats_slice_kernel(const float* __restrict__ y,
+                                                            int64_t len, int64_t S,
+                                                            float eps,
+                                                            float* __restrict__ part,
+                                                            float* mean, float* rstd) {
+  __shared__ Stats wsh[NT / 64];
+  const int64_t gs = blockIdx.x;           // (n*G + g)*S + s
+  const int64_t ng = gs / S, sl = gs - ng * S;
+  const int64_t off = sl * kStatSlice;
+  const int64_t rem = len - off;
+  const int64_t cnt = rem < kStatSlice ? rem : kStatSlice;
+  const float* p = y + ng * len + off;
   const int tid = threadIdx.x;
   Stats st = {0.f, 0.f, 0.f};
-  if (tid < head) st = Stats{1.f, p[tid], 0.f};
-  const f32x4* pv = (const f32x4*)(p + head);
-  const int64_t nvec = (len - head) >> 2;
-  const int64_t nb = nvec >> 2;  // batches of 4 vectors per thread-iteration
-  for (int64_t b = tid; b < nb; b += NT) {
+  // full batches: 16 values per thread per iteration, all loads issued first
+  constexpr int64_t BATCH = 16 * NT;
+  const int64_t nfull = cnt / BATCH;
+  for (int64_t it = 0; it < nfull; ++it) {
     f32x4 v[4];
+    if (VEC) {
+      const f32x4* pv = (const f32x4*)(p + it * BATCH);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = pv[4 * b + i];
+      for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(pv + u * NT + tid);
+    } else {
+      const float* pb = p + it * BATCH;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[u][e] = pb[(4 * u + e) * NT + tid];
+    }
     st = stats_merge(st, batch16(v));
   }
-  for (int64_t q = 4 * nb + tid; q < nvec; q += NT) {
-    const f32x4 v = pv[q];
-    const float mu = ((v[0] + v[1]) + (v[2] + v[3])) * 0.25f;
-    float m2 = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { const float dv = v[e] - mu; m2 += dv * dv; }
-    st = stats_merge(st, Stats{4.f, mu, m2});
-  }
-  for (int64_t e = head + 4 * nvec + tid; e < len; e += NT) st = stats_merge(st, Stats{1.f, p[e], 0.f});
-  st = block_merge(st, sh);
+  // the tail of the slice, value by value
+  for (int64_t e = nfull * BATCH + tid; e < cnt; e += NT) st = stats_merge(st, Stats{1.f, p[e], 0.f});
+  st = wave_merge(st);
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) wsh[wave] = st;
+  __syncthreads();
   if (tid == 0) {
+    Stats r = wsh[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r = stats_merge(r, wsh[w]);
+    if (S == 1) {
+      mean[ng] = r.mean;
+      rstd[ng] = 1.0f / sqrtf(r.m2 / r.n + eps);
+    } else {
+      *(f32x2*)(part + 2 * gs) = f32x2{r.mean, r.m2};
+    }
+  }
+}
+
+__global__ __launch_bounds__(NT) void gn_stats_merge_kernel(const float* __restrict__ part,
+                                                            int64_t NG, int64_t len, int64_t S,
+                                                            float eps, float* mean,
+                                                            float* rstd) {
+  const int lane = threadIdx.x & 63;
+  const int64_t ng = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  if (ng >= NG) return;  // whole wave
+  Stats st = {0.f, 0.f, 0.f};
+  for (int64_t s = lane; s < S; s += 64) {
+    const int64_t rem = len - s * kStatSlice;
+    const float cnt = (float)(rem < kStatSlice ? rem : kStatSlice);
+    const f32x2 v = *(const f32x2*)(part + 2 * (ng * S + s));
+    st = stats_merge(st, Stats{cnt, v[0], v[1]});
+  }
+  st = wave_merge(st);
+  if (lane == 0) {
     mean[ng] = st.mean;
     rstd[ng] = 1.0f / sqrtf(st.m2 / st.n + eps);
   }
@@ -436,10 +500,28 @@ hipError_t gn_merge_launch(const float* part, int64_t N, int64_t C, int64_t L, i
   return hipGetLastError();
 }
 
+size_t gn_stats_workspace_bytes(int64_t N, int64_t C, int64_t L, int32_t G) {
+  const int64_t S = stat_slices(C / G * L, true);
+  return S > 1 ? (size_t)(N * G * S) * 2 * sizeof(float) : 0;
+}
+
 hipError_t gn_stats_launch(const float* y, int64_t N, int64_t C, int64_t L, int32_t G,
-                           float eps, float* mean, float* rstd, hipStream_t s) {
-  hipLaunchKernelGGL(gn_stats_kernel, dim3((unsigned)(N * G)), dim3(NT), 0, s, y, C, L, G, eps,
-                     mean, rstd);
+                           float eps, float* mean, float* rstd, float* part, hipStream_t s) {
+  const int64_t len = C / G * L, NG = N * G;
+  // without a workspace: one workgroup per group
+  const int64_t S = stat_slices(len, part != nullptr);
+  const bool vec = (len % 4 == 0) && ((((uintptr_t)y) & 15) == 0);
+  const dim3 grid((unsigned)(NG * S));
+  if (vec)
+    hipLaunchKernelGGL(gn_stats_slice_kernel<true>, grid, dim3(NT), 0, s, y, len, S, eps,
+                       part, mean, rstd);
+  else
+    hipLaunchKernelGGL(gn_stats_slice_kernel<false>, grid, dim3(NT), 0, s, y, len, S, eps,
+                       part, mean, rstd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  hipLaunchKernelGGL(gn_stats_merge_kernel, dim3((unsigned)((NG + NT / 64 - 1) / (NT / 64))),
+                     dim3(NT), 0, s, part, NG, len, S, eps, mean, rstd);
   return hipGetLastError();
 }
 

@@ -49,6 +49,17 @@ struct ConvArgs {
   uint32_t polls;      // polls before a barrier wait gives up (set by the launcher)
 };
 
+// ---- kernels whose workgroups wait on each other (residency.hip)
+// Workgroups of `kernel` (`threads` per workgroup, no dynamic LDS) the
+// current device keeps resident at once, 0 if unknown; queried once per
+// (device, kernel) and cached.
+int resident_capacity(const void* kernel, int threads);
+// Launch with grid <= resident_capacity (hipErrorInvalidValue otherwise): an
+// ordinary launch, or (cooperative) hipLaunchCooperativeKernel, whose
+// co-residency guarantee also holds while other work shares the device.
+hipError_t launch_coresident(const void* kernel, unsigned grid, int threads, void** args,
+                             bool cooperative, hipStream_t s);
+
 // ---- fp32 split-path convolution (k_conv_f32.hip)
 // Tile geometry: TM output positions x TN output channels, CK input channels
 // per K-chunk.  xcap is the widest input window one tile may need.
@@ -83,7 +94,7 @@ hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s);
 // unknown); the launch zeroes the counters, fills spr/rounds and launches
 // cooperatively.
 int conv_bf16_fused_capacity(int stride, int K, int dilation);
-hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, hipStream_t s);
+hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStream_t s);
 
 // ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
 // GEMM_GN_ROWMIN writes per-tile row minima for rowmin_bcast;
@@ -120,9 +131,9 @@ hipError_t transpose_nlc_f32(const float* x, float* xt, int64_t N, int64_t T, in
 // GEMM + GroupNorm + row-min + bias2 in one cooperative launch: workgroups the
 // device keeps resident at once with the GN_ROWMIN_ONE kernel (0 on error);
 // the launch needs n_ctiles * n_ntiles of them and n_ntiles + 1 zeroed
-// words at a.sync (zeroed here)
+// words at a.sync (zeroed here); cooperative: see launch_coresident
 int gemm_bf16_rowmin_capacity();
-hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, hipStream_t s);
+hipError_t gemm_bf16_rowmin_one_launch(GemmArgs a, bool cooperative, hipStream_t s);
 // out[n][c] = min_t part[n][t] + bias2[c]; out fp32 or (out_bf16) bf16
 hipError_t rowmin_bcast_launch(const float* part, int64_t N, int n_ctiles, const float* bias2,
                                void* out, bool out_bf16, int64_t C, hipStream_t s);
@@ -154,9 +165,13 @@ hipError_t fused_gn_launch(const FusedArgs& a, hipStream_t s);
 hipError_t gn_merge_launch(const float* part, int64_t N, int64_t C, int64_t L, int32_t G,
                            int32_t n_ttiles, int32_t tm, float eps, float* mean, float* rstd,
                            hipStream_t s);
-// GroupNorm statistics straight from y [N, C, L] -> mean/rstd [N, G]
+// GroupNorm statistics straight from y [N, C, L] -> mean/rstd [N, G]: each
+// group's values in slices, one workgroup per slice, then a fixed-order merge
+// of the slice partials held in `part` (gn_stats_workspace_bytes of it);
+// part == nullptr: one workgroup per group, no workspace
+size_t gn_stats_workspace_bytes(int64_t N, int64_t C, int64_t L, int32_t G);
 hipError_t gn_stats_launch(const float* y, int64_t N, int64_t C, int64_t L, int32_t G,
-                           float eps, float* mean, float* rstd, hipStream_t s);
+                           float eps, float* mean, float* rstd, float* part, hipStream_t s);
 // Element types of y and out in the passes below (values of enum c1g_dtype):
 // fp32 -> fp32, bf16 -> bf16 and fp32 -> bf16 are built; out may equal y.
 // out = (y - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c]

@@ -48,7 +48,9 @@ class Workload:
     affine: bool = True           # gamma/beta present
     rowmin_bias: bool = False     # per-row min over channels + bias2 broadcast
     persistent: bool = True       # allow the persistent conv + normalisation route
-    one_launch: bool = False      # Linear + GroupNorm + row-min as one cooperative launch
+    one_launch: bool = False      # Linear + GroupNorm + row-min as one launch
+    cooperative: bool = False     # kernels whose workgroups wait on each other launched
+                                  # through the runtime's cooperative launch
     channels_last: bool = False   # hand x to the library as [N, T, C_in]
     w_bound: Optional[float] = None
 

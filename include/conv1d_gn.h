@@ -122,15 +122,27 @@ typedef struct c1g_norm_desc {
 
 /* c1g_norm_desc.flags */
 enum c1g_flags {
-  C1G_FLAG_NO_PERSISTENT = 1,  /* no cooperative launches: never take the
-                                  "fused_persistent" route, and ignore
-                                  C1G_FLAG_ROWMIN_ONE_LAUNCH (the cooperative forms
-                                  need every workgroup of a round resident at once) */
-  C1G_FLAG_ROWMIN_ONE_LAUNCH = 2  /* "gemm_rows" with GroupNorm + row-min: one
-                                  cooperative launch instead of a GEMM and a broadcast
-                                  kernel (same result, bit for bit; on MI355X the
-                                  cooperative launch's queue synchronisation costs more
-                                  than the second launch, so it is not the default) */
+  C1G_FLAG_NO_PERSISTENT = 1,  /* no kernel whose workgroups wait on each other:
+                                  never take the "fused_persistent" route, and ignore
+                                  C1G_FLAG_ROWMIN_ONE_LAUNCH (both need every
+                                  workgroup of a round resident at once) */
+  C1G_FLAG_ROWMIN_ONE_LAUNCH = 2, /* "gemm_rows" with GroupNorm + row-min: one
+                                  launch whose workgroups wait on each other instead of
+                                  a GEMM and a broadcast kernel (same result, bit for
+                                  bit) */
+  C1G_FLAG_COOPERATIVE = 4     /* launch the kernels whose workgroups wait on each
+                                  other ("fused_persistent", the one-launch row-min)
+                                  through hipLaunchCooperativeKernel.  By default they
+                                  are ordinary launches whose grid fits the device's
+                                  resident capacity, which keeps every workgroup
+                                  resident as long as no other work runs on the device
+                                  at the same time; callers that share the device with
+                                  concurrent work set this flag, and the runtime then
+                                  guarantees co-residency (at the cost of a queue
+                                  synchronisation on each side of the launch, ~11 us
+                                  each on MI355X).  Either way every wait is bounded: a
+                                  workgroup denied co-residency gives up and writes NaN,
+                                  it never hangs */
 };
 
 /* T_out of the geometry, or -1 if the geometry is invalid or has no output.
@@ -157,28 +169,42 @@ size_t c1g_conv1d_workspace_size(const c1g_conv_desc* d);
 int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
                    void* y, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes gn_stats needs. */
+/* Workspace bytes gn_stats needs: 0 when every group holds at most 32768
+ * values (C/G * L), else 8 bytes per slice of 32768 values of every group
+ * (rounded up to 256 bytes).  0 for invalid arguments. */
 size_t c1g_gn_stats_workspace_size(int64_t N, int64_t C, int64_t L, int32_t G);
 
-/* GroupNorm statistics of an existing y ("Kimi-K2.6 l2_p35" GroupNorm
- * definition; "Kimi-K2.6 l2_p3" statistics-then-apply split):
+/* GroupNorm statistics of an existing y ("Kimi-K2.6 l2_p35", the GroupNorm
+ * definition: mean and population variance over the C/G channels x L
+ * positions of (n, g), eps inside the square root; "Kimi-K2.6 l2_p3", the
+ * statistics kernel of its stats-then-apply split):
  *   y    [N, C, L] fp32 device, C % G == 0
  *   mean [N, G]  fp32 device: mean of the C/G x L values of (n, g)
  *   rstd [N, G]  fp32 device: 1/sqrt(population variance + eps)
- *   ws   device scratch of ws_bytes >= c1g_gn_stats_workspace_size(...) */
+ *   ws   device scratch of ws_bytes >= c1g_gn_stats_workspace_size(...),
+ *        256-byte aligned (C1G_ERR_MISALIGNED otherwise); may be NULL when
+ *        that size is 0 (C1G_ERR_WORKSPACE when needed and missing or short).
+ * Two stages: every slice of 32768 values of a group is reduced by its own
+ * workgroup to (mean, M2) in ws, then the slices of each group are merged in
+ * a fixed order (bit-identical results from run to run).  eps must be finite
+ * and > 0 (C1G_ERR_INVALID_ARG). */
 int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float* y,
              float* mean, float* rstd, void* ws, size_t ws_bytes, void* stream);
 
-/* GroupNorm normalise + affine:
+/* GroupNorm normalise + affine ("Kimi-K2.6 l2_p35", GroupNorm: normalise
+ * each value with its group's mean and rstd, then the per-channel affine;
+ * "Kimi-K2.6 l2_p3", the apply kernel of its stats-then-apply split):
  *   out[n,c,l] = (y[n,c,l] - mean[n,g]) * rstd[n,g] * gamma[c] + beta[c],  g = c / (C/G)
  *   y, out [N, C, L] fp32 device; out may equal y (in place), no other overlap
  *   mean, rstd [N, G] fp32 device
- *   gamma, beta [C] fp32 device, or NULL (1 and 0) */
+ *   gamma, beta [C] fp32 device, or NULL (1 and 0)
+ * N*C*L < 2^32 (C1G_ERR_UNSUPPORTED otherwise). */
 int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const float* mean,
              const float* rstd, const float* gamma, const float* beta, float* out,
              void* stream);
 
-/* gn_apply on bf16 tensors (the same definition): y, out [N, C, L] bf16
+/* gn_apply on bf16 tensors (the same definition and passages as gn_apply):
+ * y, out [N, C, L] bf16
  * device (out may equal y), everything else as gn_apply; computed in fp32,
  * out rounded to nearest even.  The apply pass of a bf16 output moves half
  * the bytes of the fp32 one. */
@@ -225,7 +251,8 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
  *                        row-min epilogue runs as the GEMM plus a broadcast
  *                        kernel, or with C1G_FLAG_ROWMIN_ONE_LAUNCH (and the
  *                        device able to keep every GEMM tile resident at once)
- *                        as one cooperative launch: each workgroup publishes
+ *                        as one launch (C1G_FLAG_COOPERATIVE: cooperative)
+ *                        whose workgroups wait on each other: each publishes
  *                        its rows' partial minima, waits for the other channel
  *                        tiles of those rows and writes its block of the
  *                        broadcast output (same result, bit for bit)
@@ -233,7 +260,8 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
  *                        (C_out/G divides 128 or 128 divides it) or LayerNorm
  *                        over channels, no epilogue, at most 256 tiles per
  *                        sample, flags without C1G_FLAG_NO_PERSISTENT: one
- *                        cooperative launch in rounds of whole samples; each
+ *                        launch (C1G_FLAG_COOPERATIVE: cooperative) in rounds
+ *                        of whole samples; each
  *                        workgroup publishes partial statistics, waits for
  *                        the other workgroups of its sample, merges them in a
  *                        fixed order, normalises its tile in registers and

@@ -51,6 +51,7 @@ def run_library(wl: Workload, inp: dict, *, return_stats=False, poison=True):
                                     norm=wl.norm, groups=wl.G, eps=wl.eps, gamma=ga, beta=be,
                                     rowmin_bias=b2, return_stats=True, out=out,
                                     persistent=wl.persistent, one_launch=wl.one_launch,
+                                    cooperative=wl.cooperative,
                                     channels_last=wl.channels_last)
     torch.cuda.synchronize()
     return res if return_stats else res[0]
@@ -86,7 +87,7 @@ def library_route(wl: Workload):
                          out_dtype=c1g.C1G_BF16 if wl.out_dtype == "bf16" else c1g.C1G_F32,
                          x_layout=c1g.LAYOUT_NLC if wl.channels_last else c1g.LAYOUT_NCL)
     return c1g.route(desc, c1g.make_norm(wl.norm, wl.G, wl.eps, wl.rowmin_bias, wl.persistent,
-                                         wl.one_launch))
+                                         wl.one_launch, wl.cooperative))
 
 
 def bf16_out_bound(wl: Workload, inp: dict, ref: dict):

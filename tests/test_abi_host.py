@@ -184,6 +184,15 @@ def test_pointer_checks_fail_before_any_launch():
     # standalone GroupNorm entry points
     assert lib.gn_stats(2, 32, 10, 5, 1e-5, good, good, good, None, 0, None) == 1
     assert lib.gn_stats(2, 32, 10, 8, 1e-5, odd, good, good, None, 0, None) == 4
+    # groups of more than 32768 values need the two-stage workspace
+    need = lib.c1g_gn_stats_workspace_size(1, 64, 4096, 1)
+    assert need == 256                       # 8 slices x 8 bytes, rounded up to 256
+    assert lib.c1g_gn_stats_workspace_size(2, 32, 1000, 8) == 0
+    assert lib.c1g_gn_stats_workspace_size(2, 32, 1000, 5) == 0   # invalid: 0
+    assert lib.gn_stats(1, 64, 4096, 1, 1e-5, good, good, good, None, 0, None) == 3
+    assert lib.gn_stats(1, 64, 4096, 1, 1e-5, good, good, good, good, need - 8, None) == 3
+    assert lib.gn_stats(1, 64, 4096, 1, 1e-5, good, good, good, P(0x10010), need, None) == 4
+    assert lib.gn_stats(1, 64, 4096, 1, 0.0, good, good, good, good, need, None) == 1
     assert lib.gn_apply(2, 32, 10, 8, good, good, good, None, None, None, None) == 1
     assert lib.gn_apply(2, 32, 10, 8, good, odd, good, None, None, good, None) == 4
     # bf16 outputs need 2-byte alignment only

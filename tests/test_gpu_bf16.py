@@ -69,7 +69,7 @@ GEMM_CASES = [
     W("gemm_tail_only", N=17, C_in=40, C_out=64, T=1, K=1, G=4, rowmin_bias=True, **BF),
     # odd number of whole chunks plus a tail
     W("gemm_odd_chunks_tail", N=90, C_in=200, C_out=128, T=1, K=1, G=8, **BF),
-    # GroupNorm + row-min in one cooperative launch over 3 row blocks x 5
+    # GroupNorm + row-min in one launch over 3 row blocks x 5
     # channel tiles, both ragged (1040 = 4 * 256 + 16 channels, 300 = 2 * 128 + 44
     # rows), and the same as a GEMM plus a broadcast kernel
     W("gemm_gn_rowmin_one_launch_ragged", N=300, C_in=200, C_out=1040, T=1, K=1, G=65,
@@ -142,7 +142,7 @@ def test_bf16_determinism():
     assert torch.equal(run_library(g, inp), run_library(g, inp))
 
 
-# The persistent route: one cooperative launch in rounds of whole samples
+# The persistent route: one launch in rounds of whole samples
 # (256 resident workgroups / tiles per sample = samples per round), partial
 # statistics published, merged after a barrier among the sample's workgroups,
 # the output written once.
@@ -195,6 +195,22 @@ def test_persistent_and_split_agree_with_oracle():
         assert max_abs_err(mean, ref["mean"]) <= 1e-4, persistent
         r = rstd.cpu().double().numpy()
         assert float(np.max(np.abs(r / ref["rstd"] - 1))) <= 1e-4, persistent
+
+
+@pytest.mark.parametrize("name", ["persist_gn_2rounds", "persist_ln_k8",
+                                  "gemm_gn_rowmin_one_launch_ragged"])
+def test_cooperative_launch_identical(name):
+    """The kernels whose workgroups wait on each other give the same bits
+    launched ordinarily (the default) and through the runtime's cooperative
+    launch (C1G_FLAG_COOPERATIVE)."""
+    wl = next(w for w in PERSIST_CASES + GEMM_CASES if w.name == name)
+    announce("cooperative vs ordinary launch", wl.name)
+    inp = make_inputs(wl, 3)
+    plain = run_library(wl, inp, return_stats=True)
+    coop = run_library(wl.replace(cooperative=True), inp, return_stats=True)
+    for a, b in zip(plain, coop):
+        assert torch.isfinite(a).all()
+        assert torch.equal(a, b)
 
 
 def test_persistent_determinism():

@@ -156,7 +156,13 @@ def test_gn_stats_and_apply_standalone():
     """gn_stats + gn_apply on an existing y (and in place) vs the oracle's GroupNorm."""
     announce("gn_stats/gn_apply")
     g = torch.Generator().manual_seed(5)
-    for (N, C, L, G) in [(2, 32, 1000, 8), (3, 24, 77, 8), (1, 16, 4093, 4), (4, 12, 1, 3)]:
+    # groups of up to 32768 values (one workgroup each), then groups cut into
+    # several slices merged in a second stage: one group over a whole sample
+    # (N * G = 1), a ragged last slice, and a length that is no multiple of 4
+    # (the unvectorised loads)
+    for (N, C, L, G) in [(2, 32, 1000, 8), (3, 24, 77, 8), (1, 16, 4093, 4), (4, 12, 1, 3),
+                         (1, 64, 4096, 1), (2, 96, 2000, 2), (1, 35, 3001, 1),
+                         (2, 1024, 4092, 32)]:
         y = torch.randn(N, C, L, generator=g) * 2 + 0.5
         gam = torch.rand(C, generator=g) + 0.5
         bet = torch.randn(C, generator=g) * 0.1
@@ -170,6 +176,30 @@ def test_gn_stats_and_apply_standalone():
         assert max_abs_err(out, z_ref) <= TOL_F32
         c1g.gn_apply(yd, mean, rstd, to_dev(gam), to_dev(bet), groups=G, out=yd)  # in place
         assert torch.equal(yd, out)
+
+
+def test_gn_stats_two_stage_deterministic_and_unaligned():
+    """gn_stats on groups of several slices: bit-identical from run to run, and
+    the same values (to rounding) when y starts 4 bytes off a 16-byte
+    boundary, which takes the unvectorised loads."""
+    announce("gn_stats two-stage determinism / unaligned y")
+    g = torch.Generator().manual_seed(11)
+    N, C, L, G = 3, 64, 3000, 4                   # 48000 values per group: 2 slices
+    y = torch.randn(N, C, L, generator=g) * 3 - 1
+    assert c1g.load_library().c1g_gn_stats_workspace_size(N, C, L, G) > 0
+    yd = to_dev(y)
+    m1, r1 = c1g.gn_stats(yd, G)
+    m2, r2 = c1g.gn_stats(yd, G)
+    assert torch.equal(m1, m2) and torch.equal(r1, r2)
+    flat = torch.empty(N * C * L + 1, device=DEV)
+    yo = flat[1:].view(N, C, L)
+    yo.copy_(yd)
+    assert yo.data_ptr() % 16 == 4
+    m3, r3 = c1g.gn_stats(yo, G)
+    _, m_ref, r_ref = oracle.group_norm(y.double().numpy(), G, 1e-5)
+    for m, r in ((m1, r1), (m3, r3)):
+        assert max_abs_err(m, m_ref) <= 1e-5
+        assert float(np.max(np.abs(r.cpu().double().numpy() / r_ref - 1))) <= 1e-5
 
 
 def test_error_status_no_launch():
