@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     conv1d_forward(x, w, bias=None, *, stride, padding/pad_left/pad_right, causal, dilation)
     conv1d_gn_forward(x, w, bias=None, *, ..., norm, groups, eps, gamma, beta,
                       rowmin_bias=None, return_stats=False)
+    conv1d_gn_forward_noalloc(x, w, bias=None, *, out, ...)   (no workspace, no allocation)
     gn_stats(y, groups, eps)        -> (mean[N,G], rstd[N,G])
     gn_apply(y, mean, rstd, gamma, beta, groups, out=None)   (fp32, or bf16 -> gn_apply_bf16)
 Outputs are fp32 unless ``out_dtype=torch.bfloat16`` (or a bf16 ``out``) is
@@ -42,8 +43,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 # every symbol include/conv1d_gn.h declares
 EXPORTS = ["c1g_out_len", "c1g_check", "c1g_conv1d_workspace_size", "conv1d_forward",
            "c1g_gn_stats_workspace_size", "gn_stats", "gn_apply", "gn_apply_bf16",
-           "c1g_conv1d_gn_workspace_size", "conv1d_gn_forward", "c1g_route",
-           "c1g_status_string"]
+           "c1g_conv1d_gn_workspace_size", "conv1d_gn_forward", "conv1d_gn_forward_noalloc",
+           "c1g_route", "c1g_status_string"]
+# device scratch conv1d_gn_forward_noalloc holds per device (its largest workspace)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ConvDesc(ctypes.Structure):
@@ -102,6 +105,8 @@ def load_library():
         lib.c1g_conv1d_gn_workspace_size.argtypes = [PD, PN]
         lib.conv1d_gn_forward.restype = ctypes.c_int
         lib.conv1d_gn_forward.argtypes = [PD, PN, P, P, P, P, P, P, P, P, P, P, sz, P]
+        lib.conv1d_gn_forward_noalloc.restype = ctypes.c_int
+        lib.conv1d_gn_forward_noalloc.argtypes = [PD, PN, P, P, P, P, P, P, P, P, P, P]
         lib.c1g_route.restype = ctypes.c_char_p
         lib.c1g_route.argtypes = [PD, PN]
         lib.c1g_status_string.restype = ctypes.c_char_p
@@ -335,6 +340,47 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
                                _stream(x.device))
     _raise(st, "conv1d_gn_forward")
     return (out, mean, rstd) if return_stats else out
+
+
+def conv1d_gn_forward_noalloc(x, w, bias=None, *, out, stride=1, padding=0, pad_left=None,
+                              pad_right=None, causal=False, dilation=1, norm="group", groups=1,
+                              eps=1e-5, gamma=None, beta=None, rowmin_bias=None, mean=None,
+                              rstd=None, persistent=True, one_launch=False, cooperative=False,
+                              channels_last=False):
+    """conv1d_gn_forward without a workspace, for callers that cannot
+    allocate: the library's own device scratch (NOALLOC_SCRATCH_BYTES per
+    device) serves as the workspace, and nothing is allocated here either, so
+    ``out`` (and, to export the statistics, ``mean``/``rstd``) must be given.
+    Raises C1GError (workspace) when the problem needs a larger workspace.
+    Calls on one device share the scratch: calls that overlap in time on one
+    device race; calls on one stream are ordered."""
+    lib = load_library()
+    C_out = w.shape[0] if isinstance(w, torch.Tensor) else -1
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
+        _per_channel(t, nm, C_out)
+    if not isinstance(out, torch.Tensor):
+        raise TypeError("out must be a tensor")
+    odt = _out_dtype(out, None)
+    desc, T_out = _conv_desc(x, w, stride, padding, pad_left, pad_right, causal, dilation,
+                             odt, channels_last, out)
+    nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent, one_launch,
+                   cooperative)
+    if mean is not None or rstd is not None:
+        if nd.norm == NORM_NONE:
+            raise ValueError("mean/rstd exports need a normalisation")
+        shp = _stats_shape(desc, nd, T_out, groups)
+        _shape(mean, "mean", shp)
+        _shape(rstd, "rstd", shp)
+    _conv_device(x, w)
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias"),
+                  (mean, "mean"), (rstd, "rstd")):
+        _need(t, nm, torch.float32, x.device)
+    _need(out, "out", odt, x.device)
+    st = lib.conv1d_gn_forward_noalloc(ctypes.byref(desc), ctypes.byref(nd), _ptr(x), _ptr(w),
+                                       _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(rowmin_bias),
+                                       _ptr(out), _ptr(mean), _ptr(rstd), _stream(x.device))
+    _raise(st, "conv1d_gn_forward_noalloc")
+    return out
 
 
 def gn_stats(y, groups, eps=1e-5):

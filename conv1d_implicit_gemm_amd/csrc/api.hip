@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/conv1d_gn.h"
 #include "launch.hpp"
@@ -464,13 +465,14 @@ int gn_apply_bf16(int64_t N, int64_t C, int64_t L, int32_t G, const uint16_t* y,
                                    L, G, (hipStream_t)stream));
 }
 
-int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
-                      const void* w, const float* bias, const float* gamma, const float* beta,
-                      const float* bias2, void* out, float* mean_out, float* rstd_out,
-                      void* ws, size_t ws_bytes, void* stream) {
-  if (!d || !nd) return C1G_ERR_INVALID_ARG;
-  const Plan p = make_plan(d, nd);
-  if (p.status != C1G_OK) return p.status;
+}  // extern "C"
+
+namespace {
+
+// The pointer checks of conv1d_gn_forward (everything but the workspace).
+int check_forward_ptrs(const Plan& p, const void* x, const void* w, const float* bias,
+                       const float* gamma, const float* beta, const float* bias2,
+                       const void* out, const float* mean_out, const float* rstd_out) {
   if (!x || !w || !out) return C1G_ERR_INVALID_ARG;
   if (p.epi == C1G_EPI_ROWMIN_BIAS && !bias2) return C1G_ERR_INVALID_ARG;
   const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
@@ -479,6 +481,49 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
       (bias2 && !aligned(bias2, 4)) || (mean_out && !aligned(mean_out, 4)) ||
       (rstd_out && !aligned(rstd_out, 4)))
     return C1G_ERR_MISALIGNED;
+  return C1G_OK;
+}
+
+// Device scratch of conv1d_gn_forward_noalloc, the workspace of callers that
+// cannot allocate; each device the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names the runtime's host-side
+// handle of the symbol, not device memory: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is ever given to kernels.
+static __device__ __align__(256) unsigned char scratch[C1G_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices];  // per device; null until looked up
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return C1G_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return C1G_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return C1G_ERR_HIP;
+    scratch_addr[dev] = ptr;
+  }
+  *out = scratch_addr[dev];
+  return C1G_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
+                      const void* w, const float* bias, const float* gamma, const float* beta,
+                      const float* bias2, void* out, float* mean_out, float* rstd_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (!d || !nd) return C1G_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, nd);
+  if (p.status != C1G_OK) return p.status;
+  const int pst = check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out);
+  if (pst != C1G_OK) return pst;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
   if (p.total > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
   hipStream_t s = (hipStream_t)stream;
@@ -563,6 +608,25 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
                            d->C_out, p.T_out, 0, 0, s);
   }
   return hip_status(e);
+}
+
+int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
+                              const void* w, const float* bias, const float* gamma,
+                              const float* beta, const float* bias2, void* out,
+                              float* mean_out, float* rstd_out, void* stream) {
+  if (!d || !nd) return C1G_ERR_INVALID_ARG;
+  const Plan p = make_plan(d, nd);
+  if (p.status != C1G_OK) return p.status;
+  const int pst = check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out);
+  if (pst != C1G_OK) return pst;
+  if (p.total > C1G_NOALLOC_SCRATCH_BYTES) return C1G_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.total > 0) {
+    const int st = scratch_address(&ws);
+    if (st != C1G_OK) return st;
+  }
+  return conv1d_gn_forward(d, nd, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, ws,
+                           p.total > 0 ? C1G_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 const char* c1g_status_string(int status) {

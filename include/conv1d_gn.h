@@ -238,6 +238,28 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* norm, const v
                       const float* bias2, void* out, float* mean_out, float* rstd_out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Device scratch conv1d_gn_forward_noalloc holds on each device it runs on
+ * (until the process ends): the largest workspace it can serve. */
+#define C1G_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* conv1d_gn_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation, arguments and results, without the
+ * workspace: the library uses its own static device scratch of
+ * C1G_NOALLOC_SCRATCH_BYTES per device (its address is looked up on the first
+ * call on each device).  The caller still allocates x, w, the parameters and
+ * the outputs.  Returns C1G_ERR_WORKSPACE, launching nothing, when
+ * c1g_conv1d_gn_workspace_size for these arguments exceeds the scratch.
+ * Allocates and frees nothing.  Every call on a device shares that device's
+ * scratch, which keeps the last call's contents (each call initialises what
+ * it reads): calls that may overlap in time on one device (other streams,
+ * other host threads) race on it and must be serialised by the caller; calls
+ * on one stream are ordered. */
+int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* norm, const void* x,
+                              const void* w, const float* bias, const float* gamma,
+                              const float* beta, const float* bias2, void* out,
+                              float* mean_out, float* rstd_out, void* stream);
+
 /* Name of the kernel route conv1d_gn_forward takes for these arguments, or
  * "invalid".  Pure host function.  Routes:
  *   "conv_only"          norm == C1G_NORM_NONE and no epilogue: the convolution

@@ -266,3 +266,30 @@ def test_channels_last_planning():
         a, b = _desc(dtype=dt, **lin), _desc(dtype=dt, x_layout=c1g.LAYOUT_NLC, **lin)
         assert c1g.route(a, gn) == c1g.route(b, gn)
         assert c1g.conv1d_gn_workspace_size(a, gn) == c1g.conv1d_gn_workspace_size(b, gn)
+
+
+def test_noalloc_rejects_before_any_launch():
+    """conv1d_gn_forward_noalloc checks its pointers and refuses problems whose
+    workspace exceeds its static scratch before anything touches a device
+    (fake addresses are safe: nothing is dereferenced or launched)."""
+    lib = c1g.load_library()
+    P = ctypes.c_void_p
+    good, odd = P(0x10000), P(0x10002)
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    d = _desc(dtype=c1g.C1G_BF16)
+    f = lib.conv1d_gn_forward_noalloc
+    assert f(ctypes.byref(d), ctypes.byref(gn), None, good, None, None, None, None, good,
+             None, None, None) == 1
+    assert f(ctypes.byref(d), ctypes.byref(gn), good, good, None, None, None, None, odd,
+             None, None, None) == 4
+    # the dilated-conv workload needs ~290 MB of workspace: more than the scratch
+    big = _desc(N=64, C_in=512, C_out=1024, T=4096, K=5, dilation=2, pad_left=2, pad_right=2,
+                dtype=c1g.C1G_BF16)
+    gn32 = c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0)
+    assert c1g.conv1d_gn_workspace_size(big, gn32) > c1g.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), ctypes.byref(gn32), good, good, None, None, None, None, good,
+             None, None, None) == 3
+    # invalid geometry is reported as such
+    bad = _desc(T=2, K=5, pad_left=0, pad_right=0)
+    assert f(ctypes.byref(bad), ctypes.byref(gn), good, good, None, None, None, None, good,
+             None, None, None) == 1
