@@ -5,23 +5,38 @@
 
 A step is one conv1d_gn_forward call (every kernel of the path) over one
 batch of seeded synthetic input already resident in HBM.  W untimed steps,
-then K steps timed with HIP events on the launch stream, bracketed by device
-synchronisation.  Prints ONE JSON line with the throughput (TFLOP/s of the
-implicit GEMM, 2*M*N*K per step), the roofline position of the dominant
-kernel, and the fp64 CPU oracle timed on this host's cores as a reference
-baseline.
+then K timed steps.  Before each timed step the L2 caches and the Infinity
+Cache are flushed (a 1 GiB buffer is read, so they hold only clean, unrelated
+lines), and the step is timed alone with HIP events on the launch stream:
+``ms_per_step`` and ``value`` are the median over the K steps (the minimum is
+reported beside it).  The same K steps back to back, caches warm, are
+reported under ``warm``.  ``roofline`` places the dominant kernel against the
+MI355X peak for both (``frac`` flushed, ``frac_warm``).
+
+Without --workload the line is for the headline workload (fp32 conv1d +
+GroupNorm, N16 C128->256 T1024 K3) and also carries
+  - ``configs``: the same protocol on the causal conv, the Linear + GroupNorm
+    + row-min, and the bf16 dilated conv with GroupNorm and with LayerNorm
+    over channels;
+  - ``passes``: the HBM-bound standalone passes (gn_stats, gn_apply,
+    gn_apply_bf16) on tensors of the dilated-conv output's and the headline
+    output's shapes, in GB/s of algorithmic bytes against the 8 TB/s peak;
+  - ``cpu_baseline``: the fp64 oracle timed on this host's cores.
 
 Other modes (used by the profiling runs recorded under profiles/):
     --mode copy     a plain device-to-device copy of known size, to scale the
                     FETCH_SIZE / WRITE_SIZE counters to bytes
+    --mode passes   only the standalone HBM-bound passes
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -39,6 +54,12 @@ KERNEL_SOURCES = {
     "fused_single_pass": ["conv1d_implicit_gemm_amd/csrc/k_fused_gn.hip",
                           "conv1d_implicit_gemm_amd/csrc/common.hpp"],
 }
+# the workloads timed beside the headline, in the order of the pages' configurations
+EXTRA_CONFIGS = ["causal_conv1d_f32_n32_c256x256_t8192_k4",
+                 "gemm_gn_rowmin_bf16_m1024_n8192_k8192",
+                 "conv1d_gn_bf16_n64_c512x1024_t4096_k5d2",
+                 "conv1d_lnc_bf16_n64_c512x1024_t4096_k5d2"]
+FLUSH_BYTES = 1 << 30
 
 
 def source_hash(route):
@@ -61,7 +82,7 @@ def stored_traffic(workload, route):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256_16") != source_hash(route):
+    if not KERNEL_SOURCES.get(route) or rec.get("kernel_source_sha256_16") != source_hash(route):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -110,23 +131,143 @@ def cpu_baseline(wl, inp, flops, budget_s=10.0):
                               "sample": "sample 0 of %d, one run in %.2f s, fp64" % (wl.N, el1)}}
 
 
-def cold_timing(op, stream, reps=10, flush_bytes=1 << 30):
-    """Per-step time with the L2 and Infinity Cache flushed before each step
-    (a 1 GiB buffer is overwritten first); median over reps, in ms."""
-    import torch
-    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
-    times = []
-    for _ in range(reps):
-        buf.fill_(1.0)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        op()
-        b.record(stream)
+class Timer:
+    """Per-step timing on one stream with HIP events, caches flushed or warm."""
+
+    def __init__(self, stream):
+        import torch
+        self.torch = torch
+        self.stream = stream
+        # filled once: reading it later leaves only clean, unrelated lines in
+        # every cache level (no write-back of the flush lands in a timed step)
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def flush(self):
+        self.torch.sum(self.buf, dim=0, out=self.sink)
+
+    def flushed(self, op, reps):
+        """Median and minimum (ms) over reps steps, each timed alone after a flush."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    del buf
-    times.sort()
-    return times[len(times) // 2], times[0]
+        for a, b in evs:
+            self.flush()
+            a.record(self.stream)
+            op()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        return statistics.median(t), t[0]
+
+    def warm(self, op, reps):
+        """Mean ms per step over reps back-to-back steps."""
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        for _ in range(reps):
+            op()
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+
+def prepared(wl, persistent=True, one_launch=False):
+    """The workload's seeded inputs on the device and a pre-marshalled call."""
+    import torch
+    import conv1d_implicit_gemm_amd as c1g
+    from conv1d_implicit_gemm_amd.workloads import make_inputs
+    inp = make_inputs(wl, 0)
+    d = {k: (v.to("cuda:0").contiguous() if v is not None else None) for k, v in inp.items()}
+    op = c1g.PreparedConv1dGN(d["x"], d["w"], d["bias"], stride=wl.stride,
+                              dilation=wl.dilation, pad_left=wl.pad_left,
+                              pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
+                              gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"],
+                              out_dtype=torch.bfloat16 if wl.out_dtype == "bf16"
+                              else torch.float32, persistent=persistent,
+                              one_launch=one_launch)
+    return inp, op
+
+
+def measure(wl, op, timer, steps, warmup):
+    """Flushed median/min and warm mean of one workload's step, with its roofline."""
+    flops = 2 * wl.N * op.T_out * wl.C_out * wl.C_in * wl.K
+    for _ in range(warmup):
+        op()
+    med, mn = timer.flushed(op, steps)
+    warm = timer.warm(op, steps)
+    bound, peak, unit = PEAKS[wl.dtype]
+    algo_bytes = (wl.N * wl.C_in * wl.T * wl.elem_bytes + wl.C_out * wl.C_in * wl.K *
+                  wl.elem_bytes + wl.N * wl.C_out * op.T_out * (2 if wl.out_dtype == "bf16" else 4))
+    tf = lambda ms: flops / (ms * 1e-3) / 1e12
+    return {"flops": flops, "ms_median": med, "ms_min": mn, "ms_warm": warm,
+            "tflops": tf(med), "tflops_warm": tf(warm), "bound": bound, "peak": peak,
+            "unit": unit, "frac": tf(med) / peak, "frac_warm": tf(warm) / peak,
+            "algo_bytes": algo_bytes}
+
+
+def config_of(wl, op):
+    return {"workload": wl.name, "N": wl.N, "C_in": wl.C_in, "C_out": wl.C_out, "T": wl.T,
+            "T_out": op.T_out, "K": wl.K, "stride": wl.stride, "dilation": wl.dilation,
+            "pad_left": wl.pad_left, "pad_right": wl.pad_right, "norm": wl.norm, "G": wl.G,
+            "rowmin_bias": wl.rowmin_bias, "out_dtype": wl.out_dtype, "route": op.route,
+            "parallelism": "single GPU"}
+
+
+def passes(timer, steps, warmup):
+    """The standalone HBM-bound passes on the dilated-conv output's shape
+    ([64, 1024, 4092], G 32) and the headline output's ([16, 256, 1024], G 32):
+    algorithmic bytes = every element read once (and written once by apply)."""
+    import torch
+    import conv1d_implicit_gemm_amd as c1g
+    res = {}
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    for tag, (N, C, L, G) in (("dilated_conv_out", (64, 1024, 4092, 32)),
+                              ("headline_out", (16, 256, 1024, 32))):
+        y = torch.randn((N, C, L), generator=g, device="cuda:0")
+        gam = torch.rand((C,), generator=g, device="cuda:0") + 0.5
+        bet = torch.randn((C,), generator=g, device="cuda:0") * 0.1
+        mean, rstd = c1g.gn_stats(y, G)
+        out = torch.empty_like(y)
+        yb = y.to(torch.bfloat16)
+        outb = torch.empty_like(yb)
+        n = N * C * L
+        # direct C-ABI calls with pre-marshalled arguments: per-call host work
+        # stays far below the kernels' time
+        lib = c1g.load_library()
+        ws_bytes = lib.c1g_gn_stats_workspace_size(N, C, L, G)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda:0")
+        st_mean, st_rstd = torch.empty_like(mean), torch.empty_like(rstd)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        sp = ctypes.c_void_p(timer.stream.cuda_stream)
+        a_stats = (N, C, L, G, 1e-5, P(y), P(st_mean), P(st_rstd), P(ws), ws_bytes, sp)
+        a_apply = (N, C, L, G, P(y), P(mean), P(rstd), P(gam), P(bet), P(out), sp)
+        a_applyb = (N, C, L, G, P(yb), P(mean), P(rstd), P(gam), P(bet), P(outb), sp)
+
+        def call(fn, a):
+            def run():
+                if fn(*a) != 0:
+                    raise RuntimeError("%s failed" % fn.__name__)
+            return run
+        cases = [("gn_stats", call(lib.gn_stats, a_stats), 4 * n),
+                 ("gn_apply", call(lib.gn_apply, a_apply), 8 * n),
+                 ("gn_apply_bf16", call(lib.gn_apply_bf16, a_applyb), 4 * n)]
+        for name, fn, nbytes in cases:
+            for _ in range(warmup):
+                fn()
+            med, mn = timer.flushed(fn, steps)
+            warm = timer.warm(fn, steps)
+            gbps = nbytes / (med * 1e-3) / 1e9
+            res["%s_%s" % (name, tag)] = {
+                "shape": [N, C, L], "G": G, "algorithmic_bytes": nbytes,
+                "ms_median": round(med, 5), "ms_min": round(mn, 5), "ms_warm": round(warm, 5),
+                "gbps": round(gbps, 1), "peak_gbps": PEAKS["hbm"][1],
+                "frac": round(gbps / PEAKS["hbm"][1], 4)}
+        torch.cuda.synchronize()
+        del y, out, yb, outb, ws
+    return res
 
 
 def copy_mode(args):
@@ -145,10 +286,11 @@ def copy_mode(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="time this workload alone (no configs, passes or CPU baseline)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "passes"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
                     help="element type of the output (bf16: rounded to nearest even)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,8 +298,8 @@ def main():
                     help="bf16 conv + GroupNorm/LayerNorm: time the multi-kernel split route "
                          "instead of the persistent single-kernel one")
     ap.add_argument("--one-launch", action="store_true",
-                    help="Linear + GroupNorm + row-min: one cooperative launch instead of the "
-                         "GEMM and a broadcast kernel")
+                    help="Linear + GroupNorm + row-min: one launch instead of the GEMM and a "
+                         "broadcast kernel")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -167,78 +309,70 @@ def main():
         sys.exit(2)
     if args.mode == "copy":
         return copy_mode(args)
+    steps = max(args.steps, 1)
 
     import torch
-    import conv1d_implicit_gemm_amd as c1g
-    from conv1d_implicit_gemm_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from conv1d_implicit_gemm_amd.workloads import HEADLINE, WORKLOADS
+
+    stream = torch.cuda.current_stream("cuda:0")
+    timer = Timer(stream)
+    if args.mode == "passes":
+        print(json.dumps({"mode": "passes", "steps": steps,
+                          "passes": passes(timer, steps, args.warmup)}), flush=True)
+        return
 
     name = args.workload or HEADLINE
     wl = WORKLOADS[name].replace(out_dtype=args.out_dtype)
-    dev = "cuda:0"
-    inp = make_inputs(wl, 0)
-    d = {k: (v.to(dev).contiguous() if v is not None else None) for k, v in inp.items()}
-    op = c1g.PreparedConv1dGN(d["x"], d["w"], d["bias"], stride=wl.stride,
-                              dilation=wl.dilation, pad_left=wl.pad_left,
-                              pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
-                              gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"],
-                              out_dtype=torch.bfloat16 if wl.out_dtype == "bf16"
-                              else torch.float32, persistent=not args.no_persistent,
-                              one_launch=args.one_launch)
-    T_out = op.T_out
-    flops = 2 * wl.N * T_out * wl.C_out * wl.C_in * wl.K
-    stream = torch.cuda.current_stream(dev)
-
-    for _ in range(args.warmup):
-        op()
-    torch.cuda.synchronize()
-
-    # timed region: K back-to-back steps on the launch stream
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        op()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-
-    # the dominant kernel's duration: on the single-pass route one step is one
-    # launch, so the events around the K back-to-back steps on the launch
-    # stream time that kernel (kernel time plus the launch-to-launch gap); on
-    # the multi-kernel routes the same figure is the whole step
-    kern_ms = ms_per_step
-
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    bound, peak, unit = PEAKS[wl.dtype]
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    algo_bytes = (wl.N * wl.C_in * wl.T * wl.elem_bytes + wl.C_out * wl.C_in * wl.K *
-                  wl.elem_bytes + wl.N * wl.C_out * T_out * (2 if wl.out_dtype == "bf16" else 4))
+    inp, op = prepared(wl, persistent=not args.no_persistent, one_launch=args.one_launch)
+    m = measure(wl, op, timer, steps, args.warmup)
     # stored counters were taken with an fp32 output
     traffic = stored_traffic(name, op.route) if wl.out_dtype == "f32" else None
     res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": round(m["tflops"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(m["ms_median"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes of the pages' workloads)",
-        "config": {"workload": name, "N": wl.N, "C_in": wl.C_in, "C_out": wl.C_out, "T": wl.T,
-                   "T_out": T_out, "K": wl.K, "stride": wl.stride, "dilation": wl.dilation,
-                   "pad_left": wl.pad_left, "pad_right": wl.pad_right, "norm": wl.norm,
-                   "G": wl.G, "rowmin_bias": wl.rowmin_bias, "out_dtype": wl.out_dtype,
-                   "route": op.route,
-                   "parallelism": "single GPU"},
-        "gbps_algorithmic": round(algo_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel_ms": round(kern_ms, 5),
-                     "algorithmic_flops_per_launch": flops},
+        "config": config_of(wl, op),
+        "timing": {"protocol": "each of the %d timed steps alone, HIP events on the launch "
+                               "stream, after reading a 1 GiB buffer (L2 and Infinity Cache "
+                               "hold only clean unrelated lines); value and ms_per_step are "
+                               "the median" % steps,
+                   "ms_min": round(m["ms_min"], 5),
+                   "warm": {"ms_per_step": round(m["ms_warm"], 5),
+                            "value": round(m["tflops_warm"], 3),
+                            "note": "the same steps back to back, caches warm"}},
+        "gbps_algorithmic": round(m["algo_bytes"] / (m["ms_median"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": m["bound"], "achieved": round(m["tflops"], 3), "peak": m["peak"],
+                     "unit": m["unit"], "frac": round(m["frac"], 4), "traffic": traffic,
+                     "kernel_ms": round(m["ms_median"], 5),
+                     "achieved_warm": round(m["tflops_warm"], 3),
+                     "frac_warm": round(m["frac_warm"], 4),
+                     "kernel_ms_warm": round(m["ms_warm"], 5),
+                     "algorithmic_flops_per_launch": m["flops"],
+                     "note": "one launch per step on this route: the step's event time is "
+                             "the kernel's" if op.route == "fused_single_pass" else
+                             "several launches per step: fractions are of the whole step"},
     }
-    cold_ms, cold_min = cold_timing(op, stream)
-    res["cold"] = {"ms_per_step_median": round(cold_ms, 5), "ms_per_step_min": round(cold_min, 5),
-                   "value": round(flops / (cold_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
-                   "note": "L2 and Infinity Cache flushed (1 GiB written) before each of 10 steps; "
-                           "value/ms_per_step above are warm back-to-back steps"}
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, inp, flops)
+    if args.workload is None:
+        cfgs = {}
+        for cname in EXTRA_CONFIGS:
+            cwl = WORKLOADS[cname]
+            _, cop = prepared(cwl)
+            cm = measure(cwl, cop, timer, steps, args.warmup)
+            cfgs[cname] = {"route": cop.route, "dtype": cwl.dtype,
+                           "ms_median": round(cm["ms_median"], 5),
+                           "ms_min": round(cm["ms_min"], 5), "ms_warm": round(cm["ms_warm"], 5),
+                           "tflops": round(cm["tflops"], 2),
+                           "tflops_warm": round(cm["tflops_warm"], 2),
+                           "peak": cm["peak"], "frac": round(cm["frac"], 4),
+                           "frac_warm": round(cm["frac_warm"], 4),
+                           "algorithmic_flops": cm["flops"]}
+            del cop
+            torch.cuda.empty_cache()
+        res["configs"] = cfgs
+        res["passes"] = passes(timer, steps, args.warmup)
+    if not args.no_cpu_baseline and args.workload is None:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, m["flops"])
     print(json.dumps(res), flush=True)
 
 
