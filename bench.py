@@ -7,9 +7,10 @@ A step is one conv1d_gn_forward call (every kernel of the path) over one
 batch of seeded synthetic input already resident in HBM.  W untimed steps,
 then K timed steps.  Before each timed step the L2 caches and the Infinity
 Cache are flushed (a 1 GiB buffer is read, so they hold only clean, unrelated
-lines), and the step is timed alone with HIP events on the launch stream:
-``ms_per_step`` and ``value`` are the median over the K steps (the minimum is
-reported beside it).  The same K steps back to back, caches warm, are
+lines), and timed with HIP events on the launch stream as the time of
+[flush, step] minus that of [flush] alone in the same rep: ``ms_per_step``
+and ``value`` are the median over the K steps (the minimum is reported beside
+it).  The same K steps back to back, caches warm, are
 reported under ``warm``.  ``roofline`` places the dominant kernel against the
 MI355X peak for both (``frac`` flushed, ``frac_warm``).
 
@@ -147,18 +148,27 @@ class Timer:
         self.torch.sum(self.buf, dim=0, out=self.sink)
 
     def flushed(self, op, reps):
-        """Median and minimum (ms) over reps steps, each timed alone after a flush."""
+        """Median and minimum (ms) over reps steps, each run right after a
+        flush.  An event between the flush and the step would add the step's
+        launch latency to its time (the queue processes the event marker
+        first), so each rep times [flush, step] and, just before it, [flush]
+        alone, both after an untimed flush (so neither flush writes back what
+        the step left dirty), and takes the difference."""
         torch = self.torch
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
+        E = lambda: torch.cuda.Event(enable_timing=True)
+        evs = [(E(), E(), E(), E()) for _ in range(reps)]
         torch.cuda.synchronize()
-        for a, b in evs:
+        for c, d, a, b in evs:
             self.flush()
+            c.record(self.stream)
+            self.flush()
+            d.record(self.stream)
             a.record(self.stream)
+            self.flush()
             op()
             b.record(self.stream)
         torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in evs)
+        t = sorted(a.elapsed_time(b) - c.elapsed_time(d) for c, d, a, b in evs)
         return statistics.median(t), t[0]
 
     def warm(self, op, reps):
@@ -333,10 +343,12 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded; shapes of the pages' workloads)",
         "config": config_of(wl, op),
-        "timing": {"protocol": "each of the %d timed steps alone, HIP events on the launch "
-                               "stream, after reading a 1 GiB buffer (L2 and Infinity Cache "
-                               "hold only clean unrelated lines); value and ms_per_step are "
-                               "the median" % steps,
+        "timing": {"protocol": "each of the %d timed steps right after reading a 1 GiB "
+                               "buffer (L2 and Infinity Cache then hold only clean unrelated "
+                               "lines), HIP events on the launch stream: time of [flush, step] "
+                               "minus time of [flush] in the same rep (no event between flush "
+                               "and step, so its launch overlaps the flush as in a stream of "
+                               "work); value and ms_per_step are the median" % steps,
                    "ms_min": round(m["ms_min"], 5),
                    "warm": {"ms_per_step": round(m["ms_warm"], 5),
                             "value": round(m["tflops_warm"], 3),

@@ -54,6 +54,27 @@ def test_bf16_conv_parity(wl):
     check_parity(wl)
 
 
+# LayerNorm over channels on the split route: the apply pass that walks the
+# channels of four positions (T_out % 4 == 0; a channel count that is no
+# multiple of its 32-channel blocks; fp32 and bf16 out) and the general one
+# (T_out % 4 != 0)
+LN_SPLIT_CASES = [
+    W("ln_split_cols_f32out", N=3, C_in=48, C_out=200, T=1032, K=5, dilation=2, pad_left=2,
+      pad_right=2, norm="layer_channels", persistent=False, **BF),
+    W("ln_split_cols_bf16out", N=2, C_in=40, C_out=70, T=520, K=3, pad_left=1, pad_right=1,
+      norm="layer_channels", persistent=False, out_dtype="bf16", **BF),
+    W("ln_split_general_T_out_odd", N=2, C_in=40, C_out=96, T=523, K=3, pad_left=1,
+      pad_right=1, norm="layer_channels", persistent=False, **BF),
+]
+
+
+@pytest.mark.parametrize("wl", LN_SPLIT_CASES, ids=lambda w: w.name)
+def test_ln_split_parity(wl):
+    from tests.gpu_util import library_route
+    assert library_route(wl) == "split"
+    check_parity(wl)
+
+
 # K = 1, T = 1: the GEMM route, with every epilogue combination
 GEMM_CASES = [
     W("gemm_gn_rowmin_fused", N=70, C_in=256, C_out=512, T=1, K=1, G=32, bias=False,
