@@ -24,10 +24,11 @@
 // step from LDS before issuing its own MQ independent MFMAs; scheduling fences
 // keep that order and keep each step's accumulators apart.
 //
-// Epilogue: the group statistics are taken in two passes over the registers
-// (sum -> mean, then sum of squared deviations -> variance), reduced across
-// lanes with xor shuffles and across waves in a fixed order through LDS
-// (deterministic); each value is then normalised, scaled and written once.
+// Epilogue: each wave takes the exact statistics of its part of each group
+// (two passes over its registers: sum -> mean, then squared deviations from
+// it), reduced across lanes with DPP and lane swaps; one exchange through LDS
+// merges the waves' (mean, M2) in a fixed order (deterministic); each value is
+// then normalised, scaled and written once.
 //
 // blockIdx -> (n, channel block) is remapped so that the workgroups of one
 // sample land on the same XCD and share its L2 copy of x[n].
@@ -131,6 +132,19 @@ __device__ __forceinline__ void compute_chunk(const float* xs, const float* ws,
   }
 }
 
+// The channel's bias, gamma and beta, loaded at the start of the kernel so
+// that their latency hides under the K loop (0 / 1 / 0 past C_out or absent).
+struct ChanParams {
+  float bias, ga, be;
+};
+
+__device__ __forceinline__ ChanParams load_params(const FusedArgs& a, int c) {
+  const bool ok = c < a.C_out;
+  return ChanParams{(a.bias != nullptr && ok) ? a.bias[c] : 0.f,
+                    (a.gamma != nullptr && ok) ? a.gamma[c] : 1.f,
+                    (a.beta != nullptr && ok) ? a.beta[c] : 0.f};
+}
+
 // Statistics, normalisation and the single write of the output slab.  lo /
 // hi: LDS no longer in use (waves 0-7 / 8-15, 16 x (P + 4) floats each) in
 // which a wave re-lays its normalised fp32 tile so that each streaming store
@@ -139,28 +153,19 @@ __device__ __forceinline__ void compute_chunk(const float* xs, const float* ws,
 // merge: 1.5x the output's bytes reached HBM); nullptr: direct stores.
 template <int MQ>
 __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
-                                         f32x4 (&acc)[MQ], float* red, float* lo = nullptr,
-                                         float* hi = nullptr) {
+                                         f32x4 (&acc)[MQ], const ChanParams& prm, f32x2* red,
+                                         float* lo = nullptr, float* hi = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t n = co.n, T_out = a.T_out;
   const int c = co.cbase + lr;
   const bool cvalid = c < a.C_out;
-  const float bias = (a.bias != nullptr && cvalid) ? a.bias[c] : 0.f;
   const int cpg = (int)(a.C_out / a.G);
   const int gl = lr / cpg;                 // group within the block
   const int t_lane = wave * MQ * 16 + 4 * kq;
   const bool full = FusedGeom<MQ>::TCOV == T_out;
 
-  float sum = 0.f;
-#pragma unroll
-  for (int m = 0; m < MQ; ++m) {
-    acc[m] += bias;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (full || t_lane + m * 16 + r < T_out) sum += acc[m][r];
-  }
   // lanes of one group differ in the low log2(cpg) bits of lr and in kq
   // (cpg is 1, 2, 4, 8 or 16: a group is an aligned run of lr values)
   auto group_reduce = [&](float v) {
@@ -170,28 +175,65 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
     if (cpg > 8) v += dpp<kDppMirror>(v);
     return lane_sum<48>(v);
   };
-  auto block_total = [&](float v) {
-    v = group_reduce(v);
-    if (kq == 0 && (lr % cpg) == 0) red[wave * CB + gl] = v;
-    __syncthreads();
-    float tot = 0.f;
+  // Each wave first takes the exact statistics of its own part of each group
+  // (two passes over its registers: the mean, then the squared deviations
+  // from it), then one exchange through LDS merges the 16 waves' (mean, M2)
+  // in a fixed order.  The wave's valid positions, hence its count per group:
+  const int64_t vt64 = T_out - (int64_t)wave * MQ * 16;
+  const int vt = (int)(vt64 < 0 ? 0 : (vt64 < MQ * 16 ? vt64 : MQ * 16));
+  const float cnt_w = (float)(cpg * vt);
+  float sum = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < NW; ++wv) tot += red[wv * CB + gl];
-    __syncthreads();
-    return tot;
-  };
-  const float cnt = (float)cpg * (float)T_out;
-  const float mean = block_total(sum) / cnt;
+  for (int m = 0; m < MQ; ++m) {
+    acc[m] += prm.bias;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (full || t_lane + m * 16 + r < T_out) sum += acc[m][r];
+  }
+  const float mean_w = cnt_w > 0.f ? group_reduce(sum) / cnt_w : 0.f;
   float ss = 0.f;
 #pragma unroll
   for (int m = 0; m < MQ; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (full || t_lane + m * 16 + r < T_out) {
-        const float dv = acc[m][r] - mean;
+        const float dv = acc[m][r] - mean_w;
         ss += dv * dv;
       }
-  const float var = block_total(ss) / cnt;
+  const float m2_w = group_reduce(ss);
+  if (kq == 0 && (lr % cpg) == 0) red[wave * CB + gl] = f32x2{mean_w, m2_w};
+  __syncthreads();
+  float mean, var;
+  if (full) {
+    // every wave holds the same count n_w of each group: the mean of the
+    // group is the mean of the wave means and M2 = sum M2_w + n_w * sum
+    // (mean_w - mean)^2, exactly
+    float sm = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) sm += red[wv * CB + gl][0];
+    mean = sm * (1.0f / NW);
+    float m2 = 0.f, dd = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      const f32x2 e = red[wv * CB + gl];
+      const float dm = e[0] - mean;
+      m2 += e[1];
+      dd += dm * dm;
+    }
+    var = (m2 + cnt_w * dd) / (cnt_w * NW);
+  } else {
+    // unequal counts (the sequence ends inside the last waves' rows): the
+    // pairwise merge in wave order
+    Stats st = {0.f, 0.f, 0.f};
+    for (int wv = 0; wv < NW; ++wv) {
+      const int64_t v64 = T_out - (int64_t)wv * MQ * 16;
+      const int v = (int)(v64 < 0 ? 0 : (v64 < MQ * 16 ? v64 : MQ * 16));
+      const f32x2 e = red[wv * CB + gl];
+      st = stats_merge(st, Stats{(float)(cpg * v), e[0], e[1]});
+    }
+    mean = st.mean;
+    var = st.m2 / st.n;
+  }
   const float rstd = 1.0f / sqrtf(var + a.eps);
 
   // fp32 out, whole wave tile inside [0, T_out), aligned: through LDS
@@ -199,9 +241,8 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
   constexpr int LPC = P / 4, CPI = 64 / LPC;  // lanes per channel row; rows per store
   if (lo != nullptr && !a.out_bf16 && (T_out & 3) == 0 &&
       (((uintptr_t)a.out) & 15) == 0 && (int64_t)(wave + 1) * P <= T_out) {
-    const float ga = (a.gamma != nullptr && cvalid) ? a.gamma[c] : 1.f;
-    const float be = (a.beta != nullptr && cvalid) ? a.beta[c] : 0.f;
-    const float sc = rstd * ga;
+    const float be = prm.be;
+    const float sc = rstd * prm.ga;
     float* tile = (wave < NW / 2 ? lo : hi) + (wave % (NW / 2)) * (CB * RS);
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
@@ -229,9 +270,8 @@ __device__ __forceinline__ void epilogue(const FusedArgs& a, const Coord& co,
   }
 
   if (cvalid) {
-    const float ga = a.gamma ? a.gamma[c] : 1.f;
-    const float be = a.beta ? a.beta[c] : 0.f;
-    const float sc = rstd * ga;
+    const float be = prm.be;
+    const float sc = rstd * prm.ga;
     // out as fp32, or rounded to bf16 (out_bf16)
     auto store = [&](auto* out) __attribute__((always_inline)) {
       auto* dst = out + (n * a.C_out + c) * T_out;
@@ -276,7 +316,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) float Xs1[CK * Gm::XS];
   __shared__ __attribute__((aligned(16))) float Ws0[KT * CK * CB];
   __shared__ __attribute__((aligned(16))) float Ws1[KT * CK * CB];
-  __shared__ float red[NW * CB];
+  __shared__ f32x2 red[NW * CB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -348,6 +388,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
     }
   };
 
+  const ChanParams prm = load_params(a, cbase + lr);
   f32x4 acc[MQ];
 #pragma unroll
   for (int m = 0; m < MQ; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -376,7 +417,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_dma_kernel(FusedArgs a) {
     wait_all_mem();
     __syncthreads();
   }
-  epilogue<MQ>(a, co, acc, red, Xs0, Xs1);
+  epilogue<MQ>(a, co, acc, prm, red, Xs0, Xs1);
 }
 
 // ------------------------------------------------------------ register-staged variant
@@ -387,7 +428,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_regs_kernel(FusedArgs a) {
   using Gm = FusedGeom<MQ>;
   __shared__ __attribute__((aligned(16))) float Xs[CK * Gm::XS];
   __shared__ __attribute__((aligned(16))) float Ws[KT * CK * CB];
-  __shared__ float red[NW * CB];
+  __shared__ f32x2 red[NW * CB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -447,6 +488,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_regs_kernel(FusedArgs a) {
     }
   };
 
+  const ChanParams prm = load_params(a, cbase + lr);
   f32x4 acc[MQ];
 #pragma unroll
   for (int m = 0; m < MQ; ++m) acc[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -465,7 +507,7 @@ __global__ __launch_bounds__(NTHR) void fused_gn_regs_kernel(FusedArgs a) {
       __syncthreads();
     }
   }
-  epilogue<MQ>(a, co, acc, red);
+  epilogue<MQ>(a, co, acc, prm, red);
 }
 
 template <int MQ, int KT>
