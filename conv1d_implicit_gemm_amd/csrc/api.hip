@@ -194,8 +194,13 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   off = align_up(off + stat_elems * sizeof(float));
   p.off_rstd = off;
   off = align_up(off + stat_elems * sizeof(float));
-  p.off_sync = off;  // rounds * samples-per-round counters + 1 fault word (<= 2N + 1)
-  if (p.route == R_PERSIST) off = align_up(off + (size_t)(2 * d->N + 2) * sizeof(unsigned));
+  // rounds * samples-per-round * barrier groups counters + 1 fault word
+  // (rounds * samples-per-round < 2N; groups <= the tiles along one axis)
+  p.off_sync = off;
+  if (p.route == R_PERSIST) {
+    const int64_t groups = p.n_ttiles > p.n_ctiles ? p.n_ttiles : p.n_ctiles;
+    off = align_up(off + (size_t)(2 * d->N * groups + 2) * sizeof(unsigned));
+  }
   p.total = (p.route == R_CONV_ONLY) ? conv_bytes : off;
   return p;
 }

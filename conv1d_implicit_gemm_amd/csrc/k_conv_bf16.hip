@@ -176,10 +176,26 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
     conv_epilogue<WM, WN, WGM, WGN>(a, EPI_LN_PART, acc, n, t0, c0, ttile, ctile, wm, wn, red,
                                     true, false);
   }
-  // an incomplete set of partials (a wait that gave up) yields NaN statistics,
-  // hence a NaN output, never a plausible wrong one
+  // Wait only for the workgroups whose partials this tile's statistics need:
+  // GroupNorm, the position tiles of its groups' channel tiles; LayerNorm,
+  // the channel tiles of its position tile (fused_barrier_groups).  An
+  // incomplete set of partials (a wait that gave up) yields NaN statistics,
+  // hence a NaN output, never a plausible wrong one.
+  int nsub, sub, expect;
+  if constexpr (gn) {
+    const int cpt = cpg > TN ? cpg / TN : 1;  // channel tiles per group
+    nsub = a.n_ctiles / cpt;
+    sub = ctile / cpt;
+    expect = a.n_ttiles * cpt;
+  } else {
+    nsub = a.n_ttiles;
+    sub = ttile;
+    expect = a.n_ctiles;
+  }
+  (void)tps;
   const float poison =
-      sample_barrier(a.sync + (int64_t)round * a.spr + slot, (unsigned)tps, a.fault, a.polls)
+      sample_barrier(a.sync + ((int64_t)round * a.spr + slot) * nsub + sub, (unsigned)expect,
+                     a.fault, a.polls)
           ? 0.f : __builtin_nanf("");
 
   float* mean_s = lds;        // merged statistics of this tile
@@ -314,8 +330,12 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const int total = FUSE != 0 ? (int)gridDim.x : tps * (int)a.N;
   int lin = blockIdx.x;
   if ((total & 7) == 0) lin = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int ctile = lin % a.n_ctiles;
-  const int ttile = (lin / a.n_ctiles) % a.n_ttiles;
+  // (The persistent GroupNorm kernel orders the tiles of a sample with the
+  // t-tile fastest instead, so that the position tiles of a channel tile,
+  // which wait for each other, share an XCD.)
+  const bool tfast = FUSE == EPI_GN_FUSED;
+  const int ctile = tfast ? (lin / a.n_ttiles) % a.n_ctiles : lin % a.n_ctiles;
+  const int ttile = tfast ? lin % a.n_ttiles : (lin / a.n_ctiles) % a.n_ttiles;
   const int slot = lin / tps;  // FUSE: sample slot within a round
   const int64_t t0_ = (int64_t)ttile * TM;
   const int c0_ = ctile * TN;
@@ -796,6 +816,13 @@ int capacity_w(int K) {
 }
 }  // namespace
 
+int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctiles) {
+  if (epi == EPI_LN_FUSED) return n_ttiles;
+  const int64_t cpg = C_out / G;
+  const int64_t cpt = cpg > TN ? cpg / TN : 1;
+  return (int)(n_ctiles / cpt);
+}
+
 int conv_bf16_fused_capacity(int stride, int K, int dilation) {
   const int tm = conv_bf16_tile_m(stride, K, dilation);
   if (tm == 512) return capacity_w<8>(K);
@@ -812,7 +839,9 @@ hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStre
   a.spr = (int32_t)spr;
   a.rounds = (int32_t)((a.N + spr - 1) / spr);
   // counters (and the fault word just after them) start at zero
-  const int64_t words = (int64_t)a.spr * a.rounds + 1;
+  const int64_t words =
+      (int64_t)a.spr * a.rounds *
+          fused_barrier_groups(epi, a.C_out, a.G, a.n_ttiles, a.n_ctiles) + 1;
   a.fault = a.sync + (words - 1);
   a.polls = barrier_poll_limit();
   hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,

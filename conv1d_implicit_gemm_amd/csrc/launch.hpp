@@ -42,7 +42,7 @@ struct ConvArgs {
   float* rstd_out;
   float eps;
   int32_t G;
-  unsigned* sync;      // [rounds * spr] arrival counters, zero at launch
+  unsigned* sync;      // [rounds * spr * barrier groups] arrival counters, zero at launch
   int32_t spr;         // samples per round (spr * tiles per sample workgroups)
   int32_t rounds;      // ceil(N / spr)
   unsigned* fault;     // set when a barrier wait gives up (never on a full GPU)
@@ -94,6 +94,11 @@ hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s);
 // unknown); the launch zeroes the counters, fills spr/rounds and launches
 // cooperatively.
 int conv_bf16_fused_capacity(int stride, int K, int dilation);
+// Workgroups of a persistent round wait for each other in groups: GroupNorm,
+// the position tiles of a group's channel tiles; LayerNorm over channels, the
+// channel tiles of a position tile.  Groups per sample (one arrival counter
+// each per round and sample slot):
+int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctiles);
 hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStream_t s);
 
 // ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
