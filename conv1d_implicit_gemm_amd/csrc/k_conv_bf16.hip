@@ -242,12 +242,22 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
       const int64_t t = t0 + tl;
       float mu = 0.f, rs = 0.f;
       if (t < T_out) {
+        // the channel tiles' partials of (n, t), eight loads in flight at a
+        // time (one by one, each load's round trip to the point of coherence
+        // was paid in sequence), merged in channel-tile order
         Stats st = {0.f, 0.f, 0.f};
-        for (int ct = 0; ct < a.n_ctiles; ++ct) {
-          const int64_t rem = a.C_out - (int64_t)ct * TN;
-          const float cnt = (float)(rem < TN ? rem : TN);
-          const f32x2 v = load_partial_coherent(a.part + ((n * a.n_ctiles + ct) * T_out + t) * 2);
-          st = stats_merge(st, Stats{cnt, v[0], v[1]});
+        const float* pp = a.part + (n * a.n_ctiles * T_out + t) * 2;
+        const int nct = a.n_ctiles;
+        const int crem = (int)(a.C_out - (int64_t)(nct - 1) * TN);  // last tile's channels
+        for (int ct0 = 0; ct0 < nct; ct0 += 8) {
+          f32x2 v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (ct0 + k < nct) v[k] = load_partial_coherent(pp + (int64_t)(ct0 + k) * T_out * 2);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (ct0 + k < nct)
+              st = stats_merge(st, Stats{(float)(ct0 + k == nct - 1 ? crem : TN), v[k][0], v[k][1]});
         }
         mu = st.mean + poison;
         rs = 1.0f / sqrtf(st.m2 / st.n + a.eps) + poison;
