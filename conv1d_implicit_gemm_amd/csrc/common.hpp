@@ -66,6 +66,38 @@ __device__ __forceinline__ float lane_sum(float v) {
   if (MASK & 32) { const f32x2 p = pair32(v); v = p[0] + p[1]; }
   return v;
 }
+// lane_sum of the four elements of v at once: four independent chains per
+// cross-lane step, so no step waits on the one before it.
+template <int MASK>
+__device__ __forceinline__ f32x4 lane_sum4(f32x4 v) {
+  static_assert(((MASK & 15) & ((MASK & 15) + 1)) == 0, "row bits contiguous from bit 0");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (MASK & 1) v[k] += dpp<kDppXor1>(v[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (MASK & 2) v[k] += dpp<kDppXor2>(v[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (MASK & 4) v[k] += dpp<kDppHalfMirror>(v[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (MASK & 8) v[k] += dpp<kDppMirror>(v[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (MASK & 16) { const f32x2 p = pair16(v[k]); v[k] = p[0] + p[1]; }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (MASK & 32) { const f32x2 p = pair32(v[k]); v[k] = p[0] + p[1]; }
+  }
+  return v;
+}
+
 // Minimum over lanes differing in bits 16 and 32 of the lane index.
 __device__ __forceinline__ float lane_min48(float v) {
   f32x2 p = pair16(v);

@@ -23,6 +23,8 @@
 // persistent kernel normalises the registers afterwards).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -88,31 +90,49 @@ __device__ __forceinline__ void gn_wave_channel_stats(const ConvArgs& a,
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t T_out = a.T_out;
   // the wave's valid positions: the same count for every channel
-  const int64_t vt = T_out - (t0 + wm * WM * 16);
-  const float cnt = (float)(vt < 0 ? 0 : (vt < WM * 16 ? vt : WM * 16));
-#pragma unroll
-  for (int jn = 0; jn < WN; ++jn) {
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-        if (t < T_out) sum += acc[i][jn][r];
-      }
-    sum = lane_sum<48>(sum);
-    const float mean = cnt > 0.f ? sum / cnt : 0.f;
-    float m2 = 0.f;
+  const int64_t vt64 = T_out - (t0 + wm * WM * 16);
+  const int vt = (int)(vt64 < 0 ? 0 : (vt64 < WM * 16 ? vt64 : WM * 16));
+  const float cnt = (float)vt;
+  // The sums of the four channel columns of a lane at once, their cross-lane
+  // sums together (four independent chains per step), then the squared
+  // deviations the same way.  FULL: every position of the wave valid (all but
+  // the last position tile), no masks.
+  auto cols = [&](auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + wm * WM * 16 + i * 16 + 4 * kq + r;
-        if (t < T_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
-      }
-    m2 = lane_sum<48>(m2);
-    if (active && kq == 0) red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean, m2};
-  }
+      for (int r = 0; r < 4; ++r)
+        if (FULL || i * 16 + 4 * kq + r < vt) {
+#pragma unroll
+          for (int jn = 0; jn < WN; ++jn) sum[jn] += acc[i][jn][r];
+        }
+    const f32x4 mean = cnt > 0.f ? lane_sum4<48>(sum) / cnt : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (FULL || i * 16 + 4 * kq + r < vt) {
+#pragma unroll
+          for (int jn = 0; jn < WN; ++jn) {
+            const float dv = acc[i][jn][r] - mean[jn];
+            m2[jn] += dv * dv;
+          }
+        }
+    m2 = lane_sum4<48>(m2);
+    if (active && kq == 0) {
+#pragma unroll
+      for (int jn = 0; jn < WN; ++jn)
+        red[wm * TN + wn * WN * 16 + jn * 16 + lr] = Stats{cnt, mean[jn], m2[jn]};
+    }
+  };
+  static_assert(WN == 4, "four channel columns per lane");
+  if (vt == WM * 16)
+    cols(std::true_type{});
+  else
+    cols(std::false_type{});
 }
 
 template <int WM, int WN, int WGM, int WGN>
@@ -167,28 +187,42 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, int epi,
     const int vc = a.C_out - (c0 + wn * WN * 16);
     const float cnt = (float)(vc < 0 ? 0 : (vc < WN * 16 ? vc : WN * 16));
     const float inv = cnt > 0.f ? 1.0f / cnt : 0.f;
+    // Per MFMA row block, the four positions of a lane at once: their sums
+    // over the lane's channels, cross-lane sums of all four together (four
+    // independent chains per step), then the same for the squared deviations.
+    // FULL: every channel of the wave inside C_out (all but a ragged last
+    // channel tile), no masks.
+    auto rows = [&](auto full_tag) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      bool cin[WN];
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+      for (int jn = 0; jn < WN; ++jn) cin[jn] = FULL || (jn * 16 + lr < vc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float sum = 0.f;
+      for (int i = 0; i < WM; ++i) {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jn = 0; jn < WN; ++jn) {
-          const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-          if (c < a.C_out) sum += acc[i][jn][r];
+        for (int jn = 0; jn < WN; ++jn)
+          if (cin[jn]) sum += acc[i][jn];
+        const f32x4 mean = lane_sum4<15>(sum) * inv;
+        f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jn = 0; jn < WN; ++jn)
+          if (cin[jn]) {
+            const f32x4 dv = acc[i][jn] - mean;
+            m2 += dv * dv;
+          }
+        m2 = lane_sum4<15>(m2);
+        if (active && lr == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red[wn * TM + wm * WM * 16 + i * 16 + 4 * kq + r] = Stats{cnt, mean[r], m2[r]};
         }
-        sum = lane_sum<15>(sum);
-        const float mean = sum * inv;
-        float m2 = 0.f;
-#pragma unroll
-        for (int jn = 0; jn < WN; ++jn) {
-          const int c = c0 + wn * WN * 16 + jn * 16 + lr;
-          if (c < a.C_out) { const float dv = acc[i][jn][r] - mean; m2 += dv * dv; }
-        }
-        m2 = lane_sum<15>(m2);
-        const int tl = wm * WM * 16 + i * 16 + 4 * kq + r;
-        if (active && lr == 0) red[wn * TM + tl] = Stats{cnt, mean, m2};
       }
+    };
+    if (vc >= WN * 16)
+      rows(std::true_type{});
+    else
+      rows(std::false_type{});
     __syncthreads();
     for (int tl = tid; tl < TM; tl += blockDim.x) {
       const int64_t t = t0 + tl;
