@@ -29,16 +29,16 @@ inline unsigned barrier_poll_limit() {
   return 1u << 22;
 }
 
-// Every thread of the workgroup returns once `expect` workgroups have arrived
-// on *ctr (this one included).  Waits for this wave's outstanding memory
+// sample_barrier: every thread of the workgroup returns once `expect`
+// workgroups have arrived on *ctr (this one included).  Waits for this wave's outstanding memory
 // operations first, so every store the workgroup issued before the call is
 // visible to the others once they see its arrival.  The wait gives up after
 // a bound no legitimate wait approaches (in a cooperative launch every
 // workgroup is resident), records that in *fault and returns false, so no
 // path can hang; the caller then poisons what depended on the others.
-__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault,
-                                               unsigned max_polls) {
-  __shared__ int complete;
+// The two halves of the wait, for callers with work to issue in between
+// (barrier_arrive, then barrier_wait); sample_barrier is both.
+__device__ __forceinline__ void barrier_arrive(unsigned* ctr) {
   // This wave's stores are done: the hardware wait, and (memory clobber) no
   // store the compiler could otherwise sink past it.  Together with the
   // workgroup barrier below, every store of the workgroup has been
@@ -49,8 +49,14 @@ __device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, u
   // so no cache flush or invalidation is needed on either side.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0)
     __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool barrier_wait(unsigned* ctr, unsigned expect, unsigned* fault,
+                                             unsigned max_polls) {
+  __shared__ int complete;
+  if (threadIdx.x == 0) {
     unsigned spins = 0;
     int ok = 1;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
@@ -65,6 +71,12 @@ __device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, u
   }
   __syncthreads();
   return complete != 0;
+}
+
+__device__ __forceinline__ bool sample_barrier(unsigned* ctr, unsigned expect, unsigned* fault,
+                                               unsigned max_polls) {
+  barrier_arrive(ctr);
+  return barrier_wait(ctr, expect, fault, max_polls);
 }
 
 __global__ void zero_u32_kernel(unsigned* p, int64_t count) {

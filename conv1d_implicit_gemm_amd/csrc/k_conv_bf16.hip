@@ -133,12 +133,18 @@ __device__ __forceinline__ float group_lane_sum(float v, int w) {
 // chunk's mean is the mean of its channel means and its M2 the sum of the
 // channel M2s plus count * (channel mean - chunk mean)^2 (exact).
 // LayerNorm partials: as on the split path, per position and channel tile.
-template <int WM, int EPI>
+//
+// between(): issued after this workgroup has published its partials and
+// counted itself in, before it waits for the others (the caller's prefetch of
+// its next round's first chunk, into LDS the rest of the epilogue leaves
+// alone: the window stage 0 and the weight stage 0, which held `red`).
+template <int WM, int EPI, typename Between>
 __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
                                                     f32x4 (&acc)[WM][WN], int64_t n,
                                                     int64_t t0, int c0, int ttile, int ctile,
                                                     int wm, int wn, int round, int slot,
-                                                    int tps, Stats* red, float* lds) {
+                                                    int tps, Stats* red, float* lds,
+                                                    Between between) {
   constexpr int TM = WGM * WM * 16;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,10 +199,11 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
     expect = a.n_ctiles;
   }
   (void)tps;
+  unsigned* const ctr = a.sync + ((int64_t)round * a.spr + slot) * nsub + sub;
+  barrier_arrive(ctr);
+  between();
   const float poison =
-      sample_barrier(a.sync + ((int64_t)round * a.spr + slot) * nsub + sub, (unsigned)expect,
-                     a.fault, a.polls)
-          ? 0.f : __builtin_nanf("");
+      barrier_wait(ctr, (unsigned)expect, a.fault, a.polls) ? 0.f : __builtin_nanf("");
 
   float* mean_s = lds;        // merged statistics of this tile
   float* rstd_s = lds + 512;
@@ -350,6 +357,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const int64_t t0_ = (int64_t)ttile * TM;
   const int c0_ = ctile * TN;
   const int rounds = FUSE != 0 ? a.rounds : 1;
+  bool prefetched = false;  // this round's chunk 0 already issued
   for (int round = 0; round < rounds; ++round) {
   const ConvArgs& a = FUSE != 0 ? round_args() : a_;
   const int64_t n = FUSE != 0 ? (int64_t)round * a.spr + slot : (int64_t)slot;
@@ -375,15 +383,19 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const uint32_t lane_x =
       (uint32_t)((lane >> 2) * row_bytes + 16 * ((lane & 3) ^ swz(lane >> 2)));
   const uint32_t lane_w = (uint32_t)(16 * lane);
-  auto copy = [&](int p, int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
+  auto copy_from = [&](const char* xw, int p, int chunk, u16* xs, u16* ws)
+      __attribute__((always_inline)) {
     int piece = wave + NWAVE * p;
     if (piece >= NPIECE) piece = NPIECE - 1;
     if (piece < XP)
-      dma16(xwin + (int64_t)chunk * (CK * 2) + (int64_t)16 * piece * row_bytes, lane_x,
+      dma16(xw + (int64_t)chunk * (CK * 2) + (int64_t)16 * piece * row_bytes, lane_x,
             (char*)xs + piece * 1024);
     else
       dma16(wimg + (int64_t)chunk * (KT * TN * RW * 2) + (piece - XP) * 1024, lane_w,
             (char*)ws + (piece - XP) * 1024);
+  };
+  auto copy = [&](int p, int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
+    copy_from(xwin, p, chunk, xs, ws);
   };
   auto stage = [&](int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
 #pragma unroll
@@ -505,7 +517,9 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // earlier.
   const int n_chunks = a.n_chunks, last = n_chunks - 1;
   auto cl = [&](int c) { return c < last ? c : last; };
-  stage(0, Xs0, Ws0);
+  // the persistent kernel's later rounds find chunk 0 already copied (issued
+  // by the previous round while it waited at its barrier)
+  if (!prefetched) stage(0, Xs0, Ws0);
   wait_all_mem();
   lds_barrier();
   read_tap(Xs0, Ws0, 0);
@@ -538,8 +552,18 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   if constexpr (FUSE == 0) {
     conv_epilogue<WM, WN, WGM, WGN>(a, epi, acc, n, t0, c0, ttile, ctile, wm, wn, (Stats*)Ws0);
   } else {
+    // while this round waits at its barrier: the next round's chunk 0
+    const int64_t n_next = n + a.spr;
+    prefetched = n_next < a.N;
     fused_norm_epilogue<WM, FUSE>(a, acc, n, t0, c0, ttile, ctile, wm, wn, round, slot, tps,
-                                  (Stats*)Ws0, (float*)Ws1);
+                                  (Stats*)Ws0, (float*)Ws1, [&]() __attribute__((always_inline)) {
+                                    if (n_next < a.N) {
+                                      const char* xw = (const char*)a.ximg +
+                                                       (n_next * a.T_img + t0 * s) * row_bytes;
+#pragma unroll
+                                      for (int p = 0; p < PPW; ++p) copy_from(xw, p, 0, Xs0, Ws0);
+                                    }
+                                  });
     __syncthreads();  // the LDS is reused by the next round
   }
   }  // rounds
