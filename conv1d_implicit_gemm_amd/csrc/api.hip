@@ -250,8 +250,16 @@ int run_conv(const Plan& p, const c1g_conv_desc* d, const void* x, const void* w
   }
   ConvArgs a = conv_args(p, d, x, bias, y, ws);
   if (p.bf16) {
+    const bool fused = epi == EPI_GN_FUSED || epi == EPI_LN_FUSED;
+    // the persistent kernel's arrival counters, zeroed by the weight pack
+    const int64_t zw =
+        fused ? conv_bf16_fused_sync_words(d->N, p.n_ttiles * p.n_ctiles, d->stride, d->K,
+                                           d->dilation, epi, d->C_out, nd->G, p.n_ttiles,
+                                           p.n_ctiles)
+              : 0;
+    if (fused && zw < 1) return C1G_ERR_HIP;
     e = conv_bf16_pack((const uint16_t*)w, (uint16_t*)(ws + p.off_pack), d->C_in, d->C_out,
-                       d->K, s);
+                       d->K, s, fused ? (unsigned*)(ws + p.off_sync) : nullptr, zw);
     if (e != hipSuccess) return C1G_ERR_HIP;
     e = conv_bf16_pack_x((const uint16_t*)x, (uint16_t*)(ws + p.off_ximg), d->N, d->C_in, d->T,
                          d->pad_left, p.T_img, p.x_nlc, s);

@@ -576,10 +576,13 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
 //     = w[ctile*TN + c][chunk*32 + 8*q + e][j]      (0 outside the tensor)
 // A thread reads the 8 * K contiguous weights of 8 input channels of one
 // output channel (every tap) once, and writes the K 16-byte pieces they form.
+// Also zeroes `zero_words` words at `zero` (the persistent kernel's arrival
+// counters and fault word), so they need no launch of their own.
 __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict__ wp,
                                       int64_t C_in, int64_t C_out, int K, int n_chunks,
-                                      int64_t total) {
+                                      int64_t total, unsigned* zero, int64_t zero_words) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < zero_words) zero[idx] = 0u;
   if (idx >= total / (8 * K)) return;
   const int pq = (int)(idx % (RW / 8));
   int64_t rest = idx / (RW / 8);
@@ -783,12 +786,14 @@ size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K) {
 }
 
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
-                          hipStream_t s) {
+                          hipStream_t s, unsigned* zero, int64_t zero_words) {
   const int n_chunks = (int)((C_in + CK - 1) / CK);
   const int64_t total = (int64_t)(conv_bf16_packed_bytes(C_in, C_out, K) / sizeof(u16));
-  const int64_t blocks = (total / (8 * K) + 255) / 256;
+  int64_t threads = total / (8 * K);
+  if (threads < zero_words) threads = zero_words;
+  const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(conv_bf16_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, wp, C_in,
-                     C_out, K, n_chunks, total);
+                     C_out, K, n_chunks, total, zero, zero_words);
   return hipGetLastError();
 }
 
@@ -864,6 +869,17 @@ int conv_bf16_fused_capacity(int stride, int K, int dilation) {
   return 0;
 }
 
+int64_t conv_bf16_fused_sync_words(int64_t N, int tiles_per_sample, int stride, int K,
+                                   int dilation, int epi, int64_t C_out, int G, int n_ttiles,
+                                   int n_ctiles) {
+  const int cap = conv_bf16_fused_capacity(stride, K, dilation);
+  if (tiles_per_sample < 1 || cap < tiles_per_sample) return 0;
+  int64_t spr = cap / tiles_per_sample;
+  if (spr > N) spr = N;
+  const int64_t rounds = (N + spr - 1) / spr;
+  return spr * rounds * fused_barrier_groups(epi, C_out, G, n_ttiles, n_ctiles) + 1;
+}
+
 hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStream_t s) {
   const int tps = a.n_ttiles * a.n_ctiles;
   const int cap = conv_bf16_fused_capacity(a.stride, a.K, a.dilation);
@@ -872,16 +888,13 @@ hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStre
   if (spr > a.N) spr = a.N;
   a.spr = (int32_t)spr;
   a.rounds = (int32_t)((a.N + spr - 1) / spr);
-  // counters (and the fault word just after them) start at zero
-  const int64_t words =
-      (int64_t)a.spr * a.rounds *
-          fused_barrier_groups(epi, a.C_out, a.G, a.n_ttiles, a.n_ctiles) + 1;
+  // the counters (and the fault word just after them), zeroed by the weight
+  // pack launched before this (conv_bf16_fused_sync_words of them)
+  const int64_t words = conv_bf16_fused_sync_words(a.N, tps, a.stride, a.K, a.dilation, epi,
+                                                   a.C_out, a.G, a.n_ttiles, a.n_ctiles);
+  if (words < 1) return hipErrorInvalidValue;
   a.fault = a.sync + (words - 1);
   a.polls = barrier_poll_limit();
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
-                     a.sync, words);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
   return tm == 512 ? launch_w<8>(a, epi, s, cooperative) : launch_w<2>(a, epi, s, cooperative);
 }

@@ -86,19 +86,26 @@ size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img);
 hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_t C_in,
                             int64_t T, int pad_left, int64_t T_img, bool nlc, hipStream_t s);
 size_t conv_bf16_packed_bytes(int64_t C_in, int64_t C_out, int K);
+// also zeroes zero_words 32-bit words at zero (nullptr / 0: none)
 hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t C_out, int K,
-                          hipStream_t s);
+                          hipStream_t s, unsigned* zero = nullptr, int64_t zero_words = 0);
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s);
 // Persistent conv + normalisation (EPI_GN_FUSED / EPI_LN_FUSED): workgroups
 // that can be resident at once on the current device for this geometry (0 if
-// unknown); the launch zeroes the counters, fills spr/rounds and launches
-// cooperatively.
+// unknown); the launch fills spr/rounds and launches (cooperatively on
+// request).
 int conv_bf16_fused_capacity(int stride, int K, int dilation);
 // Workgroups of a persistent round wait for each other in groups: GroupNorm,
 // the position tiles of a group's channel tiles; LayerNorm over channels, the
 // channel tiles of a position tile.  Groups per sample (one arrival counter
 // each per round and sample slot):
 int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctiles);
+// Words of arrival counters + fault word the persistent launch expects zeroed
+// at a.sync (0 when the geometry does not fit the device); the weight pack
+// zeroes them (conv_bf16_pack's zero / zero_words).
+int64_t conv_bf16_fused_sync_words(int64_t N, int tiles_per_sample, int stride, int K,
+                                   int dilation, int epi, int64_t C_out, int G, int n_ttiles,
+                                   int n_ctiles);
 hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStream_t s);
 
 // ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
