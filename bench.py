@@ -56,10 +56,12 @@ KERNEL_SOURCES = {
                           "conv1d_implicit_gemm_amd/csrc/common.hpp"],
 }
 # the workloads timed beside the headline, in the order of the pages' configurations
+# (a ":out_bf16" suffix: the same workload with its output rounded to bf16)
 EXTRA_CONFIGS = ["causal_conv1d_f32_n32_c256x256_t8192_k4",
                  "gemm_gn_rowmin_bf16_m1024_n8192_k8192",
                  "conv1d_gn_bf16_n64_c512x1024_t4096_k5d2",
-                 "conv1d_lnc_bf16_n64_c512x1024_t4096_k5d2"]
+                 "conv1d_lnc_bf16_n64_c512x1024_t4096_k5d2",
+                 "conv1d_gn_bf16_n64_c512x1024_t4096_k5d2:out_bf16"]
 FLUSH_BYTES = 1 << 30
 
 
@@ -147,13 +149,15 @@ class Timer:
     def flush(self):
         self.torch.sum(self.buf, dim=0, out=self.sink)
 
-    def flushed(self, op, reps):
+    def flushed(self, op, reps, all_reps=False):
         """Median and minimum (ms) over reps steps, each run right after a
         flush.  An event between the flush and the step would add the step's
         launch latency to its time (the queue processes the event marker
         first), so each rep times [flush, step] and, just before it, [flush]
         alone, both after an untimed flush (so neither flush writes back what
-        the step left dirty), and takes the difference."""
+        the step left dirty), and takes the difference.  The two flushes of a
+        rep differ by a few microseconds, so a single rep's figure carries
+        that much noise (all_reps: return the sorted per-rep figures too)."""
         torch = self.torch
         E = lambda: torch.cuda.Event(enable_timing=True)
         evs = [(E(), E(), E(), E()) for _ in range(reps)]
@@ -169,6 +173,8 @@ class Timer:
             b.record(self.stream)
         torch.cuda.synchronize()
         t = sorted(a.elapsed_time(b) - c.elapsed_time(d) for c, d, a, b in evs)
+        if all_reps:
+            return statistics.median(t), t[0], t
         return statistics.median(t), t[0]
 
     def warm(self, op, reps):
@@ -229,7 +235,11 @@ def config_of(wl, op):
 def passes(timer, steps, warmup):
     """The standalone HBM-bound passes on the dilated-conv output's shape
     ([64, 1024, 4092], G 32) and the headline output's ([16, 256, 1024], G 32):
-    algorithmic bytes = every element read once (and written once by apply)."""
+    algorithmic bytes = every element read once (and written once by apply).
+    Flushed figures: median and 10th / 90th percentiles over 5 x steps reps
+    (a pass on the headline's shape takes ~5 us, the same order as the
+    rep-to-rep noise of the flushed protocol, so one rep's figure, and the
+    minimum, mean little there)."""
     import torch
     import conv1d_implicit_gemm_amd as c1g
     res = {}
@@ -267,12 +277,14 @@ def passes(timer, steps, warmup):
         for name, fn, nbytes in cases:
             for _ in range(warmup):
                 fn()
-            med, mn = timer.flushed(fn, steps)
+            med, _, t = timer.flushed(fn, 5 * steps, all_reps=True)
             warm = timer.warm(fn, steps)
             gbps = nbytes / (med * 1e-3) / 1e9
+            p10, p90 = t[len(t) // 10], t[(9 * len(t)) // 10]
             res["%s_%s" % (name, tag)] = {
                 "shape": [N, C, L], "G": G, "algorithmic_bytes": nbytes,
-                "ms_median": round(med, 5), "ms_min": round(mn, 5), "ms_warm": round(warm, 5),
+                "ms_median": round(med, 5), "ms_p10": round(p10, 5), "ms_p90": round(p90, 5),
+                "ms_warm": round(warm, 5),
                 "gbps": round(gbps, 1), "peak_gbps": PEAKS["hbm"][1],
                 "frac": round(gbps / PEAKS["hbm"][1], 4)}
         torch.cuda.synchronize()
@@ -368,10 +380,13 @@ def main():
     if args.workload is None:
         cfgs = {}
         for cname in EXTRA_CONFIGS:
-            cwl = WORKLOADS[cname]
+            base, _, variant = cname.partition(":")
+            cwl = WORKLOADS[base]
+            if variant == "out_bf16":
+                cwl = cwl.replace(out_dtype="bf16")
             _, cop = prepared(cwl)
             cm = measure(cwl, cop, timer, steps, args.warmup)
-            cfgs[cname] = {"route": cop.route, "dtype": cwl.dtype,
+            cfgs[cname] = {"route": cop.route, "dtype": cwl.dtype, "out_dtype": cwl.out_dtype,
                            "ms_median": round(cm["ms_median"], 5),
                            "ms_min": round(cm["ms_min"], 5), "ms_warm": round(cm["ms_warm"], 5),
                            "tflops": round(cm["tflops"], 2),
