@@ -15,7 +15,7 @@ using namespace c1g;
 
 namespace {
 
-enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT, R_GEMM, R_PERSIST };
+enum Route { R_INVALID = 0, R_CONV_ONLY, R_FUSED, R_SPLIT, R_GEMM, R_PERSIST, R_EMPTY };
 
 // Workgroups of the bf16 conv that one full MI355X keeps resident at once
 // (one per compute unit); the persistent route needs a sample's tiles to fit.
@@ -43,7 +43,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t out_len(const c1g_conv_desc* d) {
   if (!d) return -1;
-  if (d->N < 1 || d->C_in < 1 || d->C_out < 1 || d->T < 1) return -1;
+  if (d->N < 0 || d->C_in < 1 || d->C_out < 1 || d->T < 1) return -1;
   if (d->K < 1 || d->stride < 1 || d->dilation < 1 || d->pad_left < 0 || d->pad_right < 0)
     return -1;
   const int64_t span =
@@ -90,6 +90,12 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
       p.status = C1G_ERR_INVALID_ARG;
       return p;
     }
+  }
+  // an empty batch: nothing to read, write or launch
+  if (d->N == 0) {
+    p.route = R_EMPTY;
+    p.total = 0;
+    return p;
   }
   // size limits of the kernels' index arithmetic and grids
   const uint64_t n_out = (uint64_t)d->N * (uint64_t)d->C_out * (uint64_t)p.T_out;
@@ -365,6 +371,7 @@ const char* route_name(int r) {
     case R_SPLIT: return "split";
     case R_GEMM: return "gemm_rows";
     case R_PERSIST: return "fused_persistent";
+    case R_EMPTY: return "empty";
     default: return "invalid";
   }
 }
@@ -406,6 +413,7 @@ int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const f
   if (!d) return C1G_ERR_INVALID_ARG;
   const Plan p = make_plan(d, nullptr);
   if (p.status != C1G_OK) return p.status;
+  if (p.route == R_EMPTY) return C1G_OK;
   if (!x || !w || !y) return C1G_ERR_INVALID_ARG;
   const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
   if (!aligned(x, es) || !aligned(w, es) || !aligned(y, os) || (bias && !aligned(bias, 4)))
@@ -420,7 +428,7 @@ int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const f
 
 namespace {
 bool gn_stats_args_ok(int64_t N, int64_t C, int64_t L, int32_t G) {
-  return N >= 1 && C >= 1 && L >= 1 && G >= 1 && C % G == 0;
+  return N >= 0 && C >= 1 && L >= 1 && G >= 1 && C % G == 0;
 }
 // grid of the first stage: one workgroup per slice of 32768 values of a group
 bool gn_stats_fits(int64_t N, int64_t C, int64_t L, int32_t G) {
@@ -439,6 +447,7 @@ int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float*
              float* rstd, void* ws, size_t ws_bytes, void* stream) {
   if (!gn_stats_args_ok(N, C, L, G) || !(eps > 0.f && std::isfinite(eps)))
     return C1G_ERR_INVALID_ARG;
+  if (N == 0) return C1G_OK;  // an empty batch
   if (!y || !mean || !rstd) return C1G_ERR_INVALID_ARG;
   if (!gn_stats_fits(N, C, L, G)) return C1G_ERR_UNSUPPORTED;
   if (!aligned(y, 4) || !aligned(mean, 4) || !aligned(rstd, 4)) return C1G_ERR_MISALIGNED;
@@ -453,7 +462,8 @@ int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float*
 int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const float* mean,
              const float* rstd, const float* gamma, const float* beta, float* out,
              void* stream) {
-  if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
+  if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
+  if (N == 0) return C1G_OK;  // an empty batch
   if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
   if ((uint64_t)N * C * L >= (1ull << 32) || C > (1ll << 31) || L > (1ll << 31))
     return C1G_ERR_UNSUPPORTED;
@@ -467,7 +477,8 @@ int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const f
 int gn_apply_bf16(int64_t N, int64_t C, int64_t L, int32_t G, const uint16_t* y,
                   const float* mean, const float* rstd, const float* gamma, const float* beta,
                   uint16_t* out, void* stream) {
-  if (N < 1 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
+  if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
+  if (N == 0) return C1G_OK;  // an empty batch
   if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
   if ((uint64_t)N * C * L >= (1ull << 32) || C > (1ll << 31) || L > (1ll << 31))
     return C1G_ERR_UNSUPPORTED;
@@ -535,6 +546,7 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
   if (!d || !nd) return C1G_ERR_INVALID_ARG;
   const Plan p = make_plan(d, nd);
   if (p.status != C1G_OK) return p.status;
+  if (p.route == R_EMPTY) return C1G_OK;
   const int pst = check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out);
   if (pst != C1G_OK) return pst;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
@@ -630,6 +642,7 @@ int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* nd, c
   if (!d || !nd) return C1G_ERR_INVALID_ARG;
   const Plan p = make_plan(d, nd);
   if (p.status != C1G_OK) return p.status;
+  if (p.route == R_EMPTY) return C1G_OK;
   const int pst = check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out);
   if (pst != C1G_OK) return pst;
   if (p.total > C1G_NOALLOC_SCRATCH_BYTES) return C1G_ERR_WORKSPACE;

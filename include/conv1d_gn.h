@@ -43,6 +43,9 @@
  *     identical from run to run (no atomics; fixed reduction orders).
  *   - Thread safety: entry points may be called concurrently from several
  *     host threads; calls on one stream execute in order.
+ *   - Empty batch: N = 0 is valid everywhere.  The call checks the other
+ *     arguments, then returns C1G_OK without reading a pointer or launching
+ *     anything (tensor pointers may be NULL); its workspace size is 0.
  */
 #ifndef CONV1D_GN_H
 #define CONV1D_GN_H
@@ -294,7 +297,8 @@ int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* norm,
  *                        C1G_BARRIER_SPINS, default 4194304 polls); a wait
  *                        that gives up makes that workgroup's output NaN.
  *   "split"              everything else: conv with a partial-statistics
- *                        epilogue, a fixed-order merge, then the apply pass */
+ *                        epilogue, a fixed-order merge, then the apply pass
+ *   "empty"              N = 0: nothing to do */
 const char* c1g_route(const c1g_conv_desc* d, const c1g_norm_desc* norm);
 
 /* Static string describing a status code. */

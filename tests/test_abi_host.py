@@ -56,7 +56,7 @@ def _desc(**kw):
                         base["dtype"], base["out_dtype"], base["x_layout"])
 
 
-@pytest.mark.parametrize("kw", [dict(N=0), dict(C_in=0), dict(C_out=0), dict(T=0), dict(K=0),
+@pytest.mark.parametrize("kw", [dict(N=-1), dict(C_in=0), dict(C_out=0), dict(T=0), dict(K=0),
                                 dict(stride=0), dict(dilation=0), dict(pad_left=-1),
                                 dict(pad_right=-1), dict(T=2, K=5, pad_left=0, pad_right=0)])
 def test_invalid_geometry(kw):
@@ -64,6 +64,42 @@ def test_invalid_geometry(kw):
     assert c1g.check(d) == 1
     assert c1g.route(d) == "invalid"
     assert c1g.out_len(d) == -1
+
+
+def test_empty_batch_is_a_no_op():
+    """N = 0: valid on every route's geometry, route "empty", no workspace,
+    and the other arguments are still checked; the standalone passes return
+    OK without touching their (NULL) pointers."""
+    lin = dict(C_in=256, C_out=512, T=1, K=1, pad_left=0, pad_right=0, dtype=c1g.C1G_BF16)
+    cases = [(_desc(N=0), c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)),
+             (_desc(N=0, C_in=512, C_out=1024, T=4096, K=5, dilation=2, pad_left=4,
+                    pad_right=4, dtype=c1g.C1G_BF16), c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)),
+             (_desc(N=0, **lin), c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 1)),
+             (_desc(N=0), None)]
+    for d, nd in cases:
+        assert c1g.out_len(d) == c1g.out_len(_desc(**{k: getattr(d, k) for k in (
+            "C_in", "C_out", "T", "K", "stride", "dilation", "pad_left", "pad_right")}))
+        assert c1g.route(d, nd) == "empty"
+        assert c1g.check(d, nd, 0) == 0
+        assert c1g.conv1d_workspace_size(d) == 0
+        if nd is not None:
+            assert c1g.conv1d_gn_workspace_size(d, nd) == 0
+    assert c1g.check(_desc(N=0), c1g.NormDesc(c1g.NORM_GROUP, 5, 1e-5, 0)) == 1  # 32 % 5
+    assert c1g.check(_desc(N=0, dtype=7)) == 2
+    lib = c1g.load_library()
+    assert lib.c1g_gn_stats_workspace_size(0, 32, 100, 8) == 0
+    assert lib.gn_stats(0, 32, 100, 8, 1e-5, None, None, None, None, 0, None) == 0
+    assert lib.gn_stats(0, 32, 100, 8, 0.0, None, None, None, None, 0, None) == 1    # eps
+    assert lib.gn_apply(0, 32, 100, 8, None, None, None, None, None, None, None) == 0
+    assert lib.gn_apply(0, 32, 100, 5, None, None, None, None, None, None, None) == 1
+    assert lib.gn_apply_bf16(0, 32, 100, 8, None, None, None, None, None, None, None) == 0
+    for fn in (lib.conv1d_forward,):
+        assert fn(ctypes.byref(_desc(N=0)), None, None, None, None, None, 0, None) == 0
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    assert lib.conv1d_gn_forward(ctypes.byref(_desc(N=0)), ctypes.byref(gn), None, None, None,
+                                 None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.conv1d_gn_forward_noalloc(ctypes.byref(_desc(N=0)), ctypes.byref(gn), None, None,
+                                         None, None, None, None, None, None, None, None) == 0
 
 
 def test_invalid_norm_args():

@@ -239,3 +239,49 @@ def test_groupnorm_invariant_on_device(wl):
     assert float(np.abs(zg.mean(axis=2)).max()) <= 1e-5
     want = 1.0 - wl.eps * r * r
     assert float(np.abs(zg.var(axis=2) / want - 1).max()) <= 1e-4
+
+
+# N = 0: every entry point returns an empty result without launching anything
+EMPTY_CASES = [
+    dict(name="fused_fp32", C_in=16, C_out=32, T=256, K=3, pad=1, dil=1, dtype=torch.float32,
+         norm="group", G=8, rowmin=False),
+    dict(name="persistent_bf16", C_in=64, C_out=128, T=512, K=5, pad=4, dil=2,
+         dtype=torch.bfloat16, norm="layer_channels", G=0, rowmin=False),
+    dict(name="gemm_bf16", C_in=256, C_out=512, T=1, K=1, pad=0, dil=1, dtype=torch.bfloat16,
+         norm="group", G=32, rowmin=True),
+]
+
+
+@pytest.mark.parametrize("case", EMPTY_CASES, ids=lambda c: c["name"])
+def test_empty_batch(case):
+    announce("empty batch", case["name"])
+    C_in, C_out, T, K = case["C_in"], case["C_out"], case["T"], case["K"]
+    dt = case["dtype"]
+    x = torch.empty((0, C_in, T), device=DEV, dtype=dt)
+    w = torch.randn((C_out, C_in, K), device=DEV).to(dt)
+    b = torch.randn((C_out,), device=DEV)
+    b2 = torch.randn((C_out,), device=DEV) if case["rowmin"] else None
+    kw = dict(pad_left=case["pad"], pad_right=case["pad"], dilation=case["dil"])
+    T_out = T + 2 * case["pad"] - case["dil"] * (K - 1)
+    out, mean, rstd = c1g.conv1d_gn_forward(x, w, b, norm=case["norm"], groups=case["G"],
+                                            rowmin_bias=b2, return_stats=True, **kw)
+    assert out.shape == (0, C_out, T_out)
+    assert mean.shape[0] == 0 and rstd.shape[0] == 0
+    y = c1g.conv1d_forward(x, w, b, **kw)
+    assert y.shape == (0, C_out, T_out)
+    if case["norm"] == "group" and not case["rowmin"]:
+        o2 = torch.empty((0, C_out, T_out), device=DEV)
+        c1g.conv1d_gn_forward_noalloc(x, w, b, out=o2, norm="group", groups=case["G"], **kw)
+    torch.cuda.synchronize()
+
+
+def test_empty_batch_passes():
+    announce("empty batch: gn_stats / gn_apply")
+    y = torch.empty((0, 64, 100), device=DEV)
+    mean, rstd = c1g.gn_stats(y, 8)
+    assert mean.shape == (0, 8) and rstd.shape == (0, 8)
+    out = c1g.gn_apply(y, mean, rstd, groups=8)
+    assert out.shape == (0, 64, 100)
+    yb = y.to(torch.bfloat16)
+    assert c1g.gn_apply(yb, mean, rstd, groups=8).shape == (0, 64, 100)
+    torch.cuda.synchronize()
