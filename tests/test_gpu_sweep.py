@@ -5,11 +5,12 @@ per-element bound for bf16 outputs)."""
 import pytest
 
 from tests.gpu_util import check_parity
-from tests.sweep_cases import sweep_cases
+from tests.sweep_cases import SWEEP_SEEDS, sweep_cases
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("wl", sweep_cases(), ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [w for sd in SWEEP_SEEDS for w in sweep_cases(sd)],
+                         ids=lambda w: w.name)
 def test_sweep_parity(wl):
     check_parity(wl, seed=7)
