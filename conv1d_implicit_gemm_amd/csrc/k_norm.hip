@@ -293,8 +293,10 @@ __global__ __launch_bounds__(NT) void apply_kernel(const TI* __restrict__ y,
     auto load = [&](uint32_t v) __attribute__((always_inline)) {
       return __builtin_nontemporal_load((const u32x4*)(y + (size_t)v * EPV));
     };
-    // elements past the last whole vector (bf16 y with total % 8 == 4)
-    for (uint32_t e = nv * EPV + blockIdx.x * NT + threadIdx.x; e < total; e += step) scalar(e);
+    // elements past the last whole vector (bf16 y with total % 8 == 4); a
+    // 64-bit counter, so the stride cannot wrap past 2^32 near the size limit
+    for (uint64_t e = (uint64_t)nv * EPV + blockIdx.x * NT + threadIdx.x; e < total; e += step)
+      scalar((uint32_t)e);
     if (MODE == 2) {
       // three loads per unit (y, mean, rstd): a grid-strided loop with four
       // vectors in flight per thread measured faster here
@@ -330,7 +332,8 @@ __global__ __launch_bounds__(NT) void apply_kernel(const TI* __restrict__ y,
       }
     }
   } else {
-    for (uint32_t e = blockIdx.x * NT + threadIdx.x; e < total; e += step) scalar(e);
+    for (uint64_t e = (uint64_t)blockIdx.x * NT + threadIdx.x; e < total; e += step)
+      scalar((uint32_t)e);
   }
 }
 
