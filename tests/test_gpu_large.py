@@ -23,6 +23,12 @@ LARGE = [
     # bf16, persistent route, 256 tiles per sample
     (Workload("large_persistent_bf16_gn", N=130, C_in=64, C_out=1024, T=16384, K=3,
               pad_left=1, pad_right=1, G=32, dtype="bf16"), "fused_persistent", TOL_BF16),
+    # fp32, single-pass route, 134400 workgroups
+    (Workload("large_fused_fp32_gn", N=2100, C_in=16, C_out=1024, T=1024, K=3, pad_left=1,
+              pad_right=1, G=64), "fused_single_pass", TOL_F32),
+    # bf16 Linear + GroupNorm + row-min + bias (whole rows are checked)
+    (Workload("large_gemm_rowmin", N=65535, C_in=64, C_out=40960, T=1, K=1, G=2560,
+              rowmin_bias=True, dtype="bf16"), "gemm_rows", TOL_BF16),
 ]
 
 
@@ -34,9 +40,10 @@ def test_outputs_past_2_31(wl, route, tol):
     announce("past 2^31 outputs", wl.name)
     inp = make_inputs(wl, 3)
     x, w = to_dev(inp["x"]), to_dev(inp["w"])
-    b, ga, be = (to_dev(inp[k]) for k in ("bias", "gamma", "beta"))
+    b, ga, be, b2 = (to_dev(inp[k]) for k in ("bias", "gamma", "beta", "bias2"))
     op = c1g.PreparedConv1dGN(x, w, b, pad_left=wl.pad_left, pad_right=wl.pad_right,
-                              norm="group", groups=wl.G, eps=wl.eps, gamma=ga, beta=be)
+                              norm="group", groups=wl.G, eps=wl.eps, gamma=ga, beta=be,
+                              rowmin_bias=b2)
     assert op.route == route
     op.out.fill_(float("nan"))
     out = op()
@@ -44,11 +51,13 @@ def test_outputs_past_2_31(wl, route, tol):
     cpg = wl.C_out // wl.G
     f = to_f64_numpy
     for n, g in ((0, 0), (wl.N - 1, wl.G - 1)):
-        c0, c1 = g * cpg, (g + 1) * cpg
+        # a whole group of sample n, or a whole row for the row-min
+        c0, c1 = (0, wl.C_out) if wl.rowmin_bias else (g * cpg, (g + 1) * cpg)
         ref = oracle.forward(f(inp["x"][n:n + 1]), f(inp["w"][c0:c1]), f(inp["bias"][c0:c1]),
-                             pad_left=wl.pad_left, pad_right=wl.pad_right, norm="group", G=1,
-                             eps=wl.eps, gamma=f(inp["gamma"][c0:c1]),
-                             beta=f(inp["beta"][c0:c1]))
+                             pad_left=wl.pad_left, pad_right=wl.pad_right, norm="group",
+                             G=(c1 - c0) // cpg, eps=wl.eps, gamma=f(inp["gamma"][c0:c1]),
+                             beta=f(inp["beta"][c0:c1]),
+                             bias2=f(inp["bias2"][c0:c1]) if wl.rowmin_bias else None)
         err = max_abs_err(out[n:n + 1, c0:c1], ref["out"])
         assert err <= tol, (n, g, err)
     del op, out
