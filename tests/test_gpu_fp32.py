@@ -285,3 +285,49 @@ def test_empty_batch_passes():
     yb = y.to(torch.bfloat16)
     assert c1g.gn_apply(yb, mean, rstd, groups=8).shape == (0, 64, 100)
     torch.cuda.synchronize()
+
+
+# x one element past a 16-byte boundary: the kernels' unaligned staging paths
+# (register-staged fused kernel, element-wise window loads, scalar input pack)
+UNALIGNED_CASES = [
+    Workload("unaligned_fused_fp32", N=2, C_in=32, C_out=64, T=300, K=3, pad_left=1,
+             pad_right=1, G=8),
+    Workload("unaligned_split_fp32", N=2, C_in=24, C_out=40, T=1500, K=5, dilation=2,
+             pad_left=4, G=5),
+    Workload("unaligned_bf16_persistent", N=2, C_in=40, C_out=128, T=600, K=5, dilation=2,
+             pad_left=2, pad_right=2, G=8, dtype="bf16"),
+    Workload("unaligned_bf16_split_ln", N=2, C_in=40, C_out=96, T=333, K=3, pad_left=1,
+             pad_right=1, norm="layer_channels", dtype="bf16", persistent=False),
+]
+
+
+@pytest.mark.parametrize("wl", UNALIGNED_CASES, ids=lambda w: w.name)
+def test_unaligned_x_matches_aligned(wl):
+    """The same values handed over at an address one element past a 16-byte
+    boundary give the same bits as from an aligned address."""
+    announce("unaligned x", wl.name)
+    inp = make_inputs(wl, 9)
+    x = to_dev(inp["x"])
+    flat = torch.empty(x.numel() + 1, device=DEV, dtype=x.dtype)
+    xo = flat[1:].view(x.shape)
+    xo.copy_(x)
+    assert xo.data_ptr() % 16 != 0
+    w = to_dev(inp["w"])
+    kw = dict(stride=wl.stride, dilation=wl.dilation, pad_left=wl.pad_left,
+              pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
+              gamma=to_dev(inp["gamma"]), beta=to_dev(inp["beta"]), persistent=wl.persistent)
+    a = c1g.conv1d_gn_forward(x, w, to_dev(inp["bias"]), **kw)
+    b = c1g.conv1d_gn_forward(xo, w, to_dev(inp["bias"]), **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all() and torch.equal(a, b)
+
+
+def test_unaligned_x_on_the_gemm_route_is_rejected():
+    """The Linear route copies 16-byte pieces of x and w: an unaligned x is a
+    status (misaligned), reported before any launch."""
+    announce("unaligned x, gemm route")
+    x = torch.randn(33 * 64 + 1, device=DEV).to(torch.bfloat16)[1:].view(33, 64, 1)
+    w = torch.randn(128, 64, 1, device=DEV).to(torch.bfloat16)
+    with pytest.raises(c1g.C1GError) as e:
+        c1g.conv1d_gn_forward(x, w, None, norm="group", groups=8)
+    assert e.value.status == 4
