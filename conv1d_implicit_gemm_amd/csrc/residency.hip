@@ -17,6 +17,7 @@
 // co-residency gives up and poisons its output with NaN instead of hanging.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 
 #include "launch.hpp"
@@ -45,6 +46,24 @@ int query_capacity(int dev, const void* kernel, int threads) {
   return cus * per_cu;
 }
 
+// The environment variable C1G_RESIDENT_LIMIT (a positive integer, read at
+// each call) caps the capacity reported below, so that the paths of a device
+// that keeps fewer workgroups resident (fewer samples per round of the
+// persistent conv, the split route in its place, two launches instead of the
+// one-launch row-min) can be exercised on any device.  0: no cap.
+int resident_limit() {
+  const char* e = std::getenv("C1G_RESIDENT_LIMIT");
+  if (e == nullptr || *e == '\0') return 0;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  return (end != nullptr && *end == '\0' && v > 0 && v < (1l << 30)) ? (int)v : 0;
+}
+
+int capped(int v) {
+  const int lim = resident_limit();
+  return (lim > 0 && lim < v) ? lim : v;
+}
+
 }  // namespace
 
 int resident_capacity(const void* kernel, int threads) {
@@ -54,12 +73,12 @@ int resident_capacity(const void* kernel, int threads) {
   for (int i = 0; i < cap_used; ++i)
     if (cap_table[i].dev == dev && cap_table[i].kernel == kernel &&
         cap_table[i].threads == threads)
-      return cap_table[i].value;
+      return capped(cap_table[i].value);
   const int v = query_capacity(dev, kernel, threads);
   // a failed query is not cached (the next call asks again); a full table
   // just means asking the runtime every time
   if (v > 0 && cap_used < kMaxEntries) cap_table[cap_used++] = CapEntry{dev, kernel, threads, v};
-  return v;
+  return capped(v);
 }
 
 hipError_t launch_coresident(const void* kernel, unsigned grid, int threads, void** args,

@@ -292,7 +292,11 @@ int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* norm,
  *                        fixed order, normalises its tile in registers and
  *                        writes out once (y never reaches memory).  On a
  *                        device that cannot keep a sample's tiles resident
- *                        together, the call runs the split route instead.
+ *                        together, the call runs the split route instead
+ *                        (the environment variable C1G_RESIDENT_LIMIT, a
+ *                        positive integer, caps the resident workgroups the
+ *                        library assumes, so these paths, and rounds of fewer
+ *                        samples, can be exercised on any device).
  *                        The waits are bounded (environment variable
  *                        C1G_BARRIER_SPINS, default 4194304 polls); a wait
  *                        that gives up makes that workgroup's output NaN.

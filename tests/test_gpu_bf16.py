@@ -300,3 +300,50 @@ def test_barrier_give_up_poisons_output(which, monkeypatch):
     nan = torch.isnan(forced)
     assert nan.any(), "no workgroup gave up (the wait should fail at the first poll)"
     assert torch.equal(forced[~nan], ref[~nan])
+
+
+# C1G_RESIDENT_LIMIT caps the resident workgroups the library assumes: the
+# paths of a device that keeps fewer workgroups resident, on this one.
+# PERSIST_CASES[0] and [1] have 5 x 4 = 20 tiles per sample (512 positions x
+# 128 channels), so a cap of 20 gives one sample per round (14 rounds), 45
+# two per round, and 19 too few for a sample: the split route runs instead.
+RESIDENT_CASES = [(0, "20"), (0, "45"), (0, "19"), (1, "20"), (1, "19")]
+
+
+@pytest.mark.parametrize("case,limit", RESIDENT_CASES,
+                         ids=["%s_cap%s" % (PERSIST_CASES[c].name, l) for c, l in RESIDENT_CASES])
+def test_resident_limit(case, limit, monkeypatch):
+    """Fewer samples per round give the bits of the default rounds (each
+    tile's arithmetic and each sample's merge order do not depend on the
+    round), and a cap below one sample's tiles gives the bits of the split
+    route (the same tiles and merge, the same workspace offsets); both stay
+    within tolerance of the oracle on the first and last samples.  The
+    planner still reports the persistent route: the choice is made per call."""
+    from tests.gpu_util import library_route
+    wl = PERSIST_CASES[case]
+    announce("resident limit", limit, wl.name)
+    inp = make_inputs(wl, 9)
+    full = run_library(wl, inp)
+    split = run_library(wl.replace(persistent=False), inp)
+    monkeypatch.setenv("C1G_RESIDENT_LIMIT", limit)
+    assert library_route(wl) == "fused_persistent"
+    capped = run_library(wl, inp)
+    monkeypatch.delenv("C1G_RESIDENT_LIMIT")
+    assert torch.isfinite(capped).all()
+    assert torch.equal(capped, split if int(limit) < 20 else full)
+    for n in (0, wl.N - 1):
+        ref = run_oracle(wl, inp, n_slice=slice(n, n + 1))
+        assert max_abs_err(capped[n:n + 1], ref["out"]) <= TOL_BF16, n
+
+
+def test_resident_limit_gemm_one_launch(monkeypatch):
+    """The one-launch GEMM + row-min with a cap below its grid runs as the GEMM
+    and a broadcast kernel: the same bits."""
+    wl = next(w for w in GEMM_CASES if w.name == "gemm_gn_rowmin_one_launch_ragged")
+    announce("resident limit", wl.name)
+    inp = make_inputs(wl, 9)
+    ref = run_library(wl, inp)
+    monkeypatch.setenv("C1G_RESIDENT_LIMIT", "1")
+    capped = run_library(wl, inp)
+    monkeypatch.delenv("C1G_RESIDENT_LIMIT")
+    assert torch.isfinite(ref).all() and torch.equal(capped, ref)
