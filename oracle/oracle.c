@@ -166,7 +166,9 @@ void oracle_layer_norm_channels(int64_t N, int64_t C, int64_t L, double eps,
 
 /* Per-row min over channels plus a broadcast per-channel bias
  * ("Kimi-K2.6 l2_p75"): m[n,l] = min_c z[n,c,l]; out[n,c,l] = m[n,l] + bias2[c].
- * rowmin_out ([N,L]) may be NULL. */
+ * The page's model reduces with PyTorch's min over the channel dimension, which
+ * returns NaN for a row holding a NaN; so does this one, whichever channel
+ * holds it.  rowmin_out ([N,L]) may be NULL. */
 void oracle_rowmin_bias(int64_t N, int64_t C, int64_t L, const double* z,
                         const double* bias2, double* out, double* rowmin_out) {
 #pragma omp parallel for collapse(2) schedule(static)
@@ -175,7 +177,7 @@ void oracle_rowmin_bias(int64_t N, int64_t C, int64_t L, const double* z,
       double m = z[(n * C) * L + l];
       for (int64_t c = 1; c < C; ++c) {
         double v = z[(n * C + c) * L + l];
-        if (v < m) m = v;
+        if (v < m || v != v) m = v;
       }
       if (rowmin_out) rowmin_out[n * L + l] = m;
       for (int64_t c = 0; c < C; ++c) out[(n * C + c) * L + l] = m + bias2[c];

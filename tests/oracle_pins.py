@@ -290,6 +290,28 @@ def check_rowmin_bias(orc):
         assert np.allclose(d, np.broadcast_to(d[:, :1, :], d.shape), rtol=0, atol=1e-15 * 8)
 
 
+def check_rowmin_nan(orc):
+    """A row holding a NaN (in the first, a middle or the last channel, or in
+    every channel) has a NaN minimum, as PyTorch's min over a dimension gives
+    (the reduction of the page's model); rows without one are unaffected."""
+    torch, _ = _torch()
+    rng = _rng(14)
+    N, C, L = 2, 9, 6
+    z = rng.standard_normal((N, C, L))
+    z[0, 0, 1] = np.nan
+    z[0, 4, 2] = np.nan
+    z[1, C - 1, 3] = np.nan
+    z[1, :, 5] = np.nan
+    b2 = rng.standard_normal(C)
+    out, m = orc.rowmin_bias(z, b2)
+    want = torch.min(torch.from_numpy(z), dim=1)[0].numpy()
+    assert np.array_equal(np.isnan(m), np.isnan(want))
+    assert np.isnan(want).sum() == 4
+    ok = ~np.isnan(want)
+    assert np.array_equal(m[ok], want[ok])
+    assert np.array_equal(np.isnan(out), np.broadcast_to(np.isnan(want)[:, None, :], out.shape))
+
+
 def check_forward_composition(orc):
     """forward() = conv -> GN -> row-min + bias2 on a small k=1, T=1 case
     against numpy/torch float64 built independently."""

@@ -36,7 +36,8 @@ MUTANTS = [
     ("ln_wrong_count", "double mean = s / (double)C;", "double mean = s / (double)(C + 1);", 0),
     ("ln_eps_dropped", "1.0 / sqrt(ss / (double)C + eps)", "1.0 / sqrt(ss / (double)C)", 0),
     ("ln_affine_swapped", "* rstd * ga + be;", "* rstd * be + ga;", 1),
-    ("rowmin_is_max", "if (v < m) m = v;", "if (v > m) m = v;", 0),
+    ("rowmin_is_max", "if (v < m || v != v) m = v;", "if (v > m || v != v) m = v;", 0),
+    ("rowmin_drops_nan", "if (v < m || v != v) m = v;", "if (v < m) m = v;", 0),
     ("rowmin_bias_index", "out[(n * C + c) * L + l] = m + bias2[c];",
      "out[(n * C + c) * L + l] = m + bias2[0];", 0),
 ]
