@@ -98,12 +98,20 @@ __device__ __forceinline__ f32x4 lane_sum4(f32x4 v) {
   return v;
 }
 
-// Minimum over lanes differing in bits 16 and 32 of the lane index.
+// The smaller of a and b, or NaN if either is NaN: the row-min reduces like
+// PyTorch's min over a dimension, which returns NaN for a row holding one
+// (fminf would drop it).  One v_minimum3_f32 on gfx950.
+__device__ __forceinline__ float min_nan(float a, float b) {
+  return __builtin_elementwise_minimum(a, b);
+}
+
+// Minimum over lanes differing in bits 16 and 32 of the lane index (NaN if
+// any of them holds one).
 __device__ __forceinline__ float lane_min48(float v) {
   f32x2 p = pair16(v);
-  v = fminf(p[0], p[1]);
+  v = min_nan(p[0], p[1]);
   p = pair32(v);
-  return fminf(p[0], p[1]);
+  return min_nan(p[0], p[1]);
 }
 
 // Running statistics of a set of values: count, mean and the sum of squared

@@ -399,8 +399,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
         const float rstd = __builtin_amdgcn_rsqf(q * (1.0f / 16.0f) + a.eps);
         float m = __builtin_inff();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) m = fminf(m, (v[r] - mean) * (rstd * ga[r]) + be[r]);
-        if (gvalid) rmin[j] = fminf(rmin[j], m);
+        for (int r = 0; r < 4; ++r) m = min_nan(m, (v[r] - mean) * (rstd * ga[r]) + be[r]);
+        if (gvalid) rmin[j] = min_nan(rmin[j], m);
         const int64_t nn = n0 + wnn * WNT * 16 + 16 * j + lr;
         if (gvalid && kq == 0 && nn < a.N) {
           const int64_t g = cg / 16;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
       const int64_t nn = n0 + tid;
       float m = red[tid];
 #pragma unroll
-      for (int w = 1; w < KSPLIT * WGC; ++w) m = fminf(m, red[w * BN + tid]);
+      for (int w = 1; w < KSPLIT * WGC; ++w) m = min_nan(m, red[w * BN + tid]);
       if (nn < a.N) {
         float* p = a.part + nn * a.n_ctiles + ctile;
         if (EPI == GEMM_GN_ROWMIN_ONE)  // read by the other c-tiles' workgroups
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(GemmArgs a) {
         float m = __builtin_inff();
         if (nn < a.N)
           for (int t = 0; t < a.n_ctiles; ++t)
-            m = fminf(m, __uint_as_float(__hip_atomic_load(
+            m = min_nan(m, __uint_as_float(__hip_atomic_load(
                              (const unsigned*)(a.part + nn * a.n_ctiles + t), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT)));
         rowm[tid] = ok ? m : __builtin_nanf("");
@@ -501,9 +501,9 @@ __global__ __launch_bounds__(NTHR) void rowmin_bcast_kernel(const float* __restr
   const int64_t n = blockIdx.x;
   const int lane = threadIdx.x & 63;
   float m = __builtin_inff();
-  for (int t = lane; t < n_ctiles; t += 64) m = fminf(m, part[n * n_ctiles + t]);
+  for (int t = lane; t < n_ctiles; t += 64) m = min_nan(m, part[n * n_ctiles + t]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fminf(m, __shfl_xor(m, off));
+  for (int off = 32; off >= 1; off >>= 1) m = min_nan(m, __shfl_xor(m, off));
   TO* row = out + n * C;
   if ((C % 4) == 0 && (((uintptr_t)out) & (4 * sizeof(TO) - 1)) == 0 &&
       (((uintptr_t)bias2) & 15) == 0) {

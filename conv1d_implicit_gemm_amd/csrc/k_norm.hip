@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NT) void rowmin_kernel(const TI* __restrict__ y,
   for (int64_t c = 0; c < C; ++c) {
     const float z = normed<KIND>(load_elem(y + (n * C + c) * L + l), mean, rstd, gamma, beta, n,
                                  c, l, L, G, cpg);
-    m = z < m ? z : m;
+    m = min_nan(m, z);
   }
   for (int64_t c = 0; c < C; ++c) store_elem(out + (n * C + c) * L + l, m + bias2[c]);
 }
@@ -400,12 +400,12 @@ __global__ __launch_bounds__(NT) void rowmin_l1_kernel(const TI* __restrict__ y,
   for (int64_t c = threadIdx.x; c < C; c += NT) {
     const float z = normed<KIND>(load_elem(y + n * C + c), mean, rstd, gamma, beta, n, c, 0, 1,
                                  G, cpg);
-    m = z < m ? z : m;
+    m = min_nan(m, z);
   }
   sh[threadIdx.x] = m;
   __syncthreads();
   for (int s = NT / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) sh[threadIdx.x] = fminf(sh[threadIdx.x], sh[threadIdx.x + s]);
+    if ((int)threadIdx.x < s) sh[threadIdx.x] = min_nan(sh[threadIdx.x], sh[threadIdx.x + s]);
     __syncthreads();
   }
   m = sh[0];
