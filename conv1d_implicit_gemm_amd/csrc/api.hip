@@ -318,8 +318,8 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
   g.n_ntiles = p.n_ttiles;
   g.eps = nd ? nd->eps : 0.f;
   if (p.gemm_fused) {
-    // one cooperative launch on request when every tile can be resident at
-    // once, else the GEMM and a broadcast kernel
+    // one launch (cooperative with C1G_FLAG_COOPERATIVE) on request when every
+    // tile can be resident at once, else the GEMM and a broadcast kernel
     if ((nd->flags & C1G_FLAG_ROWMIN_ONE_LAUNCH) && !(nd->flags & C1G_FLAG_NO_PERSISTENT) &&
         (int64_t)p.n_ctiles * p.n_ttiles <= gemm_bf16_rowmin_capacity()) {
       g.bias2 = bias2;

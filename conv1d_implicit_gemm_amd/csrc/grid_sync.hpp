@@ -1,4 +1,4 @@
-// Waits between the workgroups of one cooperative launch.
+// Waits between the workgroups of one launch whose grid is resident at once.
 //
 // A group of workgroups (the tiles of one sample, or of one row block) meets
 // on a 32-bit arrival counter in the caller's workspace, zeroed before the
@@ -33,8 +33,8 @@ inline unsigned barrier_poll_limit() {
 // workgroups have arrived on *ctr (this one included).  Waits for this wave's outstanding memory
 // operations first, so every store the workgroup issued before the call is
 // visible to the others once they see its arrival.  The wait gives up after
-// a bound no legitimate wait approaches (in a cooperative launch every
-// workgroup is resident), records that in *fault and returns false, so no
+// a bound no legitimate wait approaches (every workgroup of such a launch is
+// resident), records that in *fault and returns false, so no
 // path can hang; the caller then poisons what depended on the others.
 // The two halves of the wait, for callers with work to issue in between
 // (barrier_arrive, then barrier_wait); sample_barrier is both.

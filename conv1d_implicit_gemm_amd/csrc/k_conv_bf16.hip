@@ -1,7 +1,7 @@
 // bf16 implicit-GEMM 1-D convolution for gfx950, fp32 accumulate: the
 // convolution of the split route (y plus partial statistics) and, as a
-// persistent cooperative kernel, the whole conv + GroupNorm / channel
-// LayerNorm of the fused_persistent route.
+// persistent kernel whose workgroups wait on each other, the whole conv +
+// GroupNorm / channel LayerNorm of the fused_persistent route.
 //
 // GEMM view ("Kimi-K2.6 l1_p5", the implicit-GEMM shape M = N*T_out,
 // N = C_out, K = C_in*K): row m = (n, t), column = output channel c; the

@@ -39,8 +39,8 @@
 // one partial per (n, c-tile) (fixed slots, no atomics); optional mean/rstd
 // outputs.  rowmin_bcast then folds the partials in a fixed order and writes
 // out[n][c] = min + bias2[c].  GEMM_GN_ROWMIN_ONE does that last step inside
-// the same launch: the grid is launched cooperatively (every tile resident),
-// each workgroup publishes its partials, waits until the other c-tiles of its
+// the same launch, whose grid fits what the device keeps resident at once
+// (an ordinary launch, or a cooperative one on request): each workgroup publishes its partials, waits until the other c-tiles of its
 // rows have published theirs, folds them (min is exact, so any order gives the
 // same bits) and writes its own 256 x 128 block of the broadcast output.
 #include "common.hpp"

@@ -110,7 +110,7 @@ hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStre
 
 // ---- bf16 GEMM for K = 1, T = 1 (k_gemm_bf16.hip)
 // GEMM_GN_ROWMIN writes per-tile row minima for rowmin_bcast;
-// GEMM_GN_ROWMIN_ONE (cooperative launch, every tile resident) also waits for
+// GEMM_GN_ROWMIN_ONE (every tile resident at once) also waits for
 // the other c-tiles of its rows and writes its block of the broadcast output
 enum GemmEpi : int { GEMM_STORE = 0, GEMM_GN_ROWMIN = 1, GEMM_GN_ROWMIN_ONE = 2 };
 struct GemmArgs {
@@ -140,7 +140,8 @@ hipError_t gemm_bf16_launch(const GemmArgs& a, int epi, hipStream_t s);
 // ceil(C / 64) <= 65535
 hipError_t transpose_nlc_f32(const float* x, float* xt, int64_t N, int64_t T, int64_t C,
                              hipStream_t s);
-// GEMM + GroupNorm + row-min + bias2 in one cooperative launch: workgroups the
+// GEMM + GroupNorm + row-min + bias2 in one launch whose workgroups wait on
+// each other: workgroups the
 // device keeps resident at once with the GN_ROWMIN_ONE kernel (0 on error);
 // the launch needs n_ctiles * n_ntiles of them and n_ntiles + 1 zeroed
 // words at a.sync (zeroed here); cooperative: see launch_coresident
