@@ -575,12 +575,16 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
 //   wp[(((ctile*n_chunks + chunk)*K + j)*TN + c)*RW + 8*(q ^ swz(c)) + e]
 //     = w[ctile*TN + c][chunk*32 + 8*q + e][j]      (0 outside the tensor)
 // A thread reads the 8 * K contiguous weights of 8 input channels of one
-// output channel (every tap) once, and writes the K 16-byte pieces they form.
+// output channel (every tap) once, as K 16-byte loads when C_in % 8 == 0 and
+// w is 16-byte aligned (vec; element by element otherwise, and at the edges),
+// and writes the K 16-byte pieces they form.
 // Also zeroes `zero_words` words at `zero` (the persistent kernel's arrival
 // counters and fault word), so they need no launch of their own.
+template <int K>
 __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict__ wp,
-                                      int64_t C_in, int64_t C_out, int K, int n_chunks,
-                                      int64_t total, unsigned* zero, int64_t zero_words) {
+                                      int64_t C_in, int64_t C_out, int n_chunks,
+                                      int64_t total, unsigned* zero, int64_t zero_words,
+                                      int vec) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx < zero_words) zero[idx] = 0u;
   if (idx >= total / (8 * K)) return;
@@ -593,24 +597,35 @@ __global__ void conv_bf16_pack_kernel(const u16* __restrict__ w, u16* __restrict
   const int q = pq ^ swz(c);
   const int64_t co = ctile * TN + c;
   const int64_t ci0 = (int64_t)chunk * CK + 8 * q;
-  u16 v[8 * KMAX];
+  // v[e * K + j]: input channel ci0 + e, tap j (w's own order within the run)
+  u16 v[8 * K];
+  if (vec && co < C_out && ci0 + 8 <= C_in) {
+    const u32x4* src = (const u32x4*)(w + (co * C_in + ci0) * K);
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+    for (int i = 0; i < K; ++i) {
+      const u32x4 r = src[i];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < K)
-        v[e * KMAX + j] =
+      for (int k = 0; k < 4; ++k) {
+        v[8 * i + 2 * k] = (u16)(r[k] & 0xffffu);
+        v[8 * i + 2 * k + 1] = (u16)(r[k] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        v[e * K + j] =
             (co < C_out && ci0 + e < C_in) ? w[(co * C_in + ci0 + e) * K + j] : (u16)0;
+  }
   u16* dst = wp + ((((ctile * n_chunks + chunk) * K) * TN + c) * RW + 8 * pq);
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < K) {
-      u32x4 o;
+  for (int j = 0; j < K; ++j) {
+    u32x4 o;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o[k] = (uint32_t)v[2 * k * KMAX + j] | ((uint32_t)v[(2 * k + 1) * KMAX + j] << 16);
-      *(u32x4*)(dst + (int64_t)j * TN * RW) = o;
-    }
+    for (int k = 0; k < 4; ++k)
+      o[k] = (uint32_t)v[2 * k * K + j] | ((uint32_t)v[(2 * k + 1) * K + j] << 16);
+    *(u32x4*)(dst + (int64_t)j * TN * RW) = o;
   }
 }
 
@@ -792,8 +807,18 @@ hipError_t conv_bf16_pack(const uint16_t* w, uint16_t* wp, int64_t C_in, int64_t
   int64_t threads = total / (8 * K);
   if (threads < zero_words) threads = zero_words;
   const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(conv_bf16_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, wp, C_in,
-                     C_out, K, n_chunks, total, zero, zero_words);
+  const int vec = (C_in % 8 == 0) && ((((uintptr_t)w) & 15) == 0);
+#define C1G_PACK_K(KK)                                                                        \
+  case KK:                                                                                    \
+    hipLaunchKernelGGL(conv_bf16_pack_kernel<KK>, dim3((unsigned)blocks), dim3(256), 0, s, w, \
+                       wp, C_in, C_out, n_chunks, total, zero, zero_words, vec);              \
+    break;
+  switch (K) {
+    C1G_PACK_K(1) C1G_PACK_K(2) C1G_PACK_K(3) C1G_PACK_K(4)
+    C1G_PACK_K(5) C1G_PACK_K(6) C1G_PACK_K(7) C1G_PACK_K(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef C1G_PACK_K
   return hipGetLastError();
 }
 
