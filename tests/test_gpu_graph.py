@@ -5,7 +5,8 @@ PreparedConv1dGN call (and one allocation-free call) on a side stream, then
 replays the graph several times with the program's own eager work and
 synchronisations in between, the output poisoned with NaN before every
 replay; every replay must equal the eager result bit for bit.  Also: calls
-from several host threads at once, each on its own stream."""
+from several host threads at once, each on its own stream (the routes whose
+workgroups wait on each other with cooperative launches)."""
 import pytest
 import torch
 
@@ -125,6 +126,50 @@ def test_concurrent_host_threads():
         ref = c1g.conv1d_gn_forward(x, w, b, **kw)
         jobs.append((x, w, b, kw, ref))
     torch.cuda.synchronize()
+    results = [None] * len(jobs)
+    errors = []
+
+    def run(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [c1g.conv1d_gn_forward(x, w, b, **kw) for x, w, b, kw, _ in [jobs[k]] * 3]
+            s.synchronize()
+            results[k] = outs
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for (_, _, _, _, ref), outs in zip(jobs, results):
+        for o in outs:
+            assert torch.equal(o, ref)
+
+
+def test_concurrent_cooperative_launches():
+    """The routes whose workgroups wait on each other, called concurrently
+    from several host threads with cooperative=True (what callers that share
+    the device with other work are told to set): the runtime keeps each
+    launch's workgroups co-resident, so every call gives the bits of the same
+    call made alone (a wait that gave up would have written NaN)."""
+    import threading
+    cases = [c for c, r in CASES if r == "fused_persistent" or c.one_launch]
+    announce("concurrent cooperative launches", len(cases), "cases")
+    jobs = []
+    for i, wl in enumerate(cases * 2):
+        inp = make_inputs(wl, 40 + i)
+        x, w, b, ga, be, b2 = _tensors(wl, inp)
+        kw = dict(stride=wl.stride, dilation=wl.dilation, pad_left=wl.pad_left,
+                  pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps, gamma=ga,
+                  beta=be, rowmin_bias=b2, one_launch=wl.one_launch, cooperative=True)
+        ref = c1g.conv1d_gn_forward(x, w, b, **kw)
+        jobs.append((x, w, b, kw, ref))
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(j[4]).all() for j in jobs)
     results = [None] * len(jobs)
     errors = []
 
