@@ -43,7 +43,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t out_len(const c1g_conv_desc* d) {
   if (!d) return -1;
-  if (d->N < 0 || d->C_in < 1 || d->C_out < 1 || d->T < 1) return -1;
+  // (a T past 2^62 is no length: the span below must not overflow)
+  if (d->N < 0 || d->C_in < 1 || d->C_out < 1 || d->T < 1 || d->T > (1ll << 62)) return -1;
   if (d->K < 1 || d->stride < 1 || d->dilation < 1 || d->pad_left < 0 || d->pad_right < 0)
     return -1;
   const int64_t span =
@@ -66,6 +67,16 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   p.out_bf16 = d->out_dtype == C1G_BF16;
   if (d->x_layout != C1G_LAYOUT_NCL && d->x_layout != C1G_LAYOUT_NLC) {
     p.status = C1G_ERR_INVALID_ARG;
+    return p;
+  }
+  // sizes far past any device's memory are refused before a byte count is
+  // formed from them: N up to 65535, C_in and C_out up to 2^30, T up to 2^40,
+  // x and w below 2^46 elements each (the products are taken in 128 bits)
+  typedef unsigned __int128 u128;
+  if (d->N > 65535 || d->C_in > (1ll << 30) || d->C_out > (1ll << 30) || d->T > (1ll << 40) ||
+      (u128)(uint64_t)d->N * (uint64_t)d->C_in * (uint64_t)d->T >= ((u128)1 << 46) ||
+      (u128)(uint64_t)d->C_out * (uint64_t)d->C_in * (uint64_t)d->K >= ((u128)1 << 46)) {
+    p.status = C1G_ERR_UNSUPPORTED;
     return p;
   }
   p.x_nlc = d->x_layout == C1G_LAYOUT_NLC && d->T > 1;
@@ -99,7 +110,7 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   }
   // size limits of the kernels' index arithmetic and grids
   const uint64_t n_out = (uint64_t)d->N * (uint64_t)d->C_out * (uint64_t)p.T_out;
-  if (n_out >= (1ull << 32) || d->N > 65535 || d->C_out > (1ll << 30) || d->C_in > (1ll << 30)) {
+  if (n_out >= (1ull << 32)) {
     p.status = C1G_ERR_UNSUPPORTED;
     return p;
   }
@@ -430,10 +441,22 @@ namespace {
 bool gn_stats_args_ok(int64_t N, int64_t C, int64_t L, int32_t G) {
   return N >= 0 && C >= 1 && L >= 1 && G >= 1 && C % G == 0;
 }
-// grid of the first stage: one workgroup per slice of 32768 values of a group
+// grid of the first stage: one workgroup per slice of 32768 values of a
+// group, at most 2^31 - 1 of them; the products are taken in 128 bits with
+// each factor bounded first, so no size wraps into an accepted one (and every
+// offset, below 32768 * 2^31 values, fits 64 bits)
 bool gn_stats_fits(int64_t N, int64_t C, int64_t L, int32_t G) {
-  const uint64_t len = (uint64_t)(C / G) * (uint64_t)L;
-  return (uint64_t)N * G * ((len + 32767) / 32768) <= 0x7fffffffull;
+  typedef unsigned __int128 u128;
+  const u128 len = (u128)(uint64_t)(C / G) * (uint64_t)L;
+  const u128 slices = (len + 32767) / 32768;
+  const u128 ng = (u128)(uint64_t)N * (uint64_t)G;
+  return slices <= 0x7fffffff && ng <= 0x7fffffff && ng * slices <= 0x7fffffff;
+}
+// N * C * L < 2^32 (C and L at most 2^31), without a product that could wrap
+bool apply_fits(int64_t N, int64_t C, int64_t L) {
+  if (C > (1ll << 31) || L > (1ll << 31)) return false;
+  const uint64_t cl = (uint64_t)C * (uint64_t)L;
+  return cl < (1ull << 32) && (uint64_t)N < (1ull << 32) && (uint64_t)N * cl < (1ull << 32);
 }
 }  // namespace
 
@@ -465,8 +488,7 @@ int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const f
   if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
   if (N == 0) return C1G_OK;  // an empty batch
   if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
-  if ((uint64_t)N * C * L >= (1ull << 32) || C > (1ll << 31) || L > (1ll << 31))
-    return C1G_ERR_UNSUPPORTED;
+  if (!apply_fits(N, C, L)) return C1G_ERR_UNSUPPORTED;
   if (!aligned(y, 4) || !aligned(out, 4) || !aligned(mean, 4) || !aligned(rstd, 4) ||
       (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
     return C1G_ERR_MISALIGNED;
@@ -480,8 +502,7 @@ int gn_apply_bf16(int64_t N, int64_t C, int64_t L, int32_t G, const uint16_t* y,
   if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
   if (N == 0) return C1G_OK;  // an empty batch
   if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
-  if ((uint64_t)N * C * L >= (1ull << 32) || C > (1ll << 31) || L > (1ll << 31))
-    return C1G_ERR_UNSUPPORTED;
+  if (!apply_fits(N, C, L)) return C1G_ERR_UNSUPPORTED;
   if (!aligned(y, 2) || !aligned(out, 2) || !aligned(mean, 4) || !aligned(rstd, 4) ||
       (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
     return C1G_ERR_MISALIGNED;

@@ -46,6 +46,11 @@
  *   - Empty batch: N = 0 is valid everywhere.  The call checks the other
  *     arguments, then returns C1G_OK without reading a pointer or launching
  *     anything (tensor pointers may be NULL); its workspace size is 0.
+ *   - Sizes: conv1d_forward / conv1d_gn_forward take N up to 65535, C_in and
+ *     C_out up to 2^30, T up to 2^40, x and w below 2^46 elements each and
+ *     N*C_out*T_out below 2^32 (C1G_ERR_UNSUPPORTED beyond); every size check
+ *     is made without a product that could wrap, so no oversized argument is
+ *     accepted as a small one.
  */
 #ifndef CONV1D_GN_H
 #define CONV1D_GN_H

@@ -329,3 +329,36 @@ def test_noalloc_rejects_before_any_launch():
     bad = _desc(T=2, K=5, pad_left=0, pad_right=0)
     assert f(ctypes.byref(bad), ctypes.byref(gn), good, good, None, None, None, None, good,
              None, None, None) == 1
+
+
+def test_oversized_arguments_are_refused_not_wrapped():
+    """Sizes whose products would wrap 64 bits are refused (C1G_ERR_UNSUPPORTED,
+    workspace size 0, c1g_out_len -1 for a length past 2^62), never accepted
+    as the small sizes they wrap to.  Validation fails before any pointer is
+    read or anything is launched, so fake aligned addresses are safe."""
+    assert c1g.out_len(_desc(T=2 ** 63 - 1)) == -1
+    assert c1g.out_len(_desc(T=2 ** 62, K=1, pad_left=0, pad_right=0)) == 2 ** 62
+    for kw in (dict(T=2 ** 41, K=1, pad_left=0, pad_right=0, stride=2 ** 20, N=1, C_out=1),
+               # x of 2^59 elements (2^30 outputs)
+               dict(N=1, C_in=2 ** 29, C_out=1, T=2 ** 30, K=1, pad_left=0, pad_right=0),
+               # a channels-last fp32 x whose transpose would take 2^88 bytes
+               dict(N=65535, C_in=2 ** 30, C_out=1, T=2 ** 40, K=1, pad_left=0, pad_right=0,
+                    stride=2 ** 30, x_layout=c1g.LAYOUT_NLC),
+               # w of 2^46 elements
+               dict(N=1, C_in=2 ** 16, C_out=2 ** 30, T=1, K=1, pad_left=0, pad_right=0),
+               dict(N=65536)):
+        for dt in (c1g.C1G_F32, c1g.C1G_BF16):
+            d = _desc(**dict(kw, dtype=dt))
+            assert c1g.check(d) == 2, kw
+            assert c1g.conv1d_workspace_size(d) == 0, kw
+    lib = c1g.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    # N * C * L wraps to 0 in 64 bits
+    for f in (lib.gn_apply, lib.gn_apply_bf16):
+        assert f(2 ** 33, 2 ** 31, 1, 1, fake, fake, fake, None, None, fake, None) == 2
+    assert lib.gn_apply(2 ** 20, 2 ** 12, 2 ** 12, 1, fake, fake, fake, None, None, fake,
+                        None) == 2
+    # N * G * slices wraps to 0 in 64 bits
+    assert lib.c1g_gn_stats_workspace_size(2 ** 34, 2 ** 30, 2 ** 34, 2 ** 30) == 0
+    assert lib.gn_stats(2 ** 34, 2 ** 30, 2 ** 34, 2 ** 30, 1e-5, fake, fake, fake, fake,
+                        1 << 30, None) == 2
