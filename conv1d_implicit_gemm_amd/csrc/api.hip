@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -23,6 +26,7 @@ constexpr int64_t kResidentTiles = 256;
 
 struct Plan {
   int status = C1G_OK;
+  const char* why = "";   // what made the planner refuse (for the C1G_LOG log)
   int route = R_INVALID;
   int64_t T_out = -1;
   bool bf16 = false;      // x and w are bf16
@@ -37,6 +41,20 @@ struct Plan {
   size_t off_xt = 0;    // fp32 and x_nlc: x transposed to [N, C_in, T] (at offset 0)
   int64_t T_img = 0;
 };
+
+Plan& refuse(Plan& p, int status, const char* why) {
+  p.status = status;
+  p.why = why;
+  return p;
+}
+
+// C1G_FORCE_PATH=split (read at each call; for tests): problems the planner
+// would give a single-kernel route (fused_single_pass, fused_persistent) take
+// the split route instead, so one problem can be run down both.
+bool force_split() {
+  const char* e = std::getenv("C1G_FORCE_PATH");
+  return e != nullptr && std::strcmp(e, "split") == 0;
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -57,50 +75,43 @@ int64_t out_len(const c1g_conv_desc* d) {
 Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   Plan p;
   p.T_out = out_len(d);
-  if (p.T_out < 1) { p.status = C1G_ERR_INVALID_ARG; return p; }
-  if (d->dtype != C1G_F32 && d->dtype != C1G_BF16) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+  if (p.T_out < 1)
+    return refuse(p, C1G_ERR_INVALID_ARG,
+                  "a size, tap, stride, dilation or padding out of range, or no output position");
+  if (d->dtype != C1G_F32 && d->dtype != C1G_BF16)
+    return refuse(p, C1G_ERR_UNSUPPORTED, "dtype is neither fp32 nor bf16");
   p.bf16 = d->dtype == C1G_BF16;
-  if (d->out_dtype != C1G_F32 && d->out_dtype != C1G_BF16) {
-    p.status = C1G_ERR_UNSUPPORTED;
-    return p;
-  }
+  if (d->out_dtype != C1G_F32 && d->out_dtype != C1G_BF16)
+    return refuse(p, C1G_ERR_UNSUPPORTED, "out_dtype is neither fp32 nor bf16");
   p.out_bf16 = d->out_dtype == C1G_BF16;
-  if (d->x_layout != C1G_LAYOUT_NCL && d->x_layout != C1G_LAYOUT_NLC) {
-    p.status = C1G_ERR_INVALID_ARG;
-    return p;
-  }
+  if (d->x_layout != C1G_LAYOUT_NCL && d->x_layout != C1G_LAYOUT_NLC)
+    return refuse(p, C1G_ERR_INVALID_ARG, "x_layout is neither NCL nor NLC");
   // sizes far past any device's memory are refused before a byte count is
   // formed from them: N up to 65535, C_in and C_out up to 2^30, T up to 2^40,
   // x and w below 2^46 elements each (the products are taken in 128 bits)
   typedef unsigned __int128 u128;
   if (d->N > 65535 || d->C_in > (1ll << 30) || d->C_out > (1ll << 30) || d->T > (1ll << 40) ||
       (u128)(uint64_t)d->N * (uint64_t)d->C_in * (uint64_t)d->T >= ((u128)1 << 46) ||
-      (u128)(uint64_t)d->C_out * (uint64_t)d->C_in * (uint64_t)d->K >= ((u128)1 << 46)) {
-    p.status = C1G_ERR_UNSUPPORTED;
-    return p;
-  }
+      (u128)(uint64_t)d->C_out * (uint64_t)d->C_in * (uint64_t)d->K >= ((u128)1 << 46))
+    return refuse(p, C1G_ERR_UNSUPPORTED,
+                  "past the size limits (N 65535, C 2^30, T 2^40, x and w 2^46 elements)");
   p.x_nlc = d->x_layout == C1G_LAYOUT_NLC && d->T > 1;
   // fp32 kernels read x position-contiguous: a channels-last x is transposed
   // into the front of the workspace first
   const size_t xt_bytes =
       (p.x_nlc && !p.bf16) ? align_up((size_t)d->N * d->C_in * d->T * sizeof(float)) : 0;
-  if (xt_bytes && (d->C_in + 63) / 64 > 65535) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+  if (xt_bytes && (d->C_in + 63) / 64 > 65535)
+    return refuse(p, C1G_ERR_UNSUPPORTED, "channels-last fp32 x with C_in past 65535 * 64");
   if (nd) {
     p.norm = nd->norm;
     p.epi = nd->epilogue;
     if (p.norm < C1G_NORM_NONE || p.norm > C1G_NORM_LAYER_CHANNELS ||
-        p.epi < C1G_EPI_NONE || p.epi > C1G_EPI_ROWMIN_BIAS) {
-      p.status = C1G_ERR_INVALID_ARG;
-      return p;
-    }
-    if (p.norm == C1G_NORM_GROUP && (nd->G < 1 || d->C_out % nd->G != 0)) {
-      p.status = C1G_ERR_INVALID_ARG;
-      return p;
-    }
-    if (p.norm != C1G_NORM_NONE && !(nd->eps > 0.f && std::isfinite(nd->eps))) {
-      p.status = C1G_ERR_INVALID_ARG;
-      return p;
-    }
+        p.epi < C1G_EPI_NONE || p.epi > C1G_EPI_ROWMIN_BIAS)
+      return refuse(p, C1G_ERR_INVALID_ARG, "unknown norm or epilogue");
+    if (p.norm == C1G_NORM_GROUP && (nd->G < 1 || d->C_out % nd->G != 0))
+      return refuse(p, C1G_ERR_INVALID_ARG, "G < 1 or C_out % G != 0");
+    if (p.norm != C1G_NORM_NONE && !(nd->eps > 0.f && std::isfinite(nd->eps)))
+      return refuse(p, C1G_ERR_INVALID_ARG, "eps not finite and > 0");
   }
   // an empty batch: nothing to read, write or launch
   if (d->N == 0) {
@@ -110,15 +121,13 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   }
   // size limits of the kernels' index arithmetic and grids
   const uint64_t n_out = (uint64_t)d->N * (uint64_t)d->C_out * (uint64_t)p.T_out;
-  if (n_out >= (1ull << 32)) {
-    p.status = C1G_ERR_UNSUPPORTED;
-    return p;
-  }
+  if (n_out >= (1ull << 32))
+    return refuse(p, C1G_ERR_UNSUPPORTED, "N * C_out * T_out >= 2^32");
 
   // route
   const bool want_gn = p.norm == C1G_NORM_GROUP, want_ln = p.norm == C1G_NORM_LAYER_CHANNELS;
   const bool conv_only = p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE;
-  if (!p.bf16 && want_gn && p.epi == C1G_EPI_NONE &&
+  if (!p.bf16 && want_gn && p.epi == C1G_EPI_NONE && !force_split() &&
       fused_gn_supported(d->C_in, d->C_out, nd->G, p.T_out, d->stride, d->K, d->dilation)) {
     p.route = R_FUSED;
     p.total = xt_bytes;
@@ -156,36 +165,38 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
   size_t pack_bytes, ximg_bytes = 0;
   if (p.bf16) {
     const int tm = conv_bf16_tile_m(d->stride, d->K, d->dilation);
-    if (tm == 0) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+    if (tm == 0)
+      return refuse(p, C1G_ERR_UNSUPPORTED,
+                    "bf16: K > 8, or the input window wider than any tile's");
     p.tm = tm;
     p.tn = ConvBf16Cfg::TN;
     p.n_chunks = (int)((d->C_in + ConvBf16Cfg::CK - 1) / ConvBf16Cfg::CK);
     pack_bytes = conv_bf16_packed_bytes(d->C_in, d->C_out, d->K);
     p.T_img = conv_bf16_image_rows(p.T_out, d->stride, d->K, d->dilation);
     // row offsets into the image are 32-bit within a tile's window
-    if ((int64_t)p.n_chunks * ConvBf16Cfg::CK * 2 * 1024 >= (1ll << 31)) {
-      p.status = C1G_ERR_UNSUPPORTED;
-      return p;
-    }
+    if ((int64_t)p.n_chunks * ConvBf16Cfg::CK * 2 * 1024 >= (1ll << 31))
+      return refuse(p, C1G_ERR_UNSUPPORTED, "bf16: C_in too large for 32-bit image offsets");
     ximg_bytes = conv_bf16_image_bytes(d->N, d->C_in, p.T_img);
   } else {
-    if (d->K > 8) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+    if (d->K > 8) return refuse(p, C1G_ERR_UNSUPPORTED, "fp32: K > 8");
     const int64_t xw = (int64_t)(ConvF32Cfg::TM - 1) * d->stride +
                        (int64_t)(d->K - 1) * d->dilation + 1;
-    if (xw > conv_f32_window_cap(d->stride)) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+    if (xw > conv_f32_window_cap(d->stride))
+      return refuse(p, C1G_ERR_UNSUPPORTED, "fp32: the input window is wider than a tile's");
     p.tm = ConvF32Cfg::TM;
     p.tn = ConvF32Cfg::TN;
     p.n_chunks = (int)((d->C_in + ConvF32Cfg::CK - 1) / ConvF32Cfg::CK);
     pack_bytes = conv_f32_packed_bytes(d->C_in, d->C_out, d->K);
   }
   const int64_t n_tt = (p.T_out + p.tm - 1) / p.tm, n_ct = (d->C_out + p.tn - 1) / p.tn;
-  if (n_tt > (1ll << 31) - 1 || n_ct > 65535) { p.status = C1G_ERR_UNSUPPORTED; return p; }
+  if (n_tt > (1ll << 31) - 1 || n_ct > 65535)
+    return refuse(p, C1G_ERR_UNSUPPORTED, "too many tiles for the grid");
   p.n_ttiles = (int)n_tt;
   p.n_ctiles = (int)n_ct;
   // bf16 GroupNorm (groups that tile the 128-channel tiles) or channel
   // LayerNorm without the row-min: normalise inside the persistent conv
   if (p.bf16 && (want_gn || want_ln) && p.epi == C1G_EPI_NONE &&
-      !(nd->flags & C1G_FLAG_NO_PERSISTENT) && n_tt * n_ct <= kResidentTiles) {
+      !(nd->flags & C1G_FLAG_NO_PERSISTENT) && !force_split() && n_tt * n_ct <= kResidentTiles) {
     const int64_t tn = ConvBf16Cfg::TN;
     const int64_t cpg = want_gn ? d->C_out / nd->G : tn;
     if (tn % cpg == 0 || cpg % tn == 0) p.route = R_PERSIST;
@@ -225,6 +236,16 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
 bool aligned(const void* p, size_t a) { return (((uintptr_t)p) % a) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? C1G_OK : C1G_ERR_HIP; }
+
+// What a call did beyond its plan (a fallback it took), for its log line;
+// set by the run paths, cleared by each entry point.
+thread_local const char* t_note = nullptr;
+
+// Records what made a call refuse (for its log line) and returns the status.
+int refused(const char*& why, int status, const char* reason) {
+  why = reason;
+  return status;
+}
 
 ConvArgs conv_args(const Plan& p, const c1g_conv_desc* d, const void* x, const float* bias,
                    void* y, char* ws) {
@@ -304,7 +325,10 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
              const void* w, const float* bias, const float* gamma, const float* beta,
              const float* bias2, void* out, float* mean_out, float* rstd_out, char* ws,
              hipStream_t s) {
-  if (!aligned(x, 16) || !aligned(w, 16)) return C1G_ERR_MISALIGNED;
+  if (!aligned(x, 16) || !aligned(w, 16)) {
+    t_note = "gemm_rows: x or w not 16-byte aligned";
+    return C1G_ERR_MISALIGNED;
+  }
   const bool conv_only = !nd || (p.norm == C1G_NORM_NONE && p.epi == C1G_EPI_NONE);
   const int out_dt = p.out_bf16 ? C1G_BF16 : C1G_F32;
   GemmArgs g{};
@@ -331,8 +355,10 @@ int run_gemm(const Plan& p, const c1g_conv_desc* d, const c1g_norm_desc* nd, con
   if (p.gemm_fused) {
     // one launch (cooperative with C1G_FLAG_COOPERATIVE) on request when every
     // tile can be resident at once, else the GEMM and a broadcast kernel
-    if ((nd->flags & C1G_FLAG_ROWMIN_ONE_LAUNCH) && !(nd->flags & C1G_FLAG_NO_PERSISTENT) &&
-        (int64_t)p.n_ctiles * p.n_ttiles <= gemm_bf16_rowmin_capacity()) {
+    const bool one = (nd->flags & C1G_FLAG_ROWMIN_ONE_LAUNCH) && !(nd->flags & C1G_FLAG_NO_PERSISTENT);
+    if (one && (int64_t)p.n_ctiles * p.n_ttiles > gemm_bf16_rowmin_capacity())
+      t_note = "one launch requested, more tiles than the device keeps resident: two launches";
+    if (one && (int64_t)p.n_ctiles * p.n_ttiles <= gemm_bf16_rowmin_capacity()) {
       g.bias2 = bias2;
       g.out = out;
       g.out_bf16 = p.out_bf16;
@@ -387,6 +413,64 @@ const char* route_name(int r) {
   }
 }
 
+// ---- host-side log: with the environment variable C1G_LOG=1 (read at each
+// call) every entry point writes one line to stderr: its arguments' sizes,
+// the plan (route, tiles, workspace), the status and, for a refusal, what
+// caused it.  Nothing is logged otherwise, and never from the device.
+bool log_enabled() {
+  const char* e = std::getenv("C1G_LOG");
+  return e != nullptr && std::strcmp(e, "1") == 0;
+}
+
+const char* dtype_name(int32_t t) { return t == C1G_F32 ? "fp32" : t == C1G_BF16 ? "bf16" : "?"; }
+
+// one fputs per line, so lines of concurrent calls do not interleave
+void log_line(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fputs(buf, stderr);
+}
+
+int log_conv(const char* entry, const c1g_conv_desc* d, const c1g_norm_desc* nd, const Plan& p,
+             int status, const char* why) {
+  if (!log_enabled()) return status;
+  char geo[320] = "(no descriptor)", nrm[128] = "", plan[160] = "";
+  if (d)
+    std::snprintf(geo, sizeof(geo),
+                  "N=%lld C_in=%lld C_out=%lld T=%lld K=%d stride=%d dilation=%d pad=%d/%d "
+                  "%s->%s%s",
+                  (long long)d->N, (long long)d->C_in, (long long)d->C_out, (long long)d->T,
+                  d->K, d->stride, d->dilation, d->pad_left, d->pad_right,
+                  dtype_name(d->dtype), dtype_name(d->out_dtype),
+                  d->x_layout == C1G_LAYOUT_NLC ? " channels-last" : "");
+  if (nd)
+    std::snprintf(nrm, sizeof(nrm), " norm=%s G=%d eps=%g%s flags=%d",
+                  nd->norm == C1G_NORM_GROUP ? "group"
+                  : nd->norm == C1G_NORM_LAYER_CHANNELS ? "layer_channels"
+                  : nd->norm == C1G_NORM_NONE ? "none" : "?",
+                  nd->G, (double)nd->eps, nd->epilogue == C1G_EPI_ROWMIN_BIAS ? " rowmin" : "",
+                  nd->flags);
+  if (p.status == C1G_OK && p.route != R_INVALID)
+    std::snprintf(plan, sizeof(plan), " | %s T_out=%lld tiles=%dx%d ws=%zu",
+                  route_name(p.route), (long long)p.T_out, p.n_ttiles, p.n_ctiles, p.total);
+  const char* reason = (why && *why) ? why : (t_note ? t_note : "");
+  log_line("c1g: %s %s%s%s -> %s%s%s\n", entry, geo, nrm, plan, c1g_status_string(status),
+           *reason ? ": " : "", reason);
+  return status;
+}
+
+int log_norm(const char* entry, int64_t N, int64_t C, int64_t L, int32_t G, int status,
+             const char* why) {
+  if (!log_enabled()) return status;
+  log_line("c1g: %s N=%lld C=%lld L=%lld G=%d -> %s%s%s\n", entry, (long long)N, (long long)C,
+           (long long)L, G, c1g_status_string(status), (why && *why) ? ": " : "",
+           why ? why : "");
+  return status;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,20 +505,28 @@ size_t c1g_conv1d_gn_workspace_size(const c1g_conv_desc* d, const c1g_norm_desc*
 
 int conv1d_forward(const c1g_conv_desc* d, const void* x, const void* w, const float* bias,
                    void* y, void* ws, size_t ws_bytes, void* stream) {
-  if (!d) return C1G_ERR_INVALID_ARG;
-  const Plan p = make_plan(d, nullptr);
-  if (p.status != C1G_OK) return p.status;
-  if (p.route == R_EMPTY) return C1G_OK;
-  if (!x || !w || !y) return C1G_ERR_INVALID_ARG;
-  const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
-  if (!aligned(x, es) || !aligned(w, es) || !aligned(y, os) || (bias && !aligned(bias, 4)))
-    return C1G_ERR_MISALIGNED;
-  if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
-  if (p.total > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
-  if (p.route == R_GEMM)
-    return run_gemm(p, d, nullptr, x, w, bias, nullptr, nullptr, nullptr, y, nullptr, nullptr,
-                    (char*)ws, (hipStream_t)stream);
-  return run_conv(p, d, x, w, bias, y, (char*)ws, EPI_STORE, (hipStream_t)stream);
+  t_note = nullptr;
+  Plan p;
+  const char* why = "";
+  const int st = [&]() -> int {
+    if (!d) return refused(why, C1G_ERR_INVALID_ARG, "no descriptor");
+    p = make_plan(d, nullptr);
+    if (p.status != C1G_OK) return refused(why, p.status, p.why);
+    if (p.route == R_EMPTY) return C1G_OK;
+    if (!x || !w || !y) return refused(why, C1G_ERR_INVALID_ARG, "x, w or y is NULL");
+    const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
+    if (!aligned(x, es) || !aligned(w, es) || !aligned(y, os) || (bias && !aligned(bias, 4)))
+      return refused(why, C1G_ERR_MISALIGNED, "a tensor not aligned to its element size");
+    if (p.total > 0 && (!ws || ws_bytes < p.total))
+      return refused(why, C1G_ERR_WORKSPACE, "workspace NULL or below the size query");
+    if (p.total > 0 && !aligned(ws, kAlign))
+      return refused(why, C1G_ERR_MISALIGNED, "workspace not 256-byte aligned");
+    if (p.route == R_GEMM)
+      return run_gemm(p, d, nullptr, x, w, bias, nullptr, nullptr, nullptr, y, nullptr, nullptr,
+                      (char*)ws, (hipStream_t)stream);
+    return run_conv(p, d, x, w, bias, y, (char*)ws, EPI_STORE, (hipStream_t)stream);
+  }();
+  return log_conv("conv1d_forward", d, nullptr, p, st, why);
 }
 
 namespace {
@@ -468,64 +560,91 @@ size_t c1g_gn_stats_workspace_size(int64_t N, int64_t C, int64_t L, int32_t G) {
 
 int gn_stats(int64_t N, int64_t C, int64_t L, int32_t G, float eps, const float* y, float* mean,
              float* rstd, void* ws, size_t ws_bytes, void* stream) {
-  if (!gn_stats_args_ok(N, C, L, G) || !(eps > 0.f && std::isfinite(eps)))
-    return C1G_ERR_INVALID_ARG;
-  if (N == 0) return C1G_OK;  // an empty batch
-  if (!y || !mean || !rstd) return C1G_ERR_INVALID_ARG;
-  if (!gn_stats_fits(N, C, L, G)) return C1G_ERR_UNSUPPORTED;
-  if (!aligned(y, 4) || !aligned(mean, 4) || !aligned(rstd, 4)) return C1G_ERR_MISALIGNED;
-  // the size the query reports (rounded up to the workspace alignment)
-  const size_t need = c1g_gn_stats_workspace_size(N, C, L, G);
-  if (need > 0 && (!ws || ws_bytes < need)) return C1G_ERR_WORKSPACE;
-  if (need > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
-  return hip_status(gn_stats_launch(y, N, C, L, G, eps, mean, rstd,
-                                    need > 0 ? (float*)ws : nullptr, (hipStream_t)stream));
+  const char* why = "";
+  const int st = [&]() -> int {
+    if (!gn_stats_args_ok(N, C, L, G))
+      return refused(why, C1G_ERR_INVALID_ARG, "a size out of range, G < 1 or C % G != 0");
+    if (!(eps > 0.f && std::isfinite(eps)))
+      return refused(why, C1G_ERR_INVALID_ARG, "eps not finite and > 0");
+    if (N == 0) return C1G_OK;  // an empty batch
+    if (!y || !mean || !rstd) return refused(why, C1G_ERR_INVALID_ARG, "y, mean or rstd is NULL");
+    if (!gn_stats_fits(N, C, L, G))
+      return refused(why, C1G_ERR_UNSUPPORTED, "more than 2^31 - 1 slices of 32768 values");
+    if (!aligned(y, 4) || !aligned(mean, 4) || !aligned(rstd, 4))
+      return refused(why, C1G_ERR_MISALIGNED, "a tensor not 4-byte aligned");
+    // the size the query reports (rounded up to the workspace alignment)
+    const size_t need = c1g_gn_stats_workspace_size(N, C, L, G);
+    if (need > 0 && (!ws || ws_bytes < need))
+      return refused(why, C1G_ERR_WORKSPACE, "workspace NULL or below the size query");
+    if (need > 0 && !aligned(ws, kAlign))
+      return refused(why, C1G_ERR_MISALIGNED, "workspace not 256-byte aligned");
+    return hip_status(gn_stats_launch(y, N, C, L, G, eps, mean, rstd,
+                                      need > 0 ? (float*)ws : nullptr, (hipStream_t)stream));
+  }();
+  return log_norm("gn_stats", N, C, L, G, st, why);
 }
 
 int gn_apply(int64_t N, int64_t C, int64_t L, int32_t G, const float* y, const float* mean,
              const float* rstd, const float* gamma, const float* beta, float* out,
              void* stream) {
-  if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
-  if (N == 0) return C1G_OK;  // an empty batch
-  if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
-  if (!apply_fits(N, C, L)) return C1G_ERR_UNSUPPORTED;
-  if (!aligned(y, 4) || !aligned(out, 4) || !aligned(mean, 4) || !aligned(rstd, 4) ||
-      (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
-    return C1G_ERR_MISALIGNED;
-  return hip_status(gn_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, C1G_F32, N, C, L,
-                                   G, (hipStream_t)stream));
+  const char* why = "";
+  const int st = [&]() -> int {
+    if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0)
+      return refused(why, C1G_ERR_INVALID_ARG, "a size out of range, G < 1 or C % G != 0");
+    if (N == 0) return C1G_OK;  // an empty batch
+    if (!y || !mean || !rstd || !out)
+      return refused(why, C1G_ERR_INVALID_ARG, "y, mean, rstd or out is NULL");
+    if (!apply_fits(N, C, L))
+      return refused(why, C1G_ERR_UNSUPPORTED, "N * C * L >= 2^32, or C or L past 2^31");
+    if (!aligned(y, 4) || !aligned(out, 4) || !aligned(mean, 4) || !aligned(rstd, 4) ||
+        (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
+      return refused(why, C1G_ERR_MISALIGNED, "a tensor not aligned to its element size");
+    return hip_status(gn_apply_launch(y, C1G_F32, mean, rstd, gamma, beta, out, C1G_F32, N, C,
+                                     L, G, (hipStream_t)stream));
+  }();
+  return log_norm("gn_apply", N, C, L, G, st, why);
 }
 
 int gn_apply_bf16(int64_t N, int64_t C, int64_t L, int32_t G, const uint16_t* y,
                   const float* mean, const float* rstd, const float* gamma, const float* beta,
                   uint16_t* out, void* stream) {
-  if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0) return C1G_ERR_INVALID_ARG;
-  if (N == 0) return C1G_OK;  // an empty batch
-  if (!y || !mean || !rstd || !out) return C1G_ERR_INVALID_ARG;
-  if (!apply_fits(N, C, L)) return C1G_ERR_UNSUPPORTED;
-  if (!aligned(y, 2) || !aligned(out, 2) || !aligned(mean, 4) || !aligned(rstd, 4) ||
-      (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
-    return C1G_ERR_MISALIGNED;
-  return hip_status(gn_apply_launch(y, C1G_BF16, mean, rstd, gamma, beta, out, C1G_BF16, N, C,
-                                   L, G, (hipStream_t)stream));
+  const char* why = "";
+  const int st = [&]() -> int {
+    if (N < 0 || C < 1 || L < 1 || G < 1 || C % G != 0)
+      return refused(why, C1G_ERR_INVALID_ARG, "a size out of range, G < 1 or C % G != 0");
+    if (N == 0) return C1G_OK;  // an empty batch
+    if (!y || !mean || !rstd || !out)
+      return refused(why, C1G_ERR_INVALID_ARG, "y, mean, rstd or out is NULL");
+    if (!apply_fits(N, C, L))
+      return refused(why, C1G_ERR_UNSUPPORTED, "N * C * L >= 2^32, or C or L past 2^31");
+    if (!aligned(y, 2) || !aligned(out, 2) || !aligned(mean, 4) || !aligned(rstd, 4) ||
+        (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)))
+      return refused(why, C1G_ERR_MISALIGNED, "a tensor not aligned to its element size");
+    return hip_status(gn_apply_launch(y, C1G_BF16, mean, rstd, gamma, beta, out, C1G_BF16, N,
+                                     C, L, G, (hipStream_t)stream));
+  }();
+  return log_norm("gn_apply_bf16", N, C, L, G, st, why);
 }
 
 }  // extern "C"
 
 namespace {
 
-// The pointer checks of conv1d_gn_forward (everything but the workspace).
+// The pointer checks of conv1d_gn_forward (everything but the workspace);
+// *why names a refusal's cause.
 int check_forward_ptrs(const Plan& p, const void* x, const void* w, const float* bias,
                        const float* gamma, const float* beta, const float* bias2,
-                       const void* out, const float* mean_out, const float* rstd_out) {
-  if (!x || !w || !out) return C1G_ERR_INVALID_ARG;
-  if (p.epi == C1G_EPI_ROWMIN_BIAS && !bias2) return C1G_ERR_INVALID_ARG;
+                       const void* out, const float* mean_out, const float* rstd_out,
+                       const char** why) {
+  if (!x || !w || !out) return refused(*why, C1G_ERR_INVALID_ARG, "x, w or out is NULL");
+  if (p.epi == C1G_EPI_ROWMIN_BIAS && !bias2)
+    return refused(*why, C1G_ERR_INVALID_ARG, "the row-min epilogue without bias2");
   const size_t es = p.bf16 ? 2 : 4, os = p.out_bf16 ? 2 : 4;
   if (!aligned(x, es) || !aligned(w, es) || !aligned(out, os) || (bias && !aligned(bias, 4)) ||
       (gamma && !aligned(gamma, 4)) || (beta && !aligned(beta, 4)) ||
       (bias2 && !aligned(bias2, 4)) || (mean_out && !aligned(mean_out, 4)) ||
       (rstd_out && !aligned(rstd_out, 4)))
-    return C1G_ERR_MISALIGNED;
+    return refused(*why, C1G_ERR_MISALIGNED, "a tensor not aligned to its element size");
   return C1G_OK;
 }
 
@@ -556,22 +675,23 @@ int scratch_address(void** out) {
   return C1G_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
-                      const void* w, const float* bias, const float* gamma, const float* beta,
-                      const float* bias2, void* out, float* mean_out, float* rstd_out,
-                      void* ws, size_t ws_bytes, void* stream) {
-  if (!d || !nd) return C1G_ERR_INVALID_ARG;
-  const Plan p = make_plan(d, nd);
-  if (p.status != C1G_OK) return p.status;
+// The work of conv1d_gn_forward, for it and the allocation-free entry point:
+// p is the plan (filled in), why the cause of a refusal.
+int forward_impl(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x, const void* w,
+                 const float* bias, const float* gamma, const float* beta, const float* bias2,
+                 void* out, float* mean_out, float* rstd_out, void* ws, size_t ws_bytes,
+                 void* stream, Plan& p, const char*& why) {
+  if (!d || !nd) return refused(why, C1G_ERR_INVALID_ARG, "no descriptor");
+  p = make_plan(d, nd);
+  if (p.status != C1G_OK) return refused(why, p.status, p.why);
   if (p.route == R_EMPTY) return C1G_OK;
-  const int pst = check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out);
+  const int pst =
+      check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, &why);
   if (pst != C1G_OK) return pst;
-  if (p.total > 0 && (!ws || ws_bytes < p.total)) return C1G_ERR_WORKSPACE;
-  if (p.total > 0 && !aligned(ws, kAlign)) return C1G_ERR_MISALIGNED;
+  if (p.total > 0 && (!ws || ws_bytes < p.total))
+    return refused(why, C1G_ERR_WORKSPACE, "workspace NULL or below the size query");
+  if (p.total > 0 && !aligned(ws, kAlign))
+    return refused(why, C1G_ERR_MISALIGNED, "workspace not 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   char* wsb = (char*)ws;
 
@@ -619,6 +739,10 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
                     p.norm == C1G_NORM_GROUP ? EPI_GN_FUSED : EPI_LN_FUSED, s, nd, gamma, beta,
                     mean_out, rstd_out);
 
+  if (p.route == R_PERSIST)
+    t_note = "fused_persistent planned, more tiles per sample than the device keeps "
+             "resident: the split route ran";
+
   // split route: conv (+ partial statistics from the fp32 accumulators) into
   // out in out's type, merge, then in-place passes
   const int conv_epi = p.norm == C1G_NORM_GROUP ? EPI_GN_PART
@@ -656,24 +780,48 @@ int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const voi
   return hip_status(e);
 }
 
+}  // namespace
+
+extern "C" {
+
+int conv1d_gn_forward(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
+                      const void* w, const float* bias, const float* gamma, const float* beta,
+                      const float* bias2, void* out, float* mean_out, float* rstd_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+  t_note = nullptr;
+  Plan p;
+  const char* why = "";
+  const int st = forward_impl(d, nd, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out,
+                              ws, ws_bytes, stream, p, why);
+  return log_conv("conv1d_gn_forward", d, nd, p, st, why);
+}
+
 int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* nd, const void* x,
                               const void* w, const float* bias, const float* gamma,
                               const float* beta, const float* bias2, void* out,
                               float* mean_out, float* rstd_out, void* stream) {
-  if (!d || !nd) return C1G_ERR_INVALID_ARG;
-  const Plan p = make_plan(d, nd);
-  if (p.status != C1G_OK) return p.status;
-  if (p.route == R_EMPTY) return C1G_OK;
-  const int pst = check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out);
-  if (pst != C1G_OK) return pst;
-  if (p.total > C1G_NOALLOC_SCRATCH_BYTES) return C1G_ERR_WORKSPACE;
-  void* ws = nullptr;
-  if (p.total > 0) {
-    const int st = scratch_address(&ws);
-    if (st != C1G_OK) return st;
-  }
-  return conv1d_gn_forward(d, nd, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, ws,
-                           p.total > 0 ? C1G_NOALLOC_SCRATCH_BYTES : 0, stream);
+  t_note = nullptr;
+  Plan p;
+  const char* why = "";
+  const int st = [&]() -> int {
+    if (!d || !nd) return refused(why, C1G_ERR_INVALID_ARG, "no descriptor");
+    p = make_plan(d, nd);
+    if (p.status != C1G_OK) return refused(why, p.status, p.why);
+    if (p.route == R_EMPTY) return C1G_OK;
+    const int pst =
+        check_forward_ptrs(p, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, &why);
+    if (pst != C1G_OK) return pst;
+    if (p.total > C1G_NOALLOC_SCRATCH_BYTES)
+      return refused(why, C1G_ERR_WORKSPACE, "workspace past the static scratch");
+    void* ws = nullptr;
+    if (p.total > 0) {
+      const int sst = scratch_address(&ws);
+      if (sst != C1G_OK) return refused(why, sst, "no device scratch address");
+    }
+    return forward_impl(d, nd, x, w, bias, gamma, beta, bias2, out, mean_out, rstd_out, ws,
+                        p.total > 0 ? C1G_NOALLOC_SCRATCH_BYTES : 0, stream, p, why);
+  }();
+  return log_conv("conv1d_gn_forward_noalloc", d, nd, p, st, why);
 }
 
 const char* c1g_status_string(int status) {

@@ -51,6 +51,16 @@
  *     N*C_out*T_out below 2^32 (C1G_ERR_UNSUPPORTED beyond); every size check
  *     is made without a product that could wrap, so no oversized argument is
  *     accepted as a small one.
+ *   - Environment variables (read at each call; none is needed):
+ *       C1G_LOG=1             every entry-point call writes one line to stderr:
+ *                             its sizes, the plan (route, tiles, workspace),
+ *                             the status and, for a refusal or a fallback taken
+ *                             at run time, its cause.  Host only.
+ *       C1G_FORCE_PATH=split  for tests: problems planned on a single-kernel
+ *                             route (fused_single_pass, fused_persistent) take
+ *                             the split route, so one problem runs down both.
+ *       C1G_BARRIER_SPINS, C1G_RESIDENT_LIMIT  for tests of the routes whose
+ *                             workgroups wait on each other (see c1g_route).
  */
 #ifndef CONV1D_GN_H
 #define CONV1D_GN_H

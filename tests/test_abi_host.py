@@ -362,3 +362,65 @@ def test_oversized_arguments_are_refused_not_wrapped():
     assert lib.c1g_gn_stats_workspace_size(2 ** 34, 2 ** 30, 2 ** 34, 2 ** 30) == 0
     assert lib.gn_stats(2 ** 34, 2 ** 30, 2 ** 34, 2 ** 30, 1e-5, fake, fake, fake, fake,
                         1 << 30, None) == 2
+
+
+def test_log_names_plan_and_refusal():
+    """C1G_LOG=1: every entry-point call writes one stderr line with its sizes,
+    the plan and, for a refusal, the cause; without it nothing is written.
+    (Refused calls only: nothing here reaches a launch.)"""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import conv1d_implicit_gemm_amd as c1g
+lib = c1g.load_library()
+d = c1g.ConvDesc(2, 16, 32, 256, 3, 1, 1, 1, 1, 0, 0, 0)
+P = None
+bad_g = c1g.NormDesc(c1g.NORM_GROUP, 7, 1e-5, 0)
+good = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+print(lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(bad_g), P, P, P, P, P, P, P, P, P, P, 0, P))
+print(lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(good), P, P, P, P, P, P, P, P, P, P, 0, P))
+f = ctypes.c_void_p(1 << 20)
+print(lib.gn_apply(2 ** 33, 2 ** 31, 1, 1, f, f, f, P, P, f, P))
+print(lib.conv1d_forward(ctypes.byref(c1g.ConvDesc(2, 16, 32, 256, 9, 1, 1, 4, 4, 0, 0, 0)), f, f, P, f, P, 0, P))
+""" % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))),)
+    env = dict(os.environ, C1G_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["1", "1", "2", "2"]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("c1g: ")]
+    assert len(lines) == 4, r.stderr
+    assert lines[0].startswith("c1g: conv1d_gn_forward N=2 C_in=16 C_out=32 T=256 K=3")
+    assert "G=7" in lines[0] and lines[0].endswith("invalid argument: G < 1 or C_out % G != 0")
+    assert "| fused_single_pass T_out=256" in lines[1]
+    assert lines[1].endswith("invalid argument: x, w or out is NULL")
+    assert lines[2].startswith("c1g: gn_apply N=8589934592 C=2147483648 L=1 G=1")
+    assert "unsupported configuration: N * C * L >= 2^32" in lines[2]
+    assert lines[3].startswith("c1g: conv1d_forward") and "fp32: K > 8" in lines[3]
+    env.pop("C1G_LOG")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert r.returncode == 0 and "c1g: " not in r.stderr
+
+
+def test_force_path_split(monkeypatch):
+    """C1G_FORCE_PATH=split: problems planned on a single-kernel route are
+    planned on the split route (the workspace query follows); others keep
+    their route."""
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    fused = _desc()
+    persistent = _desc(C_in=64, C_out=256, T=1000, dtype=c1g.C1G_BF16)
+    linear = _desc(N=64, C_in=256, C_out=512, T=1, K=1, pad_left=0, pad_right=0,
+                   dtype=c1g.C1G_BF16)
+    assert c1g.route(fused, gn) == "fused_single_pass"
+    assert c1g.route(persistent, gn) == "fused_persistent"
+    assert c1g.route(linear, gn) == "gemm_rows"
+    monkeypatch.setenv("C1G_FORCE_PATH", "split")
+    assert c1g.route(fused, gn) == "split"
+    assert c1g.route(persistent, gn) == "split"
+    assert c1g.route(linear, gn) == "gemm_rows"
+    assert c1g.conv1d_gn_workspace_size(fused, gn) > 0
+    monkeypatch.setenv("C1G_FORCE_PATH", "other")
+    assert c1g.route(fused, gn) == "fused_single_pass"
