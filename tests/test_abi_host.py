@@ -424,3 +424,25 @@ def test_force_path_split(monkeypatch):
     assert c1g.conv1d_gn_workspace_size(fused, gn) > 0
     monkeypatch.setenv("C1G_FORCE_PATH", "other")
     assert c1g.route(fused, gn) == "fused_single_pass"
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="needs a machine without a GPU, where every launch fails")
+def test_launch_failure_is_reported_as_hip_error():
+    """Where no device exists a call that passes validation fails at its
+    launch: each entry point returns C1G_ERR_HIP, neither OK nor a crash.
+    (Fake, aligned addresses: nothing reads them and nothing runs.)"""
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a GPU is present")
+    lib = c1g.load_library()
+    f = ctypes.c_void_p(1 << 20)
+    d = _desc()
+    gn = c1g.NormDesc(c1g.NORM_GROUP, 8, 1e-5, 0)
+    assert c1g.route(d, gn) == "fused_single_pass"
+    assert lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(gn), f, f, f, f, f, None, f, None,
+                                 None, None, 0, None) == 5
+    assert lib.conv1d_forward(ctypes.byref(d), f, f, None, f, f, 1 << 40, None) == 5
+    assert lib.gn_stats(2, 32, 256, 8, 1e-5, f, f, f, f, 1 << 30, None) == 5
+    assert lib.gn_apply(2, 32, 256, 8, f, f, f, None, None, f, None) == 5
+    assert lib.gn_apply_bf16(2, 32, 256, 8, f, f, f, None, None, f, None) == 5
