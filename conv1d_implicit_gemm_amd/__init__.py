@@ -229,6 +229,20 @@ def _stats_shape(desc, nd, T_out, G):
     return (desc.N, G) if nd.norm == NORM_GROUP else (desc.N, T_out)
 
 
+def _workspace(ws, device=None):
+    """A caller's workspace: a contiguous tensor (any dtype) on the call's
+    device (checked once device is given); returns (ws, its size in bytes)."""
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a tensor")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if device is not None and ws.device != device:
+        raise ValueError("workspace must be on %s" % device)
+    return ws, ws.numel() * ws.element_size()
+
+
 def _raise(status, where):
     if status != 0:
         raise C1GError(status, where)
@@ -284,6 +298,7 @@ def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_r
     _per_channel(bias, "bias", w.shape[0] if isinstance(w, torch.Tensor) else -1)
     desc, T_out = _conv_desc(x, w, stride, padding, pad_left, pad_right, causal, dilation,
                              odt, channels_last, out)
+    _workspace(workspace)
     _conv_device(x, w)
     _need(bias, "bias", torch.float32, x.device)
     if out is None:
@@ -292,9 +307,9 @@ def conv1d_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pad_r
     ws_bytes = lib.c1g_conv1d_workspace_size(ctypes.byref(desc))
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+    workspace, ws_have = _workspace(workspace, x.device)
     st = lib.conv1d_forward(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(out),
-                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
-                            _stream(x.device))
+                            _ptr(workspace), ws_have, _stream(x.device))
     _raise(st, "conv1d_forward")
     return out
 
@@ -319,6 +334,7 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
                              odt, channels_last, out)
     nd = make_norm(norm, groups, eps, rowmin_bias is not None, persistent, one_launch,
                    cooperative)
+    _workspace(workspace)
     _conv_device(x, w)
     for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta"), (rowmin_bias, "rowmin_bias")):
         _need(t, nm, torch.float32, x.device)
@@ -333,10 +349,10 @@ def conv1d_gn_forward(x, w, bias=None, *, stride=1, padding=0, pad_left=None, pa
     ws_bytes = lib.c1g_conv1d_gn_workspace_size(ctypes.byref(desc), ctypes.byref(nd))
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+    workspace, ws_have = _workspace(workspace, x.device)
     st = lib.conv1d_gn_forward(ctypes.byref(desc), ctypes.byref(nd), _ptr(x), _ptr(w),
                                _ptr(bias), _ptr(gamma), _ptr(beta), _ptr(rowmin_bias),
-                               _ptr(out), _ptr(mean), _ptr(rstd), _ptr(workspace),
-                               workspace.numel() if workspace is not None else 0,
+                               _ptr(out), _ptr(mean), _ptr(rstd), _ptr(workspace), ws_have,
                                _stream(x.device))
     _raise(st, "conv1d_gn_forward")
     return (out, mean, rstd) if return_stats else out

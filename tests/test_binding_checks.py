@@ -116,3 +116,14 @@ def test_prepared_checks():
     with pytest.raises(ValueError, match="device"):
         c1g.PreparedConv1dGN(x, w, padding=1, norm="layer_channels",
                              mean=torch.zeros(N, T), rstd=torch.zeros(N, T))
+
+
+@pytest.mark.parametrize("ws", [torch.zeros(64, 4).t(), [0] * 64])
+def test_workspace_must_be_a_contiguous_tensor(ws):
+    """A caller's workspace is checked before the device: a non-contiguous
+    tensor, or something that is not a tensor, is refused."""
+    x, w = _xw()
+    with pytest.raises((ValueError, TypeError), match="workspace"):
+        c1g.conv1d_forward(x, w, padding=1, workspace=ws)
+    with pytest.raises((ValueError, TypeError), match="workspace"):
+        _gn(workspace=ws)

@@ -331,3 +331,29 @@ def test_unaligned_x_on_the_gemm_route_is_rejected():
     with pytest.raises(c1g.C1GError) as e:
         c1g.conv1d_gn_forward(x, w, None, norm="group", groups=8)
     assert e.value.status == 4
+
+
+def test_caller_workspace():
+    """A caller's workspace may have any dtype: enough bytes give the bits of
+    the library-allocated one.  One in host memory, or short of the size
+    query in bytes, is refused before anything runs."""
+    wl = Workload("ws_split_f32", N=2, C_in=24, C_out=48, T=1500, K=3, pad_left=1, pad_right=1,
+                  G=6)
+    announce("caller workspace", wl.name)
+    inp = make_inputs(wl, 5)
+    x, w, b, ga, be = (inp[k].to(DEV) for k in ("x", "w", "bias", "gamma", "beta"))
+    kw = dict(pad_left=1, pad_right=1, norm="group", groups=6, gamma=ga, beta=be)
+    ref = c1g.conv1d_gn_forward(x, w, b, **kw)
+    need = c1g.conv1d_gn_workspace_size(
+        c1g.make_desc(2, 24, 48, 1500, 3, pad_left=1, pad_right=1),
+        c1g.make_norm("group", 6))
+    assert need > 0
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=DEV)
+    got = c1g.conv1d_gn_forward(x, w, b, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    with pytest.raises(ValueError, match="workspace"):
+        c1g.conv1d_gn_forward(x, w, b, workspace=torch.empty(need, dtype=torch.uint8), **kw)
+    with pytest.raises(c1g.C1GError, match="workspace"):
+        c1g.conv1d_gn_forward(x, w, b, workspace=torch.empty(need // 8, dtype=torch.float32,
+                                                             device=DEV), **kw)
