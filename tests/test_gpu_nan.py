@@ -1,17 +1,19 @@
-"""A NaN in the input stays where the definition puts it.
+"""A NaN or an infinity in the input stays where the definition puts it.
 
-One element of x (sample n0, input channel c0, position t0) is set to NaN.
+One element of x (sample n0, input channel c0, position t0) is set to NaN
+(or +inf: the same elements become non-finite, and the GPU and the oracle
+agree on which of them are NaN, +inf or -inf).
 The convolution carries it into every output channel at the output
 positions whose window holds t0 (t·s + j·d − p_l = t0 for some tap j); a
 GroupNorm group's statistics cover all positions of its channels, so under
 GroupNorm the whole sample becomes NaN; a LayerNorm over channels keeps it
 at those positions; the row-min reduces like PyTorch's min over the channel
 dimension (the model of "Kimi-K2.6 l2_p75"), which returns NaN for a row
-holding one.  Each case checks, on every route, that the output is NaN
-exactly there, that every other value has the bits of the clean run (no
-statistics, staging or rounds shared across samples or positions leak
-it), and that the oracle marks the same elements NaN and agrees on the
-poisoned sample's finite values."""
+holding one.  Each case checks, on every route, that the output is
+non-finite exactly there, that every other value has the bits of the clean
+run (no statistics, staging or rounds shared across samples or positions
+leak it), and that the oracle marks the same elements NaN, +inf or -inf and
+agrees on the poisoned sample's finite values."""
 import numpy as np
 import pytest
 import torch
@@ -69,26 +71,30 @@ def expected_nan(wl, T_out, n0, t0):
     return mask
 
 
+@pytest.mark.parametrize("poison", [float("nan"), float("inf")], ids=["nan", "inf"])
 @pytest.mark.parametrize("wl,route,n0,c0,t0", CASES, ids=[c[0].name for c in CASES])
-def test_nan_stays_where_defined(wl, route, n0, c0, t0):
-    announce("NaN propagation", wl.name)
+def test_nan_stays_where_defined(wl, route, n0, c0, t0, poison):
+    announce("non-finite propagation", wl.name, poison)
     assert library_route(wl) == route
     inp = make_inputs(wl, 21)
     clean = run_library(wl, inp).cpu()
     bad = dict(inp)
     bad["x"] = inp["x"].clone()
-    bad["x"][n0, c0, t0] = float("nan")
+    bad["x"][n0, c0, t0] = poison
     got = run_library(wl, bad).cpu()
     mask = expected_nan(wl, got.shape[2], n0, t0)
     assert mask.any()
     assert torch.isfinite(clean).all()
-    assert np.array_equal(torch.isnan(got).numpy(), mask)
+    assert np.array_equal(~torch.isfinite(got).numpy(), mask)
     m = torch.from_numpy(mask)
     assert torch.equal(got[~m], clean[~m])
     # the oracle on the poisoned sample: the same NaN elements, the same
     # finite values within tolerance
     ref = run_oracle(wl, bad, n_slice=slice(n0, n0 + 1))["out"]
-    assert np.array_equal(np.isnan(ref), mask[n0:n0 + 1])
+    assert np.array_equal(~np.isfinite(ref), mask[n0:n0 + 1])
+    g = got[n0:n0 + 1].double().numpy()
+    for kind in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(kind(g), kind(ref)), kind.__name__
     ok = ~mask[n0:n0 + 1]
     if ok.any():
         err = float(np.abs(got[n0:n0 + 1].double().numpy()[ok] - ref[ok]).max())
