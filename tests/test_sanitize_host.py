@@ -39,8 +39,9 @@ def test_host_code_under_sanitizers(tmp_path):
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, srcs + [os.path.join(HERE, "sanitize_host.cpp")]))
     exe = str(tmp_path / "sanitize_host")
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-fsanitize=address,undefined",
-                        "-fno-gpu-sanitize"] + objs + ["-o", exe], capture_output=True, text=True)
+    # the link takes the host runtimes only (no device code is instrumented)
+    link = [HIPCC, "--offload-arch=gfx950", "-fno-gpu-sanitize", "-fsanitize=address,undefined"]
+    r = subprocess.run(link + objs + ["-o", exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
     r = subprocess.run([exe, "200000"], capture_output=True, text=True, env=env, timeout=600)
