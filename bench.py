@@ -28,6 +28,10 @@ Other modes (used by the profiling runs recorded under profiles/):
     --mode copy     a plain device-to-device copy of known size, to scale the
                     FETCH_SIZE / WRITE_SIZE counters to bytes
     --mode passes   only the standalone HBM-bound passes
+    --mode generality
+                    the full-scale cases beyond the pages' problems (stride 2
+                    and 3, eight taps at dilation 2, wide and non-tiling
+                    groups, channels-last input, fp32 with stride 2)
 """
 from __future__ import annotations
 
@@ -197,13 +201,15 @@ def prepared(wl, persistent=True, one_launch=False):
     from conv1d_implicit_gemm_amd.workloads import make_inputs
     inp = make_inputs(wl, 0)
     d = {k: (v.to("cuda:0").contiguous() if v is not None else None) for k, v in inp.items()}
+    if wl.channels_last:  # the same values, laid out [N, T, C_in]
+        d["x"] = d["x"].transpose(1, 2).contiguous()
     op = c1g.PreparedConv1dGN(d["x"], d["w"], d["bias"], stride=wl.stride,
                               dilation=wl.dilation, pad_left=wl.pad_left,
                               pad_right=wl.pad_right, norm=wl.norm, groups=wl.G, eps=wl.eps,
                               gamma=d["gamma"], beta=d["beta"], rowmin_bias=d["bias2"],
                               out_dtype=torch.bfloat16 if wl.out_dtype == "bf16"
                               else torch.float32, persistent=persistent,
-                              one_launch=one_launch)
+                              one_launch=one_launch, channels_last=wl.channels_last)
     return inp, op
 
 
@@ -222,6 +228,37 @@ def measure(wl, op, timer, steps, warmup):
             "tflops": tf(med), "tflops_warm": tf(warm), "bound": bound, "peak": peak,
             "unit": unit, "frac": tf(med) / peak, "frac_warm": tf(warm) / peak,
             "algo_bytes": algo_bytes}
+
+
+def config_entry(wl, op, m):
+    """One workload's figures as they appear under ``configs`` and ``generality``."""
+    return {"route": op.route, "dtype": wl.dtype, "out_dtype": wl.out_dtype,
+            "ms_median": round(m["ms_median"], 5), "ms_min": round(m["ms_min"], 5),
+            "ms_warm": round(m["ms_warm"], 5), "tflops": round(m["tflops"], 2),
+            "tflops_warm": round(m["tflops_warm"], 2), "peak": m["peak"],
+            "frac": round(m["frac"], 4), "frac_warm": round(m["frac_warm"], 4),
+            "algorithmic_flops": m["flops"]}
+
+
+def generality(timer, steps, warmup):
+    """The full-scale cases beyond the pages' problems (stride 2 and 3, eight
+    taps at dilation 2, groups spanning or not tiling the channel tiles,
+    channels-last input, fp32 with stride 2), each step timed like the
+    configurations, against its input type's MFMA peak."""
+    import torch
+    from conv1d_implicit_gemm_amd.workloads import GENERALITY, WORKLOADS
+    res = {}
+    for name in GENERALITY:
+        wl = WORKLOADS[name]
+        _, op = prepared(wl)
+        res[name] = config_entry(wl, op, measure(wl, op, timer, steps, warmup))
+        res[name]["shape"] = {k: getattr(wl, k) for k in (
+            "N", "C_in", "C_out", "T", "K", "stride", "dilation", "pad_left", "pad_right",
+            "norm", "G", "channels_last")}
+        res[name]["shape"]["T_out"] = op.T_out
+        del op
+        torch.cuda.empty_cache()
+    return res
 
 
 def config_of(wl, op):
@@ -312,7 +349,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     help="time this workload alone (no configs, passes or CPU baseline)")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "passes"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "passes", "generality"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
                     help="element type of the output (bf16: rounded to nearest even)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -341,6 +378,10 @@ def main():
     if args.mode == "passes":
         print(json.dumps({"mode": "passes", "steps": steps,
                           "passes": passes(timer, steps, args.warmup)}), flush=True)
+        return
+    if args.mode == "generality":
+        print(json.dumps({"mode": "generality", "steps": steps, "warmup": args.warmup,
+                          "generality": generality(timer, steps, args.warmup)}), flush=True)
         return
 
     name = args.workload or HEADLINE
@@ -385,15 +426,7 @@ def main():
             if variant == "out_bf16":
                 cwl = cwl.replace(out_dtype="bf16")
             _, cop = prepared(cwl)
-            cm = measure(cwl, cop, timer, steps, args.warmup)
-            cfgs[cname] = {"route": cop.route, "dtype": cwl.dtype, "out_dtype": cwl.out_dtype,
-                           "ms_median": round(cm["ms_median"], 5),
-                           "ms_min": round(cm["ms_min"], 5), "ms_warm": round(cm["ms_warm"], 5),
-                           "tflops": round(cm["tflops"], 2),
-                           "tflops_warm": round(cm["tflops_warm"], 2),
-                           "peak": cm["peak"], "frac": round(cm["frac"], 4),
-                           "frac_warm": round(cm["frac_warm"], 4),
-                           "algorithmic_flops": cm["flops"]}
+            cfgs[cname] = config_entry(cwl, cop, measure(cwl, cop, timer, steps, args.warmup))
             del cop
             torch.cuda.empty_cache()
         res["configs"] = cfgs

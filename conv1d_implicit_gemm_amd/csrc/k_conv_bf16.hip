@@ -27,10 +27,13 @@
 // write whole 1 KB runs, so a lane fetches the logical column that lands at
 // its physical slot.
 //
-// Workgroup: 512 threads; tile TM (512 or 128) positions x 128 channels.  The
-// eight waves form a 4 x 2 grid of wave tiles of WM x 4 MFMA tiles (128 x 64
-// for TM = 512), each running every tap, so a wave reads 12 KB of operands per
-// 32 MFMAs.  Two LDS stages, one barrier per chunk: the next chunk's copies
+// Workgroup: 512 threads; tile TM (512, 256 or 128) positions x 128
+// channels.  The eight waves form a 4 x 2 grid of wave tiles of WM x 4 MFMA
+// tiles (128 x 64 for TM = 512, 64 x 64 for 256, 32 x 64 for 128), each
+// running every tap, so a wave reads 12 KB of operands per 32 MFMAs at
+// TM = 512 (8 KB per 16 at 256, 6 KB per 8 at 128).  The largest tile whose
+// input window fits the LDS is used: the window of TM positions spans
+// (TM - 1) * stride + (K - 1) * dilation + 1 input rows.  Two LDS stages, one barrier per chunk: the next chunk's copies
 // run while the current chunk is consumed, issued in groups behind its first
 // tap steps.  Within a chunk a wave reads each
 // tap's fragments while the previous tap's MFMAs run (a fragment register is
@@ -57,11 +60,16 @@ constexpr int WGM = 4;               // waves along t
 constexpr int NWAVE = WGM * WGN;
 constexpr int NTHR = NWAVE * 64;
 // LDS per workgroup: two stages of (window XR rows + weight image of the
-// taps) of 64-byte rows.  XR = 544 rows with up to 5 taps (150 KB), or 224
-// rows with 6 to 8 taps on 128-position tiles (156 KB); gfx950 allows 160 KB.
+// taps) of 64-byte rows.  XR = 544 rows with up to 5 taps (150 KB); on
+// 256-position tiles 496 rows with 6 taps or 368 with 7 (158 KB each); on
+// 128-position tiles 224 rows with 6 to 8 taps (156 KB); gfx950 allows 160 KB.
 // A window of XR rows is 16-row copies (1 KB each).
-constexpr int XCAP_WIDE = 544, XCAP_TAPS = 224;
-static_assert(XCAP_WIDE % 16 == 0 && XCAP_TAPS % 16 == 0, "whole 16-row copies");
+constexpr int XCAP_WIDE = 544, XCAP_T6 = 496, XCAP_T7 = 368, XCAP_TAPS = 224;
+static_assert(XCAP_WIDE % 16 == 0 && XCAP_T6 % 16 == 0 && XCAP_T7 % 16 == 0 &&
+                  XCAP_TAPS % 16 == 0, "whole 16-row copies");
+static_assert(2 * (XCAP_T6 + 6 * 128) * 64 <= 160 * 1024 - 2048 &&
+                  2 * (XCAP_T7 + 7 * 128) * 64 <= 160 * 1024 - 2048,
+              "two stages fit the LDS");
 static_assert(TN == 128, "weight rows keep bit 2 of c across taps");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -757,6 +765,13 @@ hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = fals
     case 5: return launch_wk<WM, 5, XCAP_WIDE>(a, epi, st, coop);
     default: break;
   }
+  if (WM == 4) {
+    switch (a.K) {
+      case 6: return launch_wk<4, 6, XCAP_T6>(a, epi, st, coop);
+      case 7: return launch_wk<4, 7, XCAP_T7>(a, epi, st, coop);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (WM != 2) return hipErrorInvalidValue;
   switch (a.K) {
     case 6: return launch_wk<2, 6, XCAP_TAPS>(a, epi, st, coop);
@@ -771,14 +786,21 @@ int64_t window(int tm, int stride, int K, int dilation) {
   return (int64_t)(tm - 1) * stride + (int64_t)(K - 1) * dilation + 1;
 }
 
-int xcap_of(int tm, int K) { return (tm == 128 && K > 5) ? XCAP_TAPS : XCAP_WIDE; }
+// window rows a tile of tm positions and K taps can stage (0: no such kernel)
+int xcap_of(int tm, int K) {
+  if (K < 1 || K > KMAX) return 0;
+  if (K <= 5) return XCAP_WIDE;
+  if (tm == 256) return K == 6 ? XCAP_T6 : K == 7 ? XCAP_T7 : 0;
+  return tm == 128 ? XCAP_TAPS : 0;
+}
 
 }  // namespace
 
 int conv_bf16_tile_m(int stride, int K, int dilation) {
-  if (K < 1 || K > KMAX) return 0;
-  if (K <= 5 && window(512, stride, K, dilation) <= XCAP_WIDE) return 512;
-  if (window(128, stride, K, dilation) <= (K <= 5 ? XCAP_WIDE : XCAP_TAPS)) return 128;
+  for (int tm : {512, 256, 128}) {
+    const int cap = xcap_of(tm, K);
+    if (cap > 0 && window(tm, stride, K, dilation) <= cap) return tm;
+  }
   return 0;
 }
 
@@ -849,6 +871,7 @@ hipError_t conv_bf16_pack_x(const uint16_t* x, uint16_t* ximg, int64_t N, int64_
 hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
   if (tm == 512) return launch_w<8>(a, epi, s);  // wave tiles 128 x 64
+  if (tm == 256) return launch_w<4>(a, epi, s);  // wave tiles 64 x 64
   if (tm == 128) return launch_w<2>(a, epi, s);  // wave tiles 32 x 64
   return hipErrorInvalidValue;
 }
@@ -870,6 +893,13 @@ int capacity_w(int K) {
     case 5: return capacity_wk<WM, 5, XCAP_WIDE>();
     default: break;
   }
+  if (WM == 4) {
+    switch (K) {
+      case 6: return capacity_wk<4, 6, XCAP_T6>();
+      case 7: return capacity_wk<4, 7, XCAP_T7>();
+      default: return 0;
+    }
+  }
   if (WM != 2) return 0;
   switch (K) {
     case 6: return capacity_wk<2, 6, XCAP_TAPS>();
@@ -890,6 +920,7 @@ int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctil
 int conv_bf16_fused_capacity(int stride, int K, int dilation) {
   const int tm = conv_bf16_tile_m(stride, K, dilation);
   if (tm == 512) return capacity_w<8>(K);
+  if (tm == 256) return capacity_w<4>(K);
   if (tm == 128) return capacity_w<2>(K);
   return 0;
 }
@@ -921,7 +952,9 @@ hipError_t conv_bf16_fused_launch(ConvArgs a, int epi, bool cooperative, hipStre
   a.fault = a.sync + (words - 1);
   a.polls = barrier_poll_limit();
   const int tm = conv_bf16_tile_m(a.stride, a.K, a.dilation);
-  return tm == 512 ? launch_w<8>(a, epi, s, cooperative) : launch_w<2>(a, epi, s, cooperative);
+  if (tm == 512) return launch_w<8>(a, epi, s, cooperative);
+  if (tm == 256) return launch_w<4>(a, epi, s, cooperative);
+  return launch_w<2>(a, epi, s, cooperative);
 }
 
 }  // namespace c1g

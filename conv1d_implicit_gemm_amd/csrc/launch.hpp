@@ -73,7 +73,7 @@ hipError_t conv_f32_pack(const float* w, float* wp, int64_t C_in, int64_t C_out,
 hipError_t conv_f32_launch(const ConvArgs& a, int epi, hipStream_t s);
 
 // ---- bf16 split-path convolution (k_conv_bf16.hip)
-// Tile: TM (512 or 128, chosen from stride/K/dilation) positions x TN
+// Tile: TM (512, 256 or 128, chosen from stride/K/dilation) positions x TN
 // channels, CK input channels per chunk; taps K <= 8.
 struct ConvBf16Cfg {
   static constexpr int TN = 128, CK = 32;

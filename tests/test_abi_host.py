@@ -446,3 +446,35 @@ def test_launch_failure_is_reported_as_hip_error():
     assert lib.gn_stats(2, 32, 256, 8, 1e-5, f, f, f, f, 1 << 30, None) == 5
     assert lib.gn_apply(2, 32, 256, 8, f, f, f, None, None, f, None) == 5
     assert lib.gn_apply_bf16(2, 32, 256, 8, f, f, f, None, None, f, None) == 5
+
+
+@pytest.mark.parametrize("K,stride,dilation,pad,T,tiles_t", [
+    (5, 1, 2, (2, 2), 4096, 8),    # 512-position tiles: 4092 outputs
+    (5, 2, 1, (2, 2), 8192, 16),   # stride 2: the 1027-row window of 512 positions does
+                                   # not fit, 256 positions (515 rows) do
+    (6, 1, 1, (5, 0), 4096, 16),   # six taps: 256 positions within 496 rows
+    (7, 1, 2, (12, 0), 4096, 16),  # seven taps: 256 positions within 368 rows
+    (8, 1, 2, (7, 7), 4096, 32),   # eight taps: 128 positions
+    (4, 3, 1, (3, 0), 6000, 16),   # stride 3: 128 positions (385 rows); 2000 outputs
+])
+def test_bf16_tile_choice(K, stride, dilation, pad, T, tiles_t):
+    """The bf16 conv takes the largest tile (512, 256 or 128 positions) whose
+    input window fits the LDS; the log's plan shows its position tiles.
+    (Null pointers: the call is refused after planning.)"""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import conv1d_implicit_gemm_amd as c1g
+lib = c1g.load_library()
+d = c1g.ConvDesc(4, 256, 1024, %d, %d, %d, %d, %d, %d, c1g.C1G_BF16, 0, 0)
+nd = c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0)
+print(lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(nd), *([None] * 10), 0, None))
+""" % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))), T, K, stride, dilation,
+       pad[0], pad[1])
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       env=dict(os.environ, C1G_LOG="1"), timeout=120)
+    assert r.returncode == 0 and r.stdout.split() == ["1"], r.stderr
+    line = [l for l in r.stderr.splitlines() if l.startswith("c1g: ")][0]
+    assert "| fused_persistent" in line and " tiles=%dx8 " % tiles_t in line, line

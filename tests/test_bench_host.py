@@ -96,3 +96,14 @@ def test_cpu_baseline_fields():
     st = cb["single_thread"]
     assert st["cores"] == 1 and st["value"] > 0
     assert oracle.num_threads() == cb["cores"]  # the thread count is restored
+
+
+def test_generality_workloads_plan_their_routes():
+    """The full-scale cases bench.py --mode generality times take the routes
+    their parity test expects (host planner only)."""
+    from conv1d_implicit_gemm_amd.workloads import GENERALITY
+    from tests.sweep_cases import route_of
+    from tests.test_gpu_bf16 import SCALE_ROUTES
+    assert tuple(SCALE_ROUTES) == GENERALITY
+    for name in GENERALITY:
+        assert route_of(WORKLOADS[name]) == SCALE_ROUTES[name], name

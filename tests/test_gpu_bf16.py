@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import conv1d_implicit_gemm_amd as c1g
-from conv1d_implicit_gemm_amd.workloads import WORKLOADS, Workload, make_inputs
+from conv1d_implicit_gemm_amd.workloads import GENERALITY, WORKLOADS, Workload, make_inputs
 from tests.gpu_util import (TOL_BF16, announce, check_parity, max_abs_err, run_library,
                             run_oracle)
 
@@ -243,22 +243,17 @@ def test_persistent_determinism():
 
 # Generality at scale: stride > 1, 8 taps at dilation 2, groups wider than 32
 # channels (one group spanning channel tiles; a width that does not tile the
-# 128-channel tiles, hence the split route), channels-last input; the oracle
-# checks the first and the last sample of each.
-SCALE_CASES = [
-    (W("scale_bf16_stride2_gn", N=12, C_in=512, C_out=1024, T=8192, K=5, stride=2, pad_left=2,
-       pad_right=2, G=32, **BF), "fused_persistent"),
-    (W("scale_bf16_k8d2_gn", N=8, C_in=256, C_out=512, T=4096, K=8, dilation=2, pad_left=7,
-       pad_right=7, G=16, **BF), "fused_persistent"),
-    (W("scale_bf16_cpg256_gn", N=8, C_in=512, C_out=1024, T=4096, K=5, dilation=2, pad_left=4,
-       pad_right=4, G=4, **BF), "fused_persistent"),
-    (W("scale_bf16_cpg48_gn_split", N=6, C_in=256, C_out=1536, T=4096, K=3, pad_left=1,
-       pad_right=1, G=32, **BF), "split"),
-    (W("scale_bf16_stride3_ln_nlc", N=6, C_in=384, C_out=768, T=6000, K=4, stride=3,
-       pad_left=3, norm="layer_channels", channels_last=True, **BF), "fused_persistent"),
-    (W("scale_f32_stride2_gn", N=6, C_in=256, C_out=256, T=8192, K=4, stride=2, pad_left=3,
-       G=32), "split"),
-]
+# 128-channel tiles, hence the split route), channels-last input; the same
+# workloads bench.py --mode generality times.  The oracle checks the first and
+# the last sample of each.
+SCALE_ROUTES = {"conv1d_gn_bf16_n32_c512x1024_t8192_k5s2": "fused_persistent",
+                "conv1d_gn_bf16_n32_c256x512_t4096_k8d2": "fused_persistent",
+                "conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4": "fused_persistent",
+                "conv1d_gn_bf16_n16_c256x1536_t4096_k3_g32": "split",
+                "conv1d_lnc_bf16_nlc_n30_c384x768_t6000_k4s3": "fused_persistent",
+                "conv1d_gn_f32_n16_c256x256_t8192_k4s2": "split"}
+assert set(SCALE_ROUTES) == set(GENERALITY)
+SCALE_CASES = [(WORKLOADS[n], SCALE_ROUTES[n]) for n in GENERALITY]
 
 
 @pytest.mark.parametrize("wl,route", SCALE_CASES, ids=lambda c: getattr(c, "name", c))
