@@ -193,14 +193,11 @@ Plan make_plan(const c1g_conv_desc* d, const c1g_norm_desc* nd) {
     return refuse(p, C1G_ERR_UNSUPPORTED, "too many tiles for the grid");
   p.n_ttiles = (int)n_tt;
   p.n_ctiles = (int)n_ct;
-  // bf16 GroupNorm (groups that tile the 128-channel tiles) or channel
-  // LayerNorm without the row-min: normalise inside the persistent conv
+  // bf16 GroupNorm or channel LayerNorm without the row-min: normalise
+  // inside the persistent conv
   if (p.bf16 && (want_gn || want_ln) && p.epi == C1G_EPI_NONE &&
-      !(nd->flags & C1G_FLAG_NO_PERSISTENT) && !force_split() && n_tt * n_ct <= kResidentTiles) {
-    const int64_t tn = ConvBf16Cfg::TN;
-    const int64_t cpg = want_gn ? d->C_out / nd->G : tn;
-    if (tn % cpg == 0 || cpg % tn == 0) p.route = R_PERSIST;
-  }
+      !(nd->flags & C1G_FLAG_NO_PERSISTENT) && !force_split() && n_tt * n_ct <= kResidentTiles)
+    p.route = R_PERSIST;
 
   size_t off = xt_bytes;
   p.off_pack = off;

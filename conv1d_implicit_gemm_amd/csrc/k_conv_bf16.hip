@@ -115,6 +115,14 @@ __device__ __forceinline__ const ConvArgs& round_args() {
   return *(const ConvArgs*)p;
 }
 
+// Channels per GroupNorm partial of the persistent kernel: the largest power
+// of two dividing the group width cpg, at most 64 (so it divides the
+// 128-channel tile too)
+__host__ __device__ __forceinline__ int gn_partial_width(int cpg) {
+  const int low = cpg & -cpg;
+  return low < 64 ? low : 64;
+}
+
 // Sum over aligned groups of w lanes (w a power of two up to 64, uniform)
 __device__ __forceinline__ float group_lane_sum(float v, int w) {
   switch (w) {
@@ -134,8 +142,10 @@ __device__ __forceinline__ float group_lane_sum(float v, int w) {
 // affine in registers and write the output once.  Every workgroup that needs
 // a group's statistics merges the same partials in the same order.
 //
-// GroupNorm partials: one (mean, M2) per chunk of pg = min(C_out/G, 64)
-// channels of a group per position tile, at part[((n * C_out/pg + chunk) *
+// GroupNorm partials: one (mean, M2) per chunk of pg channels of a group per
+// position tile, pg the largest power of two dividing C_out/G, at most 64 (so
+// a chunk never straddles a group or a 128-channel tile), at
+// part[((n * C_out/pg + chunk) *
 // n_ttiles + ttile) * 2], so a group's partials are one contiguous run.  Every
 // channel of a tile has the same count (the tile's valid positions), so the
 // chunk's mean is the mean of its channel means and its M2 the sum of the
@@ -160,7 +170,7 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
   const int64_t T_out = a.T_out;
   constexpr bool gn = EPI == EPI_GN_FUSED;
   const int cpg = gn ? (int)(a.C_out / a.G) : 0;
-  const int pg = cpg < 64 ? cpg : 64;  // channels per GroupNorm partial
+  const int pg = gn_partial_width(cpg);  // channels per GroupNorm partial
   if constexpr (gn) {
     float bias[WN];
 #pragma unroll
@@ -197,10 +207,16 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
   // hence a NaN output, never a plausible wrong one.
   int nsub, sub, expect;
   if constexpr (gn) {
-    const int cpt = cpg > TN ? cpg / TN : 1;  // channel tiles per group
-    nsub = a.n_ctiles / cpt;
-    sub = ctile / cpt;
-    expect = a.n_ttiles * cpt;
+    if (TN % cpg == 0 || cpg % TN == 0) {
+      const int cpt = cpg > TN ? cpg / TN : 1;  // channel tiles per group
+      nsub = a.n_ctiles / cpt;
+      sub = ctile / cpt;
+      expect = a.n_ttiles * cpt;
+    } else {  // groups straddle channel tiles: the whole sample
+      nsub = 1;
+      sub = 0;
+      expect = a.n_ttiles * a.n_ctiles;
+    }
   } else {
     nsub = a.n_ttiles;
     sub = ttile;
@@ -216,16 +232,19 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
   float* mean_s = lds;        // merged statistics of this tile
   float* rstd_s = lds + 512;
   if constexpr (gn) {
-    // ng groups in this tile (cpg divides TN, or TN divides cpg: then the
-    // whole tile is one group), P partials per group, S lanes of one wave per
+    // ng groups meet this tile (the first, g0, may have begun in an earlier
+    // channel tile and the last may go on in a later one), P partials per
+    // group, S lanes of one wave per
     // group (a power of two): lane u folds partials u, u + S, ... in order,
     // then a fixed tree over the S lanes (lane u takes lane u + h)
-    const int ng = cpg >= TN ? 1 : TN / cpg;
+    const int64_t cend = c0 + TN < a.C_out ? c0 + TN : a.C_out;
+    const int g0 = c0 / cpg;
+    const int ng = (int)((cend - 1) / cpg) - g0 + 1;
     const int P = (cpg / pg) * a.n_ttiles;
     int S = 1;
     while (S < P && S < 64 && 2 * S * ng <= NTHR) S *= 2;
     const int k = tid / S, u = tid - k * S;
-    const int64_t g = (int64_t)(c0 / cpg) + k;
+    const int64_t g = (int64_t)g0 + k;
     Stats st = {0.f, 0.f, 0.f};
     if (k < ng && g < a.G) {
       const float* base = a.part + ((n * (a.C_out / pg) + g * (cpg / pg)) * a.n_ttiles) * 2;
@@ -299,7 +318,7 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
     const int cpg = (int)(a.C_out / a.G);
 #pragma unroll
     for (int jn = 0; jn < WN; ++jn) {
-      const int k = (wn * WN * 16 + jn * 16 + lr) / cpg;
+      const int k = (c0 + wn * WN * 16 + jn * 16 + lr) / cpg - c0 / cpg;
       const float mu = mean_s[k], sc = rstd_s[k] * ga[jn], b = be[jn];
 #pragma unroll
       for (int i = 0; i < WM; ++i)
@@ -913,6 +932,7 @@ int capacity_w(int K) {
 int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctiles) {
   if (epi == EPI_LN_FUSED) return n_ttiles;
   const int64_t cpg = C_out / G;
+  if (TN % cpg != 0 && cpg % TN != 0) return 1;  // groups straddle tiles: per sample
   const int64_t cpt = cpg > TN ? cpg / TN : 1;
   return (int)(n_ctiles / cpt);
 }

@@ -296,8 +296,7 @@ int conv1d_gn_forward_noalloc(const c1g_conv_desc* d, const c1g_norm_desc* norm,
  *                        its rows' partial minima, waits for the other channel
  *                        tiles of those rows and writes its block of the
  *                        broadcast output (same result, bit for bit)
- *   "fused_persistent"   bf16, GroupNorm whose groups tile the 128-channel tiles
- *                        (C_out/G divides 128 or 128 divides it) or LayerNorm
+ *   "fused_persistent"   bf16, GroupNorm (any G) or LayerNorm
  *                        over channels, no epilogue, at most 256 tiles per
  *                        sample, flags without C1G_FLAG_NO_PERSISTENT: one
  *                        launch (C1G_FLAG_COOPERATIVE: cooperative) in rounds

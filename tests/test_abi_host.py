@@ -140,10 +140,10 @@ def test_routes():
     no_p = c1g.FLAG_NO_PERSISTENT
     assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 0, no_p)) == "split"
     assert c1g.route(conv, c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0, no_p)) == "split"
-    # groups that straddle the 128-channel tiles (C_out/G = 48), the row-min
-    # epilogue, or more than 256 tiles per sample: split
+    # groups that straddle the 128-channel tiles (C_out/G = 48) stay
+    # persistent; the row-min epilogue, or more than 256 tiles per sample: split
     assert c1g.route(_desc(C_in=64, C_out=192, T=512, dtype=bf),
-                     c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0)) == "split"
+                     c1g.NormDesc(c1g.NORM_GROUP, 4, 1e-5, 0)) == "fused_persistent"
     assert c1g.route(conv, c1g.NormDesc(c1g.NORM_GROUP, 32, 1e-5, 1)) == "split"
     assert c1g.route(_desc(C_in=64, C_out=1024, T=140000, dtype=bf),
                      c1g.NormDesc(c1g.NORM_LAYER_CHANNELS, 0, 1e-5, 0)) == "split"

@@ -187,6 +187,22 @@ PERSIST_CASES = [
       norm="layer_channels", **BF),
     W("persist_gn_bf16_out", N=6, C_in=64, C_out=256, T=1100, K=5, dilation=2, pad_left=4,
       pad_right=4, G=16, out_dtype="bf16", **BF),
+    # groups that straddle the 128-channel tiles: the whole sample waits, and
+    # partials cover the largest power of two dividing the group width (<= 64)
+    W("persist_gn_cpg48", N=3, C_in=40, C_out=192, T=1300, K=5, dilation=2, pad_left=4,
+      pad_right=4, G=4, **BF),
+    W("persist_gn_cpg24_ragged", N=4, C_in=33, C_out=240, T=700, K=3, pad_left=1,
+      pad_right=1, G=10, **BF),
+    W("persist_gn_cpg3", N=2, C_in=24, C_out=300, T=555, K=3, pad_left=1, pad_right=1, G=100,
+      **BF),
+    W("persist_gn_cpg96_stride2", N=3, C_in=64, C_out=384, T=1201, K=5, stride=2, pad_left=2,
+      pad_right=2, G=4, **BF),
+    W("persist_gn_cpg192", N=2, C_in=40, C_out=576, T=900, K=3, pad_left=1, pad_right=1, G=3,
+      **BF),
+    W("persist_gn_cpg80_k8_bf16out", N=3, C_in=48, C_out=160, T=450, K=8, pad_left=7, G=2,
+      out_dtype="bf16", **BF),
+    W("persist_gn_cpg48_k6", N=2, C_in=40, C_out=240, T=800, K=6, dilation=2, pad_left=10,
+      G=5, **BF),
 ]
 
 
@@ -242,14 +258,14 @@ def test_persistent_determinism():
 
 
 # Generality at scale: stride > 1, 8 taps at dilation 2, groups wider than 32
-# channels (one group spanning channel tiles; a width that does not tile the
-# 128-channel tiles, hence the split route), channels-last input; the same
+# channels (one group spanning channel tiles; groups of 48 that straddle the
+# 128-channel tiles), channels-last input; the same
 # workloads bench.py --mode generality times.  The oracle checks the first and
 # the last sample of each.
 SCALE_ROUTES = {"conv1d_gn_bf16_n32_c512x1024_t8192_k5s2": "fused_persistent",
                 "conv1d_gn_bf16_n32_c256x512_t4096_k8d2": "fused_persistent",
                 "conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4": "fused_persistent",
-                "conv1d_gn_bf16_n16_c256x1536_t4096_k3_g32": "split",
+                "conv1d_gn_bf16_n16_c256x1536_t4096_k3_g32": "fused_persistent",
                 "conv1d_lnc_bf16_nlc_n30_c384x768_t6000_k4s3": "fused_persistent",
                 "conv1d_gn_f32_n16_c256x256_t8192_k4s2": "split"}
 assert set(SCALE_ROUTES) == set(GENERALITY)

@@ -20,7 +20,9 @@ CASES = [
     # bf16 inputs, split route: T_out % 8 == 4 (last unit of the vector apply),
     # then T_out % 4 != 0 (element-wise apply)
     (W("bf16o_conv_gn_k5d2", N=2, C_in=72, C_out=160, T=1300, K=5, dilation=2, pad_left=2,
-       pad_right=2, G=8, dtype="bf16", **BO), "split"),
+       pad_right=2, G=8, dtype="bf16", persistent=False, **BO), "split"),
+    (W("bf16o_conv_gn_k5d2_persistent", N=2, C_in=72, C_out=160, T=1300, K=5, dilation=2,
+       pad_left=2, pad_right=2, G=8, dtype="bf16", **BO), "fused_persistent"),
     (W("bf16o_conv_gn_odd_T", N=2, C_in=40, C_out=64, T=203, K=3, pad_left=1, pad_right=1,
        G=4, dtype="bf16", **BO), "fused_persistent"),
     (W("bf16o_conv_gn_odd_T_split", N=2, C_in=40, C_out=64, T=203, K=3, pad_left=1,

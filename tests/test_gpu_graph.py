@@ -24,7 +24,7 @@ CASES = [
     (Workload("graph_split_fp32_rowmin", N=2, C_in=24, C_out=48, T=200, K=4, pad_left=3, G=6,
               rowmin_bias=True), "split"),
     (Workload("graph_split_bf16_gn", N=3, C_in=72, C_out=160, T=1300, K=5, dilation=2,
-              pad_left=2, pad_right=2, G=8, **BF), "split"),
+              pad_left=2, pad_right=2, G=8, persistent=False, **BF), "split"),
     (Workload("graph_persistent_bf16_gn", N=3, C_in=72, C_out=256, T=1300, K=5, dilation=2,
               pad_left=2, pad_right=2, G=16, **BF), "fused_persistent"),
     (Workload("graph_persistent_bf16_ln", N=2, C_in=40, C_out=272, T=700, K=5, dilation=2,
@@ -65,7 +65,7 @@ def test_graph_replays_match_eager(wl, route):
         op = c1g.PreparedConv1dGN(x, w, b, stride=wl.stride, dilation=wl.dilation,
                                   pad_left=wl.pad_left, pad_right=wl.pad_right, norm=wl.norm,
                                   groups=wl.G, eps=wl.eps, gamma=ga, beta=be, rowmin_bias=b2,
-                                  one_launch=wl.one_launch)
+                                  persistent=wl.persistent, one_launch=wl.one_launch)
         assert op.route == route
         for _ in range(2):
             op()
