@@ -50,7 +50,12 @@
  *     C_out up to 2^30, T up to 2^40, x and w below 2^46 elements each and
  *     N*C_out*T_out below 2^32 (C1G_ERR_UNSUPPORTED beyond); every size check
  *     is made without a product that could wrap, so no oversized argument is
- *     accepted as a small one.
+ *     accepted as a small one.  Taps K up to 8, and the input window of a
+ *     tile of TM output positions, (TM - 1)*stride + (K - 1)*dilation + 1
+ *     rows, must fit on chip: bf16 at most 544 rows at TM = 128 for K <= 5,
+ *     224 for K = 6..8 (larger tiles are used whenever theirs fit); fp32 at
+ *     most 541 on the split path.  c1g_check reports whether a shape is
+ *     built.
  *   - Environment variables (read at each call; none is needed):
  *       C1G_LOG=1             every entry-point call writes one line to stderr:
  *                             its sizes, the plan (route, tiles, workspace),
