@@ -344,8 +344,10 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
 }
 
 // FUSE: 0 (one tile per workgroup, epilogue epi), or EPI_GN_FUSED /
-// EPI_LN_FUSED (persistent rounds of whole samples, normalised output)
-template <int WM, int KT, int XR, int FUSE>
+// EPI_LN_FUSED (persistent rounds of whole samples, normalised output).
+// NP: passes over the chunks (K = NP * KT taps; 2 for eight taps on
+// 512-position tiles, whose window and weights for all eight do not fit).
+template <int WM, int KT, int XR, int FUSE, int NP = 1>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const ConvArgs& a = a_;
   // the weight stage also holds the epilogue's cross-wave merge (<= 12 KB)
@@ -401,8 +403,12 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // piece, writing the same bytes again).
   const int64_t row_bytes = (int64_t)a.n_chunks * CK * 2;  // one image row
   const char* const xwin = (const char*)a.ximg + (n * a.T_img + t0 * s) * row_bytes;
-  const char* const wimg =
-      (const char*)a.wp + (int64_t)ctile * a.n_chunks * (KT * TN * RW * 2);
+  // NP passes over the chunks, pass p with taps p*KT .. p*KT + KT - 1: its
+  // window starts p*KT*d rows further down the image and its weights are
+  // those taps of each (c-tile, chunk) block
+  static_assert(NP == 1 || NP == 2, "one or two passes");
+  constexpr int64_t wblk = (int64_t)NP * KT * (TN * RW * 2);  // bytes of a (c-tile, chunk) block
+  const char* const wimg = (const char*)a.wp + (int64_t)ctile * a.n_chunks * wblk;
   // A copy's source offset is a wave-uniform part (its piece) plus one of two
   // lane offsets: window row 16 * piece + lane / 4 at logical column
   // (lane % 4) ^ swz(row) (the column landing at slot lane % 4; swz of the
@@ -410,16 +416,21 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const uint32_t lane_x =
       (uint32_t)((lane >> 2) * row_bytes + 16 * ((lane & 3) ^ swz(lane >> 2)));
   const uint32_t lane_w = (uint32_t)(16 * lane);
-  auto copy_from = [&](const char* xw, int p, int chunk, u16* xs, u16* ws)
+  // q: pass * n_chunks + chunk
+  auto copy_from = [&](const char* xw, int p, int q, u16* xs, u16* ws)
       __attribute__((always_inline)) {
     int piece = wave + NWAVE * p;
     if (piece >= NPIECE) piece = NPIECE - 1;
+    const int pass = NP == 2 && q >= a.n_chunks ? 1 : 0;
+    const int chunk = q - pass * a.n_chunks;
     if (piece < XP)
-      dma16(xw + (int64_t)chunk * (CK * 2) + (int64_t)16 * piece * row_bytes, lane_x,
-            (char*)xs + piece * 1024);
+      dma16(xw + (int64_t)pass * KT * d * row_bytes + (int64_t)chunk * (CK * 2) +
+                (int64_t)16 * piece * row_bytes,
+            lane_x, (char*)xs + piece * 1024);
     else
-      dma16(wimg + (int64_t)chunk * (KT * TN * RW * 2) + (piece - XP) * 1024, lane_w,
-            (char*)ws + (piece - XP) * 1024);
+      dma16(wimg + (int64_t)chunk * wblk + (int64_t)pass * (KT * TN * RW * 2) +
+                (piece - XP) * 1024,
+            lane_w, (char*)ws + (piece - XP) * 1024);
   };
   auto copy = [&](int p, int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
     copy_from(xwin, p, chunk, xs, ws);
@@ -542,7 +553,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // reads again), so the loop body is one block.  Before each barrier every
   // wave waits for all its copies: those of the next chunk, issued one chunk
   // earlier.
-  const int n_chunks = a.n_chunks, last = n_chunks - 1;
+  const int n_chunks = NP * a.n_chunks, last = n_chunks - 1;  // (pass, chunk) steps
   auto cl = [&](int c) { return c < last ? c : last; };
   // the persistent kernel's later rounds find chunk 0 already copied (issued
   // by the previous round while it waited at its barrier)
@@ -756,7 +767,7 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_nlc_kernel(const u16* __
   }
 }
 
-template <int WM, int KT, int XR>
+template <int WM, int KT, int XR, int NP = 1>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = false) {
   if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
     // one round: spr whole samples, every workgroup resident at once
@@ -764,13 +775,13 @@ hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = fal
     int ep = epi;
     void* args[] = {(void*)&ac, (void*)&ep};
     const void* k = epi == EPI_GN_FUSED
-                        ? (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>
-                        : (const void*)conv_bf16_kernel<WM, KT, XR, EPI_LN_FUSED>;
+                        ? (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED, NP>
+                        : (const void*)conv_bf16_kernel<WM, KT, XR, EPI_LN_FUSED, NP>;
     return launch_coresident(k, (unsigned)(a.spr * a.n_ttiles * a.n_ctiles), NTHR, args, coop,
                              st);
   }
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
-  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR, 0>), grid, dim3(NTHR), 0, st, a, epi);
+  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR, 0, NP>), grid, dim3(NTHR), 0, st, a, epi);
   return hipGetLastError();
 }
 
@@ -784,6 +795,8 @@ hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = fals
     case 5: return launch_wk<WM, 5, XCAP_WIDE>(a, epi, st, coop);
     default: break;
   }
+  if (WM == 8) return a.K == 8 ? launch_wk<8, 4, XCAP_WIDE, 2>(a, epi, st, coop)  // two passes
+                               : hipErrorInvalidValue;
   if (WM == 4) {
     switch (a.K) {
       case 6: return launch_wk<4, 6, XCAP_T6>(a, epi, st, coop);
@@ -805,11 +818,20 @@ int64_t window(int tm, int stride, int K, int dilation) {
   return (int64_t)(tm - 1) * stride + (int64_t)(K - 1) * dilation + 1;
 }
 
-// window rows a tile of tm positions and K taps can stage (0: no such kernel)
-int xcap_of(int tm, int K) {
+// taps per pass of the kernel for a tile of tm positions and K taps: K (one
+// pass), or 4 for eight taps on 512-position tiles (two passes); 0: none
+int kernel_taps(int tm, int K) {
   if (K < 1 || K > KMAX) return 0;
-  if (K <= 5) return XCAP_WIDE;
-  if (tm == 256) return K == 6 ? XCAP_T6 : K == 7 ? XCAP_T7 : 0;
+  if (K <= 5 || tm == 128) return K;
+  if (tm == 512) return K == 8 ? 4 : 0;
+  return K <= 7 ? K : 0;  // 256
+}
+
+// window rows a tile of tm positions staging kt taps per pass can hold
+int xcap_of(int tm, int kt) {
+  if (kt < 1 || kt > KMAX) return 0;
+  if (kt <= 5) return XCAP_WIDE;
+  if (tm == 256) return kt == 6 ? XCAP_T6 : kt == 7 ? XCAP_T7 : 0;
   return tm == 128 ? XCAP_TAPS : 0;
 }
 
@@ -817,8 +839,8 @@ int xcap_of(int tm, int K) {
 
 int conv_bf16_tile_m(int stride, int K, int dilation) {
   for (int tm : {512, 256, 128}) {
-    const int cap = xcap_of(tm, K);
-    if (cap > 0 && window(tm, stride, K, dilation) <= cap) return tm;
+    const int kt = kernel_taps(tm, K), cap = xcap_of(tm, kt);
+    if (cap > 0 && window(tm, stride, kt, dilation) <= cap) return tm;
   }
   return 0;
 }
@@ -827,8 +849,10 @@ int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation) {
   const int tm = conv_bf16_tile_m(stride, K, dilation);
   if (tm == 0) return 0;
   const int64_t n_tt = (T_out + tm - 1) / tm;
-  // the last tile copies XR rows from its first input row
-  return (n_tt - 1) * tm * stride + xcap_of(tm, K);
+  // the last tile copies XR rows from its first input row, its last pass
+  // from (passes - 1) * kt * dilation rows further
+  const int kt = kernel_taps(tm, K);
+  return (n_tt - 1) * tm * stride + (int64_t)(K / kt - 1) * kt * dilation + xcap_of(tm, kt);
 }
 
 size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img) {
@@ -898,9 +922,9 @@ hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
 namespace {
 // the GroupNorm and LayerNorm instances share their resources (same LDS,
 // launch bounds), so either stands for both
-template <int WM, int KT, int XR>
+template <int WM, int KT, int XR, int NP = 1>
 int capacity_wk() {
-  return resident_capacity((const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED>, NTHR);
+  return resident_capacity((const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED, NP>, NTHR);
 }
 template <int WM>
 int capacity_w(int K) {
@@ -912,6 +936,7 @@ int capacity_w(int K) {
     case 5: return capacity_wk<WM, 5, XCAP_WIDE>();
     default: break;
   }
+  if (WM == 8) return K == 8 ? capacity_wk<8, 4, XCAP_WIDE, 2>() : 0;  // two passes
   if (WM == 4) {
     switch (K) {
       case 6: return capacity_wk<4, 6, XCAP_T6>();

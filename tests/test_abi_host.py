@@ -454,7 +454,10 @@ def test_launch_failure_is_reported_as_hip_error():
                                    # not fit, 256 positions (515 rows) do
     (6, 1, 1, (5, 0), 4096, 16),   # six taps: 256 positions within 496 rows
     (7, 1, 2, (12, 0), 4096, 16),  # seven taps: 256 positions within 368 rows
-    (8, 1, 2, (7, 7), 4096, 32),   # eight taps: 128 positions
+    (8, 1, 2, (7, 7), 4096, 8),    # eight taps: two passes of four on 512 positions
+                                   # (518-row window each)
+    (8, 1, 11, (0, 0), 4096, 32),  # eight taps at dilation 11: a four-tap pass needs 545
+                                   # rows, so 128 positions (205 rows); 4019 outputs
     (4, 3, 1, (3, 0), 6000, 16),   # stride 3: 128 positions (385 rows); 2000 outputs
 ])
 def test_bf16_tile_choice(K, stride, dilation, pad, T, tiles_t):
