@@ -53,7 +53,7 @@ namespace {
 constexpr int TN = ConvBf16Cfg::TN;  // 128 output channels per tile
 constexpr int CK = ConvBf16Cfg::CK;  // 32 input channels per chunk
 constexpr int RW = CK;               // LDS row: 32 bf16 (64 bytes)
-constexpr int KMAX = 8;              // taps: up to 5 on 512-position tiles, 8 on 128
+constexpr int KMAX = 8;              // taps (512-position tiles: up to 5 per pass)
 constexpr int WN = 4;                // MFMA tiles per wave along c
 constexpr int WGN = 2;               // waves along c (TN = WGN * WN * 16)
 constexpr int WGM = 4;               // waves along t
