@@ -345,8 +345,8 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
 
 // FUSE: 0 (one tile per workgroup, epilogue epi), or EPI_GN_FUSED /
 // EPI_LN_FUSED (persistent rounds of whole samples, normalised output).
-// NP: passes over the chunks (K = NP * KT taps; 2 for eight taps on
-// 512-position tiles, whose window and weights for all eight do not fit).
+// NP: passes over the chunks (K = NP * KT taps; 2 for eight or six taps on
+// 512-position tiles, whose window and weights for all taps do not fit).
 template <int WM, int KT, int XR, int FUSE, int NP = 1>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const ConvArgs& a = a_;
@@ -795,8 +795,11 @@ hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = fals
     case 5: return launch_wk<WM, 5, XCAP_WIDE>(a, epi, st, coop);
     default: break;
   }
-  if (WM == 8) return a.K == 8 ? launch_wk<8, 4, XCAP_WIDE, 2>(a, epi, st, coop)  // two passes
-                               : hipErrorInvalidValue;
+  if (WM == 8) {  // eight or six taps: two passes of four or three
+    if (a.K == 8) return launch_wk<8, 4, XCAP_WIDE, 2>(a, epi, st, coop);
+    if (a.K == 6) return launch_wk<8, 3, XCAP_WIDE, 2>(a, epi, st, coop);
+    return hipErrorInvalidValue;
+  }
   if (WM == 4) {
     switch (a.K) {
       case 6: return launch_wk<4, 6, XCAP_T6>(a, epi, st, coop);
@@ -819,11 +822,12 @@ int64_t window(int tm, int stride, int K, int dilation) {
 }
 
 // taps per pass of the kernel for a tile of tm positions and K taps: K (one
-// pass), or 4 for eight taps on 512-position tiles (two passes); 0: none
+// pass), or 4 and 3 for eight and six taps on 512-position tiles (two
+// passes); 0: none
 int kernel_taps(int tm, int K) {
   if (K < 1 || K > KMAX) return 0;
   if (K <= 5 || tm == 128) return K;
-  if (tm == 512) return K == 8 ? 4 : 0;
+  if (tm == 512) return K == 8 ? 4 : K == 6 ? 3 : 0;
   return K <= 7 ? K : 0;  // 256
 }
 
@@ -936,7 +940,11 @@ int capacity_w(int K) {
     case 5: return capacity_wk<WM, 5, XCAP_WIDE>();
     default: break;
   }
-  if (WM == 8) return K == 8 ? capacity_wk<8, 4, XCAP_WIDE, 2>() : 0;  // two passes
+  if (WM == 8) {  // two passes
+    if (K == 8) return capacity_wk<8, 4, XCAP_WIDE, 2>();
+    if (K == 6) return capacity_wk<8, 3, XCAP_WIDE, 2>();
+    return 0;
+  }
   if (WM == 4) {
     switch (K) {
       case 6: return capacity_wk<4, 6, XCAP_T6>();

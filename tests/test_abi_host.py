@@ -452,7 +452,9 @@ def test_launch_failure_is_reported_as_hip_error():
     (5, 1, 2, (2, 2), 4096, 8),    # 512-position tiles: 4092 outputs
     (5, 2, 1, (2, 2), 8192, 16),   # stride 2: the 1027-row window of 512 positions does
                                    # not fit, 256 positions (515 rows) do
-    (6, 1, 1, (5, 0), 4096, 16),   # six taps: 256 positions within 496 rows
+    (6, 1, 1, (5, 0), 4096, 8),    # six taps: two passes of three on 512 positions
+    (6, 1, 20, (0, 0), 4096, 16),  # six taps at dilation 20: a three-tap pass needs 552
+                                   # rows, so 256 positions (356 rows); 3996 outputs
     (7, 1, 2, (12, 0), 4096, 16),  # seven taps: 256 positions within 368 rows
     (8, 1, 2, (7, 7), 4096, 8),    # eight taps: two passes of four on 512 positions
                                    # (518-row window each)
