@@ -203,7 +203,29 @@ PERSIST_CASES = [
       out_dtype="bf16", **BF),
     W("persist_gn_cpg48_k6", N=2, C_in=40, C_out=240, T=800, K=6, dilation=2, pad_left=10,
       G=5, **BF),
+    # six and eight taps as two passes over the chunks on 512-position tiles:
+    # four position tiles with a ragged last one, a partial last chunk,
+    # straddling 25-channel groups; LayerNorm with a bf16 output
+    W("persist_gn_k6_two_pass", N=5, C_in=72, C_out=200, T=1700, K=6, dilation=3, pad_left=7,
+      pad_right=8, G=8, **BF),
+    W("persist_ln_k8_two_pass_bf16out", N=3, C_in=40, C_out=136, T=1100, K=8, pad_left=7,
+      norm="layer_channels", out_dtype="bf16", **BF),
 ]
+
+# the same two-pass kernels on the split route
+TWO_PASS_SPLIT = [
+    W("split_gn_k8_two_pass", N=3, C_in=72, C_out=160, T=1300, K=8, pad_left=3, pad_right=4,
+      G=5, persistent=False, **BF),
+    W("split_ln_k6_two_pass", N=2, C_in=40, C_out=200, T=1111, K=6, dilation=2, pad_left=5,
+      pad_right=5, norm="layer_channels", persistent=False, **BF),
+]
+
+
+@pytest.mark.parametrize("wl", TWO_PASS_SPLIT, ids=lambda w: w.name)
+def test_two_pass_split_parity(wl):
+    from tests.gpu_util import library_route
+    assert library_route(wl) == "split"
+    check_parity(wl)
 
 
 @pytest.mark.parametrize("wl", PERSIST_CASES, ids=lambda w: w.name)
