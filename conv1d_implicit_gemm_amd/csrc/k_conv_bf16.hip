@@ -42,6 +42,8 @@
 // Epilogue: shared with the fp32 kernel (store y, GroupNorm or channel-
 // LayerNorm partial statistics), or in the persistent kernel the sample-wide
 // statistics and the normalised output (fused_norm_epilogue).
+#include <type_traits>
+
 #include "common.hpp"
 #include "conv_epilogue.hpp"
 #include "grid_sync.hpp"
@@ -345,9 +347,15 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
 
 // FUSE: 0 (one tile per workgroup, epilogue epi), or EPI_GN_FUSED /
 // EPI_LN_FUSED (persistent rounds of whole samples, normalised output).
-// NP: passes over the chunks (K = NP * KT taps; 2 for eight or six taps on
-// 512-position tiles, whose window and weights for all taps do not fit).
-template <int WM, int KT, int XR, int FUSE, int NP = 1>
+// NP: passes over the chunks.  IL = 0: K = NP * KT consecutive taps per
+// pass (NP = 2 for eight or six taps on 512-position tiles, whose window and
+// weights for all taps do not fit).  IL = 1 (strided convolutions): pass p
+// takes the taps p, p + s, p + 2s, ... (at most KT of them) and its window
+// gathers every s-th image row from row s*t0 + p*d, so that within a pass
+// the output positions advance one window row each and the taps d rows: a
+// stride-1 window of TM + (KT - 1)*d rows where the direct one would need
+// (TM - 1)*s + (K - 1)*d + 1.
+template <int WM, int KT, int XR, int FUSE, int NP = 1, int IL = 0>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const ConvArgs& a = a_;
   // the weight stage also holds the epilogue's cross-wave merge (<= 12 KB)
@@ -368,6 +376,8 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const int wm = wave % WGM, wn = wave / WGM;
   const int lr = lane & 15, kq = lane >> 4;
   const int s = a.stride, d = a.dilation;
+  const int sw = IL ? 1 : s;  // window rows per output position
+  const int sg = IL ? s : 1;  // image rows per window row
   // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
   // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
   // c-tile fastest, so the channel tiles of one input window share an L2.
@@ -406,31 +416,48 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // NP passes over the chunks, pass p with taps p*KT .. p*KT + KT - 1: its
   // window starts p*KT*d rows further down the image and its weights are
   // those taps of each (c-tile, chunk) block
-  static_assert(NP == 1 || NP == 2, "one or two passes");
-  constexpr int64_t wblk = (int64_t)NP * KT * (TN * RW * 2);  // bytes of a (c-tile, chunk) block
+  static_assert(NP >= 1 && NP <= (IL ? 3 : 2), "passes");
+  const int64_t wblk = IL ? (int64_t)a.K * (TN * RW * 2)        // bytes of a (c-tile, chunk)
+                          : (int64_t)NP * KT * (TN * RW * 2);  // block of the weight image
   const char* const wimg = (const char*)a.wp + (int64_t)ctile * a.n_chunks * wblk;
   // A copy's source offset is a wave-uniform part (its piece) plus one of two
   // lane offsets: window row 16 * piece + lane / 4 at logical column
   // (lane % 4) ^ swz(row) (the column landing at slot lane % 4; swz of the
   // row depends only on the lane), or weight bytes 16 * lane.
   const uint32_t lane_x =
-      (uint32_t)((lane >> 2) * row_bytes + 16 * ((lane & 3) ^ swz(lane >> 2)));
+      (uint32_t)((lane >> 2) * sg * row_bytes + 16 * ((lane & 3) ^ swz(lane >> 2)));
   const uint32_t lane_w = (uint32_t)(16 * lane);
   // q: pass * n_chunks + chunk
+  auto pass_of = [&](int q) __attribute__((always_inline)) {
+    return NP >= 3 && q >= 2 * a.n_chunks ? 2 : (NP >= 2 && q >= a.n_chunks ? 1 : 0);
+  };
   auto copy_from = [&](const char* xw, int p, int q, u16* xs, u16* ws)
       __attribute__((always_inline)) {
     int piece = wave + NWAVE * p;
     if (piece >= NPIECE) piece = NPIECE - 1;
-    const int pass = NP == 2 && q >= a.n_chunks ? 1 : 0;
+    const int pass = pass_of(q);
     const int chunk = q - pass * a.n_chunks;
-    if (piece < XP)
-      dma16(xw + (int64_t)pass * KT * d * row_bytes + (int64_t)chunk * (CK * 2) +
-                (int64_t)16 * piece * row_bytes,
+    if (piece < XP) {
+      dma16(xw + (int64_t)pass * (IL ? 1 : KT) * d * row_bytes + (int64_t)chunk * (CK * 2) +
+                (int64_t)16 * piece * sg * row_bytes,
             lane_x, (char*)xs + piece * 1024);
-    else
+    } else if constexpr (IL) {
+      // weight slot k of the pass: tap pass + s*k (slots past the last tap,
+      // whose MFMAs are skipped, copy the last tap: no read leaves the block)
+      const int k = (piece - XP) >> 3;
+      int tap = pass + s * k;
+      if (tap > a.K - 1) tap = a.K - 1;
+      // uniform (chunk step, piece and kernel arguments): kept in a scalar
+      // register, as the copy's base operand requires
+      tap = __builtin_amdgcn_readfirstlane(tap);
+      dma16(wimg + (int64_t)chunk * wblk + (int64_t)tap * (TN * RW * 2) +
+                ((piece - XP) & 7) * 1024,
+            lane_w, (char*)ws + (piece - XP) * 1024);
+    } else {
       dma16(wimg + (int64_t)chunk * wblk + (int64_t)pass * (KT * TN * RW * 2) +
                 (piece - XP) * 1024,
             lane_w, (char*)ws + (piece - XP) * 1024);
+    }
   };
   auto copy = [&](int p, int chunk, u16* xs, u16* ws) __attribute__((always_inline)) {
     copy_from(xwin, p, chunk, xs, ws);
@@ -445,7 +472,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // issues all its copies at once stalls for ~1.2 K cycles, and with both
   // waves of a SIMD doing so right after the barrier the MFMA pipe idles.
   // The last tap step issues none, leaving it for the copies to land.
-  constexpr int NG = KT > 2 ? KT - 1 : 1;
+  constexpr int NG = IL ? 1 : (KT > 2 ? KT - 1 : 1);  // IL: a pass may have fewer taps
   auto stage_group = [&](int chunk, u16* xs, u16* ws, int g) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < PPW; ++p)
@@ -460,7 +487,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
 
   // Operand fragments of one tap: A = 16 output positions x 32 channels
   // (window rows (t - t0) * s + j * d), B = 32 channels x 16 output channels.
-  const int arow0 = (wm * WM * 16 + lr) * s;
+  const int arow0 = (wm * WM * 16 + lr) * sw;
   const int bcol = 8 * (kq ^ swz(lr));  // weight rows: bit 2 of c = bit 2 of lr
   bf16x8 av[WM], bv[WN];
   auto xa_of = [&](const u16* xs, int j) __attribute__((always_inline)) {
@@ -476,7 +503,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
 #pragma unroll
     for (int jn = 0; jn < WN; ++jn) bv[jn] = *(const bf16x8*)(wb + jn * 16 * RW);
 #pragma unroll
-    for (int i = 0; i < WM; ++i) av[i] = *(const bf16x8*)(xa + i * 16 * s * RW);
+    for (int i = 0; i < WM; ++i) av[i] = *(const bf16x8*)(xa + i * 16 * sw * RW);
   };
   // The MFMAs of the tap whose fragments are in av/bv, each fragment replaced
   // by its counterpart of tap j of (xs, ws) as soon as its last MFMA has
@@ -488,14 +515,14 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
     for (int i = 0; i < WM - 1; ++i) {
 #pragma unroll
       for (int jn = 0; jn < WN; ++jn) acc[i][jn] = mfma16x16x32bf16(av[i], bv[jn], acc[i][jn]);
-      av[i] = *(const bf16x8*)(xa + i * 16 * s * RW);
+      av[i] = *(const bf16x8*)(xa + i * 16 * sw * RW);
     }
 #pragma unroll
     for (int jn = 0; jn < WN; ++jn) {
       acc[WM - 1][jn] = mfma16x16x32bf16(av[WM - 1], bv[jn], acc[WM - 1][jn]);
       bv[jn] = *(const bf16x8*)(wb + jn * 16 * RW);
     }
-    av[WM - 1] = *(const bf16x8*)(xa + (WM - 1) * 16 * s * RW);
+    av[WM - 1] = *(const bf16x8*)(xa + (WM - 1) * 16 * sw * RW);
 #pragma unroll
     for (int i = 0; i < WM - 1; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, WN, 0);  // MFMA
@@ -538,10 +565,14 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
         __builtin_amdgcn_s_setprio(0);
     }
   };
-  auto taps = [&](const u16* xs, const u16* ws, int cc, u16* cxs, u16* cws)
+  // taps of (pass, chunk) step q: KT, or with IL those of its pass
+  auto kt_of = [&](int q) __attribute__((always_inline)) {
+    return IL ? (a.K - pass_of(q) + s - 1) / s : kt;
+  };
+  auto taps = [&](const u16* xs, const u16* ws, int ktq, int cc, u16* cxs, u16* cws)
       __attribute__((always_inline)) {
 #pragma nounroll
-    for (int j = 1; j < kt; ++j) {
+    for (int j = 1; j < ktq; ++j) {
       set_prio(j);
       mfma_reload(xs, ws, j);
       if (j < NG) stage_group(cc, cxs, cws, j);
@@ -565,14 +596,14 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   int c = 0;
   for (; c + 1 < n_chunks; c += 2) {
     // stage 0 holds chunk c, its tap 0 in the fragments; stage 1 is loading c+1
-    taps(Xs0, Ws0, cl(c + 1), Xs1, Ws1);
+    taps(Xs0, Ws0, kt_of(c), cl(c + 1), Xs1, Ws1);
     wait_all_mem();
     lds_barrier();
     set_prio(0);
     mfma_reload(Xs1, Ws1, 0);  // chunk c's last tap; chunk c+1's tap 0
     stage_group(cl(c + 2), Xs0, Ws0, 0);
     // stage 1 holds chunk c+1; stage 0 is loading c+2
-    taps(Xs1, Ws1, cl(c + 2), Xs0, Ws0);
+    taps(Xs1, Ws1, kt_of(c + 1), cl(c + 2), Xs0, Ws0);
     wait_all_mem();
     lds_barrier();
     set_prio(0);
@@ -580,7 +611,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
     stage_group(cl(c + 3), Xs1, Ws1, 0);
   }
   if (c < n_chunks) {  // odd count: the last chunk is in stage 0
-    taps(Xs0, Ws0, cl(c + 1), Xs1, Ws1);
+    taps(Xs0, Ws0, kt_of(c), cl(c + 1), Xs1, Ws1);
     mfma_only();
   }
   __builtin_amdgcn_s_setprio(0);
@@ -767,7 +798,7 @@ __global__ __launch_bounds__(256) void conv_bf16_pack_x_nlc_kernel(const u16* __
   }
 }
 
-template <int WM, int KT, int XR, int NP = 1>
+template <int WM, int KT, int XR, int NP = 1, int IL = 0>
 hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = false) {
   if (epi == EPI_GN_FUSED || epi == EPI_LN_FUSED) {
     // one round: spr whole samples, every workgroup resident at once
@@ -775,18 +806,71 @@ hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = fal
     int ep = epi;
     void* args[] = {(void*)&ac, (void*)&ep};
     const void* k = epi == EPI_GN_FUSED
-                        ? (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED, NP>
-                        : (const void*)conv_bf16_kernel<WM, KT, XR, EPI_LN_FUSED, NP>;
+                        ? (const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED, NP, IL>
+                        : (const void*)conv_bf16_kernel<WM, KT, XR, EPI_LN_FUSED, NP, IL>;
     return launch_coresident(k, (unsigned)(a.spr * a.n_ttiles * a.n_ctiles), NTHR, args, coop,
                              st);
   }
   dim3 grid((unsigned)(a.n_ttiles * a.n_ctiles * a.N));
-  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR, 0, NP>), grid, dim3(NTHR), 0, st, a, epi);
+  hipLaunchKernelGGL((conv_bf16_kernel<WM, KT, XR, 0, NP, IL>), grid, dim3(NTHR), 0, st, a,
+                     epi);
   return hipGetLastError();
+}
+
+// How the bf16 conv runs (stride s, K taps, dilation d): tiles of tm
+// positions, np passes over the chunks of at most kt taps each, interleaved
+// (il, strided convolutions) or of consecutive taps, xr window rows.  The
+// first that fits: 512 positions with all taps in one pass; 512 with eight
+// or six taps in two passes; 512 with a stride of 2 or 3 in interleaved
+// passes; 256; 128.  tm == 0: not built.
+struct Geo {
+  int tm, kt, np, il, xr;
+};
+Geo geo_of(int s, int K, int d) {
+  if (K < 1 || K > KMAX || s < 1 || d < 1) return Geo{0, 0, 0, 0, 0};
+  auto fits = [&](int tm, int kt, int rows_per_pos, int xr) {
+    return (int64_t)(tm - 1) * rows_per_pos + (int64_t)(kt - 1) * d + 1 <= xr;
+  };
+  if (K <= 5 && fits(512, K, s, XCAP_WIDE)) return Geo{512, K, 1, 0, XCAP_WIDE};
+  if ((K == 8 || K == 6) && fits(512, K / 2, s, XCAP_WIDE))
+    return Geo{512, K / 2, 2, 0, XCAP_WIDE};
+  if (s == 2 || s == 3) {
+    const int kt = (K + s - 1) / s, np = K < s ? K : s;
+    if (kt <= 4 && fits(512, kt, 1, XCAP_WIDE)) return Geo{512, kt, np, 1, XCAP_WIDE};
+  }
+  const int cap256 = K <= 5 ? XCAP_WIDE : K == 6 ? XCAP_T6 : K == 7 ? XCAP_T7 : 0;
+  if (cap256 > 0 && fits(256, K, s, cap256)) return Geo{256, K, 1, 0, cap256};
+  const int cap128 = K <= 5 ? XCAP_WIDE : XCAP_TAPS;
+  if (fits(128, K, s, cap128)) return Geo{128, K, 1, 0, cap128};
+  return Geo{0, 0, 0, 0, 0};
+}
+
+// the interleaved instances of 512-position tiles: (kt, np) of strides 2 and 3
+template <typename F>
+hipError_t il_dispatch(const Geo& g, F&& f) {
+  switch (g.kt * 4 + g.np) {
+    case 1 * 4 + 1: return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    case 1 * 4 + 2: return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    case 1 * 4 + 3: return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{});
+    case 2 * 4 + 2: return f(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    case 2 * 4 + 3: return f(std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
+    case 3 * 4 + 2: return f(std::integral_constant<int, 3>{}, std::integral_constant<int, 2>{});
+    case 3 * 4 + 3: return f(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
+    case 4 * 4 + 2: return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int WM>
 hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = false) {
+  if constexpr (WM == 8) {
+    const Geo g = geo_of(a.stride, a.K, a.dilation);
+    if (g.il)
+      return il_dispatch(g, [&](auto kt, auto np) {
+        return launch_wk<8, decltype(kt)::value, XCAP_WIDE, decltype(np)::value, 1>(a, epi, st,
+                                                                                    coop);
+      });
+  }
   switch (a.K) {
     case 1: return launch_wk<WM, 1, XCAP_WIDE>(a, epi, st, coop);
     case 2: return launch_wk<WM, 2, XCAP_WIDE>(a, epi, st, coop);
@@ -821,42 +905,20 @@ int64_t window(int tm, int stride, int K, int dilation) {
   return (int64_t)(tm - 1) * stride + (int64_t)(K - 1) * dilation + 1;
 }
 
-// taps per pass of the kernel for a tile of tm positions and K taps: K (one
-// pass), or 4 and 3 for eight and six taps on 512-position tiles (two
-// passes); 0: none
-int kernel_taps(int tm, int K) {
-  if (K < 1 || K > KMAX) return 0;
-  if (K <= 5 || tm == 128) return K;
-  if (tm == 512) return K == 8 ? 4 : K == 6 ? 3 : 0;
-  return K <= 7 ? K : 0;  // 256
-}
-
-// window rows a tile of tm positions staging kt taps per pass can hold
-int xcap_of(int tm, int kt) {
-  if (kt < 1 || kt > KMAX) return 0;
-  if (kt <= 5) return XCAP_WIDE;
-  if (tm == 256) return kt == 6 ? XCAP_T6 : kt == 7 ? XCAP_T7 : 0;
-  return tm == 128 ? XCAP_TAPS : 0;
-}
-
 }  // namespace
 
-int conv_bf16_tile_m(int stride, int K, int dilation) {
-  for (int tm : {512, 256, 128}) {
-    const int kt = kernel_taps(tm, K), cap = xcap_of(tm, kt);
-    if (cap > 0 && window(tm, stride, kt, dilation) <= cap) return tm;
-  }
-  return 0;
-}
+int conv_bf16_tile_m(int stride, int K, int dilation) { return geo_of(stride, K, dilation).tm; }
 
 int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation) {
   const int tm = conv_bf16_tile_m(stride, K, dilation);
   if (tm == 0) return 0;
+  const Geo g = geo_of(stride, K, dilation);
   const int64_t n_tt = (T_out + tm - 1) / tm;
-  // the last tile copies XR rows from its first input row, its last pass
-  // from (passes - 1) * kt * dilation rows further
-  const int kt = kernel_taps(tm, K);
-  return (n_tt - 1) * tm * stride + (int64_t)(K / kt - 1) * kt * dilation + xcap_of(tm, kt);
+  const int64_t first = (n_tt - 1) * tm * stride;  // the last tile's first input row
+  // its last pass copies xr rows from (np - 1) * kt * dilation rows further,
+  // or (interleaved) every stride-th row from (np - 1) * dilation further
+  if (g.il) return first + (int64_t)(g.np - 1) * dilation + (int64_t)stride * (g.xr - 1) + 1;
+  return first + (int64_t)(g.np - 1) * g.kt * dilation + g.xr;
 }
 
 size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img) {
@@ -926,9 +988,10 @@ hipError_t conv_bf16_launch(const ConvArgs& a, int epi, hipStream_t s) {
 namespace {
 // the GroupNorm and LayerNorm instances share their resources (same LDS,
 // launch bounds), so either stands for both
-template <int WM, int KT, int XR, int NP = 1>
+template <int WM, int KT, int XR, int NP = 1, int IL = 0>
 int capacity_wk() {
-  return resident_capacity((const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED, NP>, NTHR);
+  return resident_capacity((const void*)conv_bf16_kernel<WM, KT, XR, EPI_GN_FUSED, NP, IL>,
+                           NTHR);
 }
 template <int WM>
 int capacity_w(int K) {
@@ -971,7 +1034,16 @@ int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctil
 }
 
 int conv_bf16_fused_capacity(int stride, int K, int dilation) {
-  const int tm = conv_bf16_tile_m(stride, K, dilation);
+  const Geo g = geo_of(stride, K, dilation);
+  const int tm = g.tm;
+  if (tm == 512 && g.il) {
+    int cap = 0;
+    il_dispatch(g, [&](auto kt, auto np) {
+      cap = capacity_wk<8, decltype(kt)::value, XCAP_WIDE, decltype(np)::value, 1>();
+      return hipSuccess;
+    });
+    return cap;
+  }
   if (tm == 512) return capacity_w<8>(K);
   if (tm == 256) return capacity_w<4>(K);
   if (tm == 128) return capacity_w<2>(K);

@@ -450,8 +450,9 @@ def test_launch_failure_is_reported_as_hip_error():
 
 @pytest.mark.parametrize("K,stride,dilation,pad,T,tiles_t", [
     (5, 1, 2, (2, 2), 4096, 8),    # 512-position tiles: 4092 outputs
-    (5, 2, 1, (2, 2), 8192, 16),   # stride 2: the 1027-row window of 512 positions does
-                                   # not fit, 256 positions (515 rows) do
+    (5, 2, 1, (2, 2), 8192, 8),    # stride 2: the 1027-row window of 512 positions does
+                                   # not fit; interleaved passes (taps 0, 2, 4 and 1, 3),
+                                   # each gathering every second row, do (514 rows)
     (6, 1, 1, (5, 0), 4096, 8),    # six taps: two passes of three on 512 positions
     (6, 1, 20, (0, 0), 4096, 16),  # six taps at dilation 20: a three-tap pass needs 552
                                    # rows, so 256 positions (356 rows); 3996 outputs
@@ -460,7 +461,10 @@ def test_launch_failure_is_reported_as_hip_error():
                                    # (518-row window each)
     (8, 1, 11, (0, 0), 4096, 32),  # eight taps at dilation 11: a four-tap pass needs 545
                                    # rows, so 128 positions (205 rows); 4019 outputs
-    (4, 3, 1, (3, 0), 6000, 16),   # stride 3: 128 positions (385 rows); 2000 outputs
+    (4, 3, 1, (3, 0), 6000, 4),    # stride 3: three interleaved passes on 512 positions
+                                   # (taps 0, 3 / 1 / 2; 513 rows); 2000 outputs
+    (5, 2, 17, (0, 0), 8192, 32),  # stride 2 at dilation 17: an interleaved pass needs 546
+                                   # rows and 256 positions 579, so 128 (323); 4062 outputs
 ])
 def test_bf16_tile_choice(K, stride, dilation, pad, T, tiles_t):
     """The bf16 conv takes the largest tile (512, 256 or 128 positions) whose
