@@ -221,6 +221,39 @@ TWO_PASS_SPLIT = [
 ]
 
 
+# strided convolutions as interleaved passes on 512-position tiles: one, two
+# and three passes, passes with fewer taps than others (MFMAs skipped),
+# dilation, channels-last input, bf16 output, straddling groups, the split
+# and conv-only routes; several position tiles with a ragged last one
+STRIDED_CASES = [
+    (W("il_s2_k1_gn_cpg17", N=2, C_in=64, C_out=136, T=2100, K=1, stride=2, G=8, **BF),
+     "fused_persistent"),
+    (W("il_s2_k2_d3_ln", N=2, C_in=40, C_out=200, T=1999, K=2, stride=2, dilation=3,
+       pad_left=1, pad_right=2, norm="layer_channels", **BF), "fused_persistent"),
+    (W("il_s2_k4_causal_gn_bf16out", N=3, C_in=72, C_out=160, T=2400, K=4, stride=2,
+       pad_left=3, G=4, out_dtype="bf16", **BF), "fused_persistent"),
+    (W("il_s2_k7_d2_gn", N=2, C_in=40, C_out=144, T=2300, K=7, stride=2, dilation=2,
+       pad_left=6, pad_right=6, G=9, **BF), "fused_persistent"),
+    (W("il_s3_k2_gn_nlc", N=2, C_in=48, C_out=128, T=3100, K=2, stride=3, pad_left=1, G=16,
+       channels_last=True, **BF), "fused_persistent"),
+    (W("il_s3_k3_d2_gn", N=2, C_in=40, C_out=136, T=3300, K=3, stride=3, dilation=2,
+       pad_left=2, pad_right=2, G=17, **BF), "fused_persistent"),
+    (W("il_s3_k5_ln_split", N=2, C_in=33, C_out=150, T=3001, K=5, stride=3, pad_left=2,
+       pad_right=2, norm="layer_channels", persistent=False, **BF), "split"),
+    (W("il_s3_k8_causal_gn", N=2, C_in=40, C_out=128, T=2900, K=8, stride=3, pad_left=7, G=8,
+       **BF), "fused_persistent"),
+    (W("il_s2_k8_d4_conv_only", N=2, C_in=64, C_out=130, T=2500, K=8, stride=2, dilation=4,
+       pad_left=14, norm=None, **BF), "conv_only"),
+]
+
+
+@pytest.mark.parametrize("wl,route", STRIDED_CASES, ids=lambda c: getattr(c, "name", c))
+def test_interleaved_strided_parity(wl, route):
+    from tests.gpu_util import library_route
+    assert library_route(wl) == route
+    check_parity(wl)
+
+
 @pytest.mark.parametrize("wl", TWO_PASS_SPLIT, ids=lambda w: w.name)
 def test_two_pass_split_parity(wl):
     from tests.gpu_util import library_route
