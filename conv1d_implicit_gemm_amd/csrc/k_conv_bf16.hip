@@ -354,7 +354,10 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
 // gathers every s-th image row from row s*t0 + p*d, so that within a pass
 // the output positions advance one window row each and the taps d rows: a
 // stride-1 window of TM + (KT - 1)*d rows where the direct one would need
-// (TM - 1)*s + (K - 1)*d + 1.
+// (TM - 1)*s + (K - 1)*d + 1.  IL = 2: consecutive taps, the last pass with
+// fewer (seven taps as four and three).  With IL != 0 a step's tap count
+// follows its pass, and weight slots past a pass's last tap copy the last
+// tap (their MFMAs are skipped).
 template <int WM, int KT, int XR, int FUSE, int NP = 1, int IL = 0>
 __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const ConvArgs& a = a_;
@@ -376,8 +379,8 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const int wm = wave % WGM, wn = wave / WGM;
   const int lr = lane & 15, kq = lane >> 4;
   const int s = a.stride, d = a.dilation;
-  const int sw = IL ? 1 : s;  // window rows per output position
-  const int sg = IL ? s : 1;  // image rows per window row
+  const int sw = IL == 1 ? 1 : s;  // window rows per output position
+  const int sg = IL == 1 ? s : 1;  // image rows per window row
   // 1-D grid, XCD-aware: workgroup ids round-robin over the 8 XCDs; XCD x
   // takes a contiguous range of tiles ordered (n, t-tile, c-tile) with the
   // c-tile fastest, so the channel tiles of one input window share an L2.
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // NP passes over the chunks, pass p with taps p*KT .. p*KT + KT - 1: its
   // window starts p*KT*d rows further down the image and its weights are
   // those taps of each (c-tile, chunk) block
-  static_assert(NP >= 1 && NP <= (IL ? 3 : 2), "passes");
+  static_assert(NP >= 1 && NP <= (IL == 1 ? 3 : 2), "passes");
   const int64_t wblk = IL ? (int64_t)a.K * (TN * RW * 2)        // bytes of a (c-tile, chunk)
                           : (int64_t)NP * KT * (TN * RW * 2);  // block of the weight image
   const char* const wimg = (const char*)a.wp + (int64_t)ctile * a.n_chunks * wblk;
@@ -438,14 +441,15 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
     const int pass = pass_of(q);
     const int chunk = q - pass * a.n_chunks;
     if (piece < XP) {
-      dma16(xw + (int64_t)pass * (IL ? 1 : KT) * d * row_bytes + (int64_t)chunk * (CK * 2) +
+      dma16(xw + (int64_t)pass * (IL == 1 ? 1 : KT) * d * row_bytes + (int64_t)chunk * (CK * 2) +
                 (int64_t)16 * piece * sg * row_bytes,
             lane_x, (char*)xs + piece * 1024);
     } else if constexpr (IL) {
-      // weight slot k of the pass: tap pass + s*k (slots past the last tap,
-      // whose MFMAs are skipped, copy the last tap: no read leaves the block)
+      // weight slot k of the pass: tap pass + s*k (IL 1) or pass*KT + k (IL
+      // 2); slots past the last tap, whose MFMAs are skipped, copy the last
+      // tap: no read leaves the block
       const int k = (piece - XP) >> 3;
-      int tap = pass + s * k;
+      int tap = IL == 1 ? pass + s * k : pass * KT + k;
       if (tap > a.K - 1) tap = a.K - 1;
       // uniform (chunk step, piece and kernel arguments): kept in a scalar
       // register, as the copy's base operand requires
@@ -567,7 +571,12 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   };
   // taps of (pass, chunk) step q: KT, or with IL those of its pass
   auto kt_of = [&](int q) __attribute__((always_inline)) {
-    return IL ? (a.K - pass_of(q) + s - 1) / s : kt;
+    if constexpr (IL == 1) return (a.K - pass_of(q) + s - 1) / s;
+    if constexpr (IL == 2) {
+      const int left = a.K - pass_of(q) * KT;
+      return left < KT ? left : KT;
+    }
+    return kt;
   };
   auto taps = [&](const u16* xs, const u16* ws, int ktq, int cc, u16* cxs, u16* cws)
       __attribute__((always_inline)) {
@@ -820,9 +829,9 @@ hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = fal
 // How the bf16 conv runs (stride s, K taps, dilation d): tiles of tm
 // positions, np passes over the chunks of at most kt taps each, interleaved
 // (il, strided convolutions) or of consecutive taps, xr window rows.  The
-// first that fits: 512 positions with all taps in one pass; 512 with eight
-// or six taps in two passes; 512 with a stride of 2 or 3 in interleaved
-// passes; 256; 128.  tm == 0: not built.
+// first that fits: 512 positions with all taps in one pass; 512 with eight,
+// six or seven taps in two passes; 512 with a stride of 2 or 3 in
+// interleaved passes; 256; 128.  tm == 0: not built.
 struct Geo {
   int tm, kt, np, il, xr;
 };
@@ -834,6 +843,7 @@ Geo geo_of(int s, int K, int d) {
   if (K <= 5 && fits(512, K, s, XCAP_WIDE)) return Geo{512, K, 1, 0, XCAP_WIDE};
   if ((K == 8 || K == 6) && fits(512, K / 2, s, XCAP_WIDE))
     return Geo{512, K / 2, 2, 0, XCAP_WIDE};
+  if (K == 7 && fits(512, 4, s, XCAP_WIDE)) return Geo{512, 4, 2, 2, XCAP_WIDE};  // 4 + 3
   if (s == 2 || s == 3) {
     const int kt = (K + s - 1) / s, np = K < s ? K : s;
     if (kt <= 4 && fits(512, kt, 1, XCAP_WIDE)) return Geo{512, kt, np, 1, XCAP_WIDE};
@@ -865,6 +875,7 @@ template <int WM>
 hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = false) {
   if constexpr (WM == 8) {
     const Geo g = geo_of(a.stride, a.K, a.dilation);
+    if (g.il == 2) return launch_wk<8, 4, XCAP_WIDE, 2, 2>(a, epi, st, coop);
     if (g.il)
       return il_dispatch(g, [&](auto kt, auto np) {
         return launch_wk<8, decltype(kt)::value, XCAP_WIDE, decltype(np)::value, 1>(a, epi, st,
@@ -917,7 +928,8 @@ int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation) {
   const int64_t first = (n_tt - 1) * tm * stride;  // the last tile's first input row
   // its last pass copies xr rows from (np - 1) * kt * dilation rows further,
   // or (interleaved) every stride-th row from (np - 1) * dilation further
-  if (g.il) return first + (int64_t)(g.np - 1) * dilation + (int64_t)stride * (g.xr - 1) + 1;
+  if (g.il == 1)
+    return first + (int64_t)(g.np - 1) * dilation + (int64_t)stride * (g.xr - 1) + 1;
   return first + (int64_t)(g.np - 1) * g.kt * dilation + g.xr;
 }
 
@@ -1036,6 +1048,7 @@ int fused_barrier_groups(int epi, int64_t C_out, int G, int n_ttiles, int n_ctil
 int conv_bf16_fused_capacity(int stride, int K, int dilation) {
   const Geo g = geo_of(stride, K, dilation);
   const int tm = g.tm;
+  if (tm == 512 && g.il == 2) return capacity_wk<8, 4, XCAP_WIDE, 2, 2>();
   if (tm == 512 && g.il) {
     int cap = 0;
     il_dispatch(g, [&](auto kt, auto np) {

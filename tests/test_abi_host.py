@@ -456,7 +456,10 @@ def test_launch_failure_is_reported_as_hip_error():
     (6, 1, 1, (5, 0), 4096, 8),    # six taps: two passes of three on 512 positions
     (6, 1, 20, (0, 0), 4096, 16),  # six taps at dilation 20: a three-tap pass needs 552
                                    # rows, so 256 positions (356 rows); 3996 outputs
-    (7, 1, 2, (12, 0), 4096, 16),  # seven taps: 256 positions within 368 rows
+    (7, 1, 2, (12, 0), 4096, 8),   # seven taps: two passes (four and three) on 512
+                                   # positions
+    (7, 1, 11, (0, 0), 4096, 16),  # seven taps at dilation 11: a four-tap pass needs 545
+                                   # rows, so 256 positions (322 rows); 4030 outputs
     (8, 1, 2, (7, 7), 4096, 8),    # eight taps: two passes of four on 512 positions
                                    # (518-row window each)
     (8, 1, 11, (0, 0), 4096, 32),  # eight taps at dilation 11: a four-tap pass needs 545

@@ -210,6 +210,9 @@ PERSIST_CASES = [
       pad_right=8, G=8, **BF),
     W("persist_ln_k8_two_pass_bf16out", N=3, C_in=40, C_out=136, T=1100, K=8, pad_left=7,
       norm="layer_channels", out_dtype="bf16", **BF),
+    # seven taps: passes of four and three (the fourth slot's MFMAs skipped)
+    W("persist_gn_k7_two_pass", N=3, C_in=72, C_out=192, T=1600, K=7, dilation=2, pad_left=6,
+      pad_right=6, G=6, **BF),
 ]
 
 # the same two-pass kernels on the split route
@@ -218,6 +221,8 @@ TWO_PASS_SPLIT = [
       G=5, persistent=False, **BF),
     W("split_ln_k6_two_pass", N=2, C_in=40, C_out=200, T=1111, K=6, dilation=2, pad_left=5,
       pad_right=5, norm="layer_channels", persistent=False, **BF),
+    W("split_gn_k7_two_pass_bf16out", N=2, C_in=33, C_out=160, T=1234, K=7, pad_left=3,
+      pad_right=3, G=8, out_dtype="bf16", persistent=False, **BF),
 ]
 
 
