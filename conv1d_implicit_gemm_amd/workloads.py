@@ -80,12 +80,15 @@ WORKLOADS = {
                  T=4096, K=5, dilation=2, pad_left=2, pad_right=2, dtype="bf16",
                  norm="layer_channels"),
         # beyond the pages' problems, at full scale: stride 2 and 3, eight taps at
-        # dilation 2, groups of 256 channels (spanning two 128-channel tiles) and of
-        # 48 (not tiling them), channels-last input, fp32 with stride 2
+        # dilation 2, seven causal taps, groups of 256 channels (spanning two
+        # 128-channel tiles) and of 48 (not tiling them), channels-last input, fp32
+        # with stride 2
         Workload("conv1d_gn_bf16_n32_c512x1024_t8192_k5s2", N=32, C_in=512, C_out=1024,
                  T=8192, K=5, stride=2, pad_left=2, pad_right=2, dtype="bf16", G=32),
         Workload("conv1d_gn_bf16_n32_c256x512_t4096_k8d2", N=32, C_in=256, C_out=512,
                  T=4096, K=8, dilation=2, pad_left=7, pad_right=7, dtype="bf16", G=16),
+        Workload("conv1d_lnc_bf16_n32_c512x512_t4096_k7", N=32, C_in=512, C_out=512, T=4096,
+                 K=7, pad_left=6, dtype="bf16", norm="layer_channels"),
         Workload("conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4", N=32, C_in=512, C_out=1024,
                  T=4096, K=5, dilation=2, pad_left=4, pad_right=4, dtype="bf16", G=4),
         Workload("conv1d_gn_bf16_n16_c256x1536_t4096_k3_g32", N=16, C_in=256, C_out=1536,
@@ -102,6 +105,7 @@ WORKLOADS = {
 # outputs, timed by bench.py --mode generality).
 GENERALITY = ("conv1d_gn_bf16_n32_c512x1024_t8192_k5s2",
               "conv1d_gn_bf16_n32_c256x512_t4096_k8d2",
+              "conv1d_lnc_bf16_n32_c512x512_t4096_k7",
               "conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4",
               "conv1d_gn_bf16_n16_c256x1536_t4096_k3_g32",
               "conv1d_lnc_bf16_nlc_n30_c384x768_t6000_k4s3",

@@ -324,6 +324,7 @@ def test_persistent_determinism():
 # the last sample of each.
 SCALE_ROUTES = {"conv1d_gn_bf16_n32_c512x1024_t8192_k5s2": "fused_persistent",
                 "conv1d_gn_bf16_n32_c256x512_t4096_k8d2": "fused_persistent",
+                "conv1d_lnc_bf16_n32_c512x512_t4096_k7": "fused_persistent",
                 "conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4": "fused_persistent",
                 "conv1d_gn_bf16_n16_c256x1536_t4096_k3_g32": "fused_persistent",
                 "conv1d_lnc_bf16_nlc_n30_c384x768_t6000_k4s3": "fused_persistent",
