@@ -911,10 +911,6 @@ hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = fals
   }
 }
 
-// input rows a TM-position tile needs
-int64_t window(int tm, int stride, int K, int dilation) {
-  return (int64_t)(tm - 1) * stride + (int64_t)(K - 1) * dilation + 1;
-}
 
 }  // namespace
 
