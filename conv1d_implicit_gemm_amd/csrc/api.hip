@@ -450,9 +450,19 @@ int log_conv(const char* entry, const c1g_conv_desc* d, const c1g_norm_desc* nd,
                   : nd->norm == C1G_NORM_NONE ? "none" : "?",
                   nd->G, (double)nd->eps, nd->epilogue == C1G_EPI_ROWMIN_BIAS ? " rowmin" : "",
                   nd->flags);
-  if (p.status == C1G_OK && p.route != R_INVALID)
-    std::snprintf(plan, sizeof(plan), " | %s T_out=%lld tiles=%dx%d ws=%zu",
-                  route_name(p.route), (long long)p.T_out, p.n_ttiles, p.n_ctiles, p.total);
+  if (p.status == C1G_OK && p.route != R_INVALID) {
+    // bf16 convolutions: the tile's positions and, beyond one, the passes
+    char conv[64] = "";
+    if (p.bf16 && d && (p.route == R_SPLIT || p.route == R_CONV_ONLY || p.route == R_PERSIST)) {
+      int il = 0;
+      const int np = conv_bf16_passes(d->stride, d->K, d->dilation, &il);
+      std::snprintf(conv, sizeof(conv), " tile=%d%s%s", p.tm, np > 1 ? " passes=" : "",
+                    np > 1 ? (il ? (np == 2 ? "2 interleaved" : "3 interleaved") : "2") : "");
+    }
+    std::snprintf(plan, sizeof(plan), " | %s T_out=%lld tiles=%dx%d ws=%zu%s",
+                  route_name(p.route), (long long)p.T_out, p.n_ttiles, p.n_ctiles, p.total,
+                  conv);
+  }
   const char* reason = (why && *why) ? why : (t_note ? t_note : "");
   log_line("c1g: %s %s%s%s -> %s%s%s\n", entry, geo, nrm, plan, c1g_status_string(status),
            *reason ? ": " : "", reason);

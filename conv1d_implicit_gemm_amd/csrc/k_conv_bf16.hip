@@ -916,6 +916,12 @@ hipError_t launch_w(const ConvArgs& a, int epi, hipStream_t st, bool coop = fals
 
 int conv_bf16_tile_m(int stride, int K, int dilation) { return geo_of(stride, K, dilation).tm; }
 
+int conv_bf16_passes(int stride, int K, int dilation, int* interleaved) {
+  const Geo g = geo_of(stride, K, dilation);
+  if (interleaved) *interleaved = g.il == 1;
+  return g.np;
+}
+
 int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation) {
   const int tm = conv_bf16_tile_m(stride, K, dilation);
   if (tm == 0) return 0;

@@ -79,6 +79,9 @@ struct ConvBf16Cfg {
   static constexpr int TN = 128, CK = 32;
 };
 int conv_bf16_tile_m(int stride, int K, int dilation);  // 0 if unsupported
+// passes over the input channels (1, 2 or 3); *interleaved: the passes take
+// every stride-th tap (strided convolutions) rather than consecutive ones
+int conv_bf16_passes(int stride, int K, int dilation, int* interleaved);
 // channels-last input image: rows per sample, bytes, and the repack of x
 int64_t conv_bf16_image_rows(int64_t T_out, int stride, int K, int dilation);
 size_t conv_bf16_image_bytes(int64_t N, int64_t C_in, int64_t T_img);

@@ -58,7 +58,9 @@
  *     built.
  *   - Environment variables (read at each call; none is needed):
  *       C1G_LOG=1             every entry-point call writes one line to stderr:
- *                             its sizes, the plan (route, tiles, workspace),
+ *                             its sizes, the plan (route, tiles, workspace;
+ *                             for the bf16 convolution its tile positions
+ *                             and passes over the input channels),
  *                             the status and, for a refusal or a fallback taken
  *                             at run time, its cause.  Host only.
  *       C1G_FORCE_PATH=split  for tests: problems planned on a single-kernel

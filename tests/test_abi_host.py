@@ -490,3 +490,13 @@ print(lib.conv1d_gn_forward(ctypes.byref(d), ctypes.byref(nd), *([None] * 10), 0
     assert r.returncode == 0 and r.stdout.split() == ["1"], r.stderr
     line = [l for l in r.stderr.splitlines() if l.startswith("c1g: ")][0]
     assert "| fused_persistent" in line and " tiles=%dx8 " % tiles_t in line, line
+    # the tile's positions and its passes over the input channels
+    outs = (T + sum(pad) - dilation * (K - 1) - 1) // stride + 1
+    tile = -(-outs // tiles_t)
+    tile = 512 if tile > 256 else 256 if tile > 128 else 128
+    passes = ""
+    if tile == 512 and K > 5 and stride == 1:
+        passes = " passes=2"
+    elif tile == 512 and stride > 1:
+        passes = " passes=%d interleaved" % min(stride, K)
+    assert line.split(" -> ")[0].endswith(" tile=%d%s" % (tile, passes)), line
