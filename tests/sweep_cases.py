@@ -14,7 +14,7 @@ import conv1d_implicit_gemm_amd as c1g
 from conv1d_implicit_gemm_amd.workloads import Workload
 
 SWEEP_SEED = 20261202
-SWEEP_SEEDS = tuple(SWEEP_SEED + k for k in range(4))  # independent draws
+SWEEP_SEEDS = tuple(SWEEP_SEED + k for k in range(8))  # independent draws
 N_CASES = 96                                # per draw
 MAX_MACS = 1.5e9  # keeps each oracle run under about a second
 
