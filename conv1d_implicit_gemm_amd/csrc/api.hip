@@ -456,8 +456,11 @@ int log_conv(const char* entry, const c1g_conv_desc* d, const c1g_norm_desc* nd,
     if (p.bf16 && d && (p.route == R_SPLIT || p.route == R_CONV_ONLY || p.route == R_PERSIST)) {
       int il = 0;
       const int np = conv_bf16_passes(d->stride, d->K, d->dilation, &il);
-      std::snprintf(conv, sizeof(conv), " tile=%d%s%s", p.tm, np > 1 ? " passes=" : "",
-                    np > 1 ? (il ? (np == 2 ? "2 interleaved" : "3 interleaved") : "2") : "");
+      if (np > 1)
+        std::snprintf(conv, sizeof(conv), " tile=%d passes=%d%s", p.tm, np,
+                      il ? " interleaved" : "");
+      else
+        std::snprintf(conv, sizeof(conv), " tile=%d", p.tm);
     }
     std::snprintf(plan, sizeof(plan), " | %s T_out=%lld tiles=%dx%d ws=%zu%s",
                   route_name(p.route), (long long)p.T_out, p.n_ttiles, p.n_ctiles, p.total,

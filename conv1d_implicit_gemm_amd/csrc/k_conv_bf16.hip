@@ -350,7 +350,8 @@ __device__ __forceinline__ void fused_norm_epilogue(const ConvArgs& a,
 // NP: passes over the chunks.  IL = 0: K = NP * KT consecutive taps per
 // pass (NP = 2 for eight or six taps on 512-position tiles, whose window and
 // weights for all taps do not fit).  IL = 1 (strided convolutions): pass p
-// takes the taps p, p + s, p + 2s, ... (at most KT of them) and its window
+// takes the taps p, p + s, p + 2s, ... (at most KT of them; strides 2 to 5)
+// and its window
 // gathers every s-th image row from row s*t0 + p*d, so that within a pass
 // the output positions advance one window row each and the taps d rows: a
 // stride-1 window of TM + (KT - 1)*d rows where the direct one would need
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   // NP passes over the chunks, pass p with taps p*KT .. p*KT + KT - 1: its
   // window starts p*KT*d rows further down the image and its weights are
   // those taps of each (c-tile, chunk) block
-  static_assert(NP >= 1 && NP <= (IL == 1 ? 3 : 2), "passes");
+  static_assert(NP >= 1 && NP <= (IL == 1 ? 5 : 2), "passes");
   const int64_t wblk = IL ? (int64_t)a.K * (TN * RW * 2)        // bytes of a (c-tile, chunk)
                           : (int64_t)NP * KT * (TN * RW * 2);  // block of the weight image
   const char* const wimg = (const char*)a.wp + (int64_t)ctile * a.n_chunks * wblk;
@@ -432,6 +433,7 @@ __global__ __launch_bounds__(NTHR) void conv_bf16_kernel(ConvArgs a_, int epi) {
   const uint32_t lane_w = (uint32_t)(16 * lane);
   // q: pass * n_chunks + chunk
   auto pass_of = [&](int q) __attribute__((always_inline)) {
+    if constexpr (NP > 3) return q / a.n_chunks;
     return NP >= 3 && q >= 2 * a.n_chunks ? 2 : (NP >= 2 && q >= a.n_chunks ? 1 : 0);
   };
   auto copy_from = [&](const char* xw, int p, int q, u16* xs, u16* ws)
@@ -830,7 +832,7 @@ hipError_t launch_wk(const ConvArgs& a, int epi, hipStream_t st, bool coop = fal
 // positions, np passes over the chunks of at most kt taps each, interleaved
 // (il, strided convolutions) or of consecutive taps, xr window rows.  The
 // first that fits: 512 positions with all taps in one pass; 512 with eight,
-// six or seven taps in two passes; 512 with a stride of 2 or 3 in
+// six or seven taps in two passes; 512 with a stride of 2 to 5 in
 // interleaved passes; 256; 128.  tm == 0: not built.
 struct Geo {
   int tm, kt, np, il, xr;
@@ -844,7 +846,7 @@ Geo geo_of(int s, int K, int d) {
   if ((K == 8 || K == 6) && fits(512, K / 2, s, XCAP_WIDE))
     return Geo{512, K / 2, 2, 0, XCAP_WIDE};
   if (K == 7 && fits(512, 4, s, XCAP_WIDE)) return Geo{512, 4, 2, 2, XCAP_WIDE};  // 4 + 3
-  if (s == 2 || s == 3) {
+  if (s >= 2 && s <= 5) {
     const int kt = (K + s - 1) / s, np = K < s ? K : s;
     if (kt <= 4 && fits(512, kt, 1, XCAP_WIDE)) return Geo{512, kt, np, 1, XCAP_WIDE};
   }
@@ -855,20 +857,21 @@ Geo geo_of(int s, int K, int d) {
   return Geo{0, 0, 0, 0, 0};
 }
 
-// the interleaved instances of 512-position tiles: (kt, np) of strides 2 and 3
+// the interleaved instances of 512-position tiles: (kt, np) of strides 2 to 5
+// (kt = ceil(K / s) taps per pass, np = min(s, K) passes)
 template <typename F>
 hipError_t il_dispatch(const Geo& g, F&& f) {
-  switch (g.kt * 4 + g.np) {
-    case 1 * 4 + 1: return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-    case 1 * 4 + 2: return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
-    case 1 * 4 + 3: return f(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{});
-    case 2 * 4 + 2: return f(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
-    case 2 * 4 + 3: return f(std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
-    case 3 * 4 + 2: return f(std::integral_constant<int, 3>{}, std::integral_constant<int, 2>{});
-    case 3 * 4 + 3: return f(std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
-    case 4 * 4 + 2: return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
+  using std::integral_constant;
+#define C1G_IL(KT_, NP_) \
+  case KT_ * 8 + NP_: return f(integral_constant<int, KT_>{}, integral_constant<int, NP_>{});
+  switch (g.kt * 8 + g.np) {
+    C1G_IL(1, 1) C1G_IL(1, 2) C1G_IL(1, 3) C1G_IL(1, 4) C1G_IL(1, 5)
+    C1G_IL(2, 2) C1G_IL(2, 3) C1G_IL(2, 4) C1G_IL(2, 5)
+    C1G_IL(3, 2) C1G_IL(3, 3)
+    C1G_IL(4, 2)
     default: return hipErrorInvalidValue;
   }
+#undef C1G_IL
 }
 
 template <int WM>

@@ -79,7 +79,7 @@ struct ConvBf16Cfg {
   static constexpr int TN = 128, CK = 32;
 };
 int conv_bf16_tile_m(int stride, int K, int dilation);  // 0 if unsupported
-// passes over the input channels (1, 2 or 3); *interleaved: the passes take
+// passes over the input channels (1 to 5); *interleaved: the passes take
 // every stride-th tap (strided convolutions) rather than consecutive ones
 int conv_bf16_passes(int stride, int K, int dilation, int* interleaved);
 // channels-last input image: rows per sample, bytes, and the repack of x

@@ -51,11 +51,11 @@
  *     N*C_out*T_out below 2^32 (C1G_ERR_UNSUPPORTED beyond); every size check
  *     is made without a product that could wrap, so no oversized argument is
  *     accepted as a small one.  Taps K up to 8, and the input window of a
- *     tile of TM output positions, (TM - 1)*stride + (K - 1)*dilation + 1
- *     rows, must fit on chip: bf16 at most 544 rows at TM = 128 for K <= 5,
- *     224 for K = 6..8 (larger tiles are used whenever theirs fit); fp32 at
- *     most 541 on the split path.  c1g_check reports whether a shape is
- *     built.
+ *     tile must fit on chip: fp32 (split path), (128 - 1)*stride +
+ *     (K - 1)*dilation + 1 <= 541 rows; bf16, the same window <= 544 rows
+ *     (224 for K = 6..8), or, for strides 2 to 5, 512 + (ceil(K/stride) -
+ *     1)*dilation <= 544 rows (passes over every stride-th row).  c1g_check
+ *     reports whether a shape is built.
  *   - Environment variables (read at each call; none is needed):
  *       C1G_LOG=1             every entry-point call writes one line to stderr:
  *                             its sizes, the plan (route, tiles, workspace;

@@ -466,6 +466,8 @@ def test_launch_failure_is_reported_as_hip_error():
                                    # rows, so 128 positions (205 rows); 4019 outputs
     (4, 3, 1, (3, 0), 6000, 4),    # stride 3: three interleaved passes on 512 positions
                                    # (taps 0, 3 / 1 / 2; 513 rows); 2000 outputs
+    (8, 4, 1, (2, 2), 16384, 8),   # stride 4: four interleaved passes of two taps (513 rows)
+    (5, 5, 1, (0, 0), 20480, 8),   # stride 5: five interleaved passes of one tap (512 rows)
     (5, 2, 17, (0, 0), 8192, 32),  # stride 2 at dilation 17: an interleaved pass needs 546
                                    # rows and 256 positions 579, so 128 (323); 4062 outputs
 ])

@@ -249,6 +249,13 @@ STRIDED_CASES = [
        **BF), "fused_persistent"),
     (W("il_s2_k8_d4_conv_only", N=2, C_in=64, C_out=130, T=2500, K=8, stride=2, dilation=4,
        pad_left=14, norm=None, **BF), "conv_only"),
+    # strides 4 and 5: four and five passes, one of them short
+    (W("il_s4_k7_gn", N=2, C_in=40, C_out=136, T=4400, K=7, stride=4, pad_left=3, pad_right=3,
+       G=8, **BF), "fused_persistent"),
+    (W("il_s5_k5_ln_nlc", N=2, C_in=48, C_out=144, T=5200, K=5, stride=5, norm="layer_channels",
+       channels_last=True, **BF), "fused_persistent"),
+    (W("il_s5_k8_d2_gn_split_bf16out", N=2, C_in=33, C_out=128, T=5500, K=8, stride=5,
+       dilation=2, pad_left=7, G=4, out_dtype="bf16", persistent=False, **BF), "split"),
 ]
 
 
