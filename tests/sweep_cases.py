@@ -54,7 +54,7 @@ def _draw(rng, i, tag=""):
     norm = None if norm == "none" else str(norm)
     K = int(rng.integers(1, 9))
     d = int(rng.integers(1, 5)) if K > 1 else 1
-    s = int(rng.choice([1, 1, 1, 2, 3]))
+    s = int(rng.choice([1, 1, 1, 1, 2, 3, 4, 5]))
     span = d * (K - 1)
     if rng.random() < 0.25:
         pl, pr = span, 0                                   # causal
