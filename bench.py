@@ -241,8 +241,8 @@ def config_entry(wl, op, m):
 
 
 def generality(timer, steps, warmup):
-    """The full-scale cases beyond the pages' problems (stride 2 and 3, eight
-    taps at dilation 2, groups spanning or not tiling the channel tiles,
+    """The full-scale cases beyond the pages' problems (stride 2, 3 and 4,
+    eight taps at dilation 2 and at stride 4, groups spanning or not tiling the channel tiles,
     channels-last input, fp32 with stride 2), each step timed like the
     configurations, against its input type's MFMA peak."""
     import torch

@@ -79,12 +79,14 @@ WORKLOADS = {
         Workload("conv1d_lnc_bf16_n64_c512x1024_t4096_k5d2", N=64, C_in=512, C_out=1024,
                  T=4096, K=5, dilation=2, pad_left=2, pad_right=2, dtype="bf16",
                  norm="layer_channels"),
-        # beyond the pages' problems, at full scale: stride 2 and 3, eight taps at
-        # dilation 2, seven causal taps, groups of 256 channels (spanning two
+        # beyond the pages' problems, at full scale: stride 2, 3 and 4, eight taps
+        # at dilation 2 and at stride 4, seven causal taps, groups of 256 channels (spanning two
         # 128-channel tiles) and of 48 (not tiling them), channels-last input, fp32
         # with stride 2
         Workload("conv1d_gn_bf16_n32_c512x1024_t8192_k5s2", N=32, C_in=512, C_out=1024,
                  T=8192, K=5, stride=2, pad_left=2, pad_right=2, dtype="bf16", G=32),
+        Workload("conv1d_gn_bf16_n32_c512x1024_t16384_k8s4", N=32, C_in=512, C_out=1024,
+                 T=16384, K=8, stride=4, pad_left=2, pad_right=2, dtype="bf16", G=32),
         Workload("conv1d_gn_bf16_n32_c256x512_t4096_k8d2", N=32, C_in=256, C_out=512,
                  T=4096, K=8, dilation=2, pad_left=7, pad_right=7, dtype="bf16", G=16),
         Workload("conv1d_lnc_bf16_n32_c512x512_t4096_k7", N=32, C_in=512, C_out=512, T=4096,
@@ -104,6 +106,7 @@ WORKLOADS = {
 # The full-scale cases beyond the pages' problems (parity-tested on sampled
 # outputs, timed by bench.py --mode generality).
 GENERALITY = ("conv1d_gn_bf16_n32_c512x1024_t8192_k5s2",
+              "conv1d_gn_bf16_n32_c512x1024_t16384_k8s4",
               "conv1d_gn_bf16_n32_c256x512_t4096_k8d2",
               "conv1d_lnc_bf16_n32_c512x512_t4096_k7",
               "conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4",

@@ -324,12 +324,13 @@ def test_persistent_determinism():
     assert torch.equal(run_library(wl, inp), run_library(wl, inp))
 
 
-# Generality at scale: stride > 1, 8 taps at dilation 2, groups wider than 32
+# Generality at scale: stride 2 to 4, 8 taps at dilation 2 and at stride 4, groups wider than 32
 # channels (one group spanning channel tiles; groups of 48 that straddle the
 # 128-channel tiles), channels-last input; the same
 # workloads bench.py --mode generality times.  The oracle checks the first and
 # the last sample of each.
 SCALE_ROUTES = {"conv1d_gn_bf16_n32_c512x1024_t8192_k5s2": "fused_persistent",
+                "conv1d_gn_bf16_n32_c512x1024_t16384_k8s4": "fused_persistent",
                 "conv1d_gn_bf16_n32_c256x512_t4096_k8d2": "fused_persistent",
                 "conv1d_lnc_bf16_n32_c512x512_t4096_k7": "fused_persistent",
                 "conv1d_gn_bf16_n32_c512x1024_t4096_k5d2_g4": "fused_persistent",
